@@ -1,0 +1,384 @@
+"""Benchmark: W4/W2 GEMV effective HBM GB/s (% of peak) + M=2048 GEMM TFLOPS.
+
+Headline workload (the `value`): one decode step of the four Llama-3-8B
+linear shapes (N x K = 14336x4096 up/gate, 4096x14336 down, 4096x4096 q/o,
+1024x4096 k/v), weights INT4 with groups of 128, M = 1 bf16 activation row.
+A step is one gq_linear per shape; value = algorithmic bytes of the step
+(packed codes + fp16 scales + uint8 zeros + x + y) / step time.  Weights are
+resident in HBM and 16 copies are rotated (1.16 GB) so the 256 MB Infinity
+Cache cannot serve them.  Steps run as replays of a captured HIP graph.
+
+The same JSON line carries:
+  roofline      the up/gate GEMV kernel alone, bytes per launch / average
+                launch time (HIP events around rotating graph replays),
+                against 8 TB/s HBM; traffic from committed rocprofv3 PMC
+                counters when they were taken on the current kernel source.
+  cpu_baseline  the CPU oracle (tests' reference implementation) timed on
+                a bounded sample of the same workload on this host.
+  secondary     INT2 decode step, INT2 M=4/16, the 224-linear Layer-mix
+                pass, the Channel-mix M=2048 GEMMs (TFLOPS vs 2.5 PFLOP/s
+                bf16/fp16 dense) and quantize+pack of their fp32 weights.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
+METRIC = "W4/W2 GEMV effective HBM GB/s (% of peak) + M=2048 GEMM TFLOPS"
+PMC_FILE = os.path.join(ROOT, "profiles", "gemv_int4_upgate_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--copies", type=int, default=16, help="rotated weight copies (defeat MALL)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    return ap.parse_args()
+
+
+def decode_bytes(N, K, bits, M):
+    g = 128 if bits == 4 else 64
+    return N * K * bits // 8 + (N * K // g) * 3 + 2 * M * K + 2 * M * N
+
+
+# ----------------------------------------------------------------- timing
+
+class GraphTimer:
+    """Capture a list of launches into one HIP graph and time replays with
+    HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, torch, fn):
+        self.torch = torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()                                    # warm: loads code objects
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            fn()
+        torch.cuda.synchronize()
+
+    def run(self, reps):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            self.g.replay()
+        e1.record()
+        t.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        return e0.elapsed_time(e1) / 1e3, wall
+
+
+def rotated_copies(torch, gq, packed, copies):
+    out = [packed]
+    for _ in range(copies - 1):
+        q = gq.Packed(packed.K, packed.N, packed.block_n, packed.bits, packed.codes.clone(),
+                      packed.scales.clone(), packed.zeros.clone(), packed.flags.clone())
+        out.append(q)
+    return out
+
+
+# ------------------------------------------------------------- workloads
+
+def build_decode(torch, gq, S, bits, M, copies):
+    """Packed Llama-3-8B decode linears (seeded), copies rotated."""
+    sets, xs, ys, nbytes = [], [], [], 0
+    for j, (N, K) in enumerate(S.LLAMA3_8B_SHAPE_LIST):
+        W = torch.from_numpy(S.decode_weight(j)).cuda()
+        p = gq.quantize_pack(W, bits)
+        del W
+        sets.append(rotated_copies(torch, gq, p, copies))
+        x = torch.from_numpy(S.decode_x(j, M).view(np.int16)).cuda().view(torch.bfloat16)
+        xs.append(x)
+        ys.append(torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+        nbytes += decode_bytes(N, K, bits, M)
+    torch.cuda.synchronize()
+    return sets, xs, ys, nbytes
+
+
+def decode_pass(gq, sets, xs, ys, c, shapes=None):
+    for j in (range(len(sets)) if shapes is None else shapes):
+        gq.linear(xs[j], sets[j][c], out=ys[j])
+
+
+def time_steps(torch, gq, sets, xs, ys, copies, steps, warmup):
+    """Time exactly `steps` decode steps (graph of `copies` steps + remainder)."""
+    full = GraphTimer(torch, lambda: [decode_pass(gq, sets, xs, ys, c) for c in range(copies)])
+    single = [GraphTimer(torch, lambda c=c: decode_pass(gq, sets, xs, ys, c)) for c in range(copies)]
+
+    def run(n):
+        t = torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(n // copies):
+            full.g.replay()
+        for c in range(n % copies):
+            single[c].g.replay()
+        e1.record()
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3, time.perf_counter() - w0
+
+    run(warmup)
+    return run(steps)
+
+
+def kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=40):
+    """Average duration of one linear's launch (rotating copies)."""
+    gt = GraphTimer(torch, lambda: [gq.linear(xs[j], sets[j][c], out=ys[j]) for c in range(copies)])
+    gt.run(4)
+    t, _ = gt.run(reps)
+    return t / (reps * copies)
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantized_gemm_groupwise_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic():
+    """Calibrated HBM bytes per launch from the committed PMC summary, if the
+    kernel source it was taken on is the current one."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != source_digest(["gemv.hip", "gq_internal.h"]):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(S, nsteps):
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    prep = []
+    nbytes = 0
+    for j, (N, K) in enumerate(S.LLAMA3_8B_SHAPE_LIST):
+        p = O.quantize_pack(S.decode_weight(j), O.Layout(K, N, N, [4]))
+        prep.append((S.decode_x(j, 1), p))
+        nbytes += decode_bytes(N, K, 4, 1)
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        for _ in range(nsteps):
+            for x, p in prep:
+                O.linear(x, p)
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {"value": round(nbytes * nsteps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nsteps} decode steps (4 INT4 g128 Llama-3-8B linears, M=1) through "
+                      f"oracle.linear (unpack, fp64 dequant, fp64 matmul), {dt:.1f} s on 1 thread"}
+
+
+def secondary(torch, gq, S, args):
+    out = {}
+    # INT2 decode step (M=1) and INT2 M=4/16 on up/gate
+    copies2 = 32
+    sets, xs, ys, nb = build_decode(torch, gq, S, 2, 1, copies2)
+    t, _ = time_steps(torch, gq, sets, xs, ys, copies2, 256, 32)
+    out["int2_decode_step_M1"] = {"GBps": round(nb * 256 / t / 1e9, 1),
+                                  "frac_hbm": round(nb * 256 / t / 1e9 / HBM_PEAK_GBS, 3),
+                                  "us_per_step": round(t / 256 * 1e6, 2), "bytes_per_step": nb}
+    per = {}
+    for j, name in enumerate(("up_gate", "down", "q_o", "k_v")):
+        N, K = S.LLAMA3_8B_SHAPE_LIST[j]
+        avg = kernel_avg(torch, gq, sets, xs, ys, j, copies2, reps=10)
+        per[name] = {"us": round(avg * 1e6, 2), "GBps": round(decode_bytes(N, K, 2, 1) / avg / 1e9, 1)}
+    out["int2_M1_per_linear"] = per
+    del sets, xs, ys
+    for M in (4, 16):
+        N, K = S.LLAMA3_8B_SHAPE_LIST[0]
+        W = torch.from_numpy(S.decode_weight(0)).cuda()
+        p = gq.quantize_pack(W, 2)
+        del W
+        cps = rotated_copies(torch, gq, p, copies2)
+        x = torch.from_numpy(S.decode_x(0, M).view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        avg = kernel_avg(torch, gq, [cps], [x], [y], 0, copies2, reps=10)
+        b = decode_bytes(N, K, 2, M)
+        out[f"int2_upgate_M{M}"] = {"us": round(avg * 1e6, 2), "GBps": round(b / avg / 1e9, 1),
+                                    "frac_hbm": round(b / avg / 1e9 / HBM_PEAK_GBS, 3)}
+        del cps, x, y
+    torch.cuda.empty_cache()
+
+    # Layer-mix pass: 224 linears, seeded per-linear INT4/INT2, M in {1, 8, 32}
+    assign = S.layer_mix_assignment()
+    packs, pbytes, n4 = [], 0, 0
+    gen = torch.Generator(device="cuda")
+    for (l, name, N, K, bits) in assign:
+        gen.manual_seed(4000 + len(packs))
+        W = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+        idx = torch.randperm(K, generator=gen, device="cuda")[: int(round(0.005 * K))]
+        W[:, idx] *= 20.0
+        p = gq.quantize_pack(W, bits)
+        del W
+        packs.append(p)
+        pbytes += p.nbytes()
+        n4 += bits == 4
+    torch.cuda.synchronize()
+    params = sum(N * K for (_, _, N, K, _) in assign)
+    lm = {"linears": len(assign), "int4_linears": n4, "bpw": round(pbytes * 8 / params, 4),
+          "packed_bytes": pbytes}
+    for M in (1, 8, 32):
+        xs = {K: torch.from_numpy(S.layer_mix_x(K, M).view(np.int16)).cuda().view(torch.bfloat16)
+              for K in (4096, 14336)}
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for (_, _, N, K, _) in assign]
+        ws = gq.workspace(max(gq.gq_linear_workspace_bytes(p.layout, M) for p in packs) + 256, "cuda")
+
+        def one_pass():
+            for p, y in zip(packs, ys):
+                gq.linear(xs[p.K], p, out=y, ws=ws)
+        gt = GraphTimer(torch, one_pass)
+        gt.run(2)
+        t, _ = gt.run(10)
+        b = pbytes + sum(2 * M * K + 2 * M * N for (_, _, N, K, _) in assign)
+        lm[f"M{M}"] = {"ms_per_pass": round(t / 10 * 1e3, 4), "GBps": round(b * 10 / t / 1e9, 1),
+                       "frac_hbm": round(b * 10 / t / 1e9 / HBM_PEAK_GBS, 3)}
+        del ys, xs
+    out["layer_mix_pass_graph"] = lm
+    del packs
+    torch.cuda.empty_cache()
+
+    # Channel-mix M=2048 GEMM on the 70B-class MLP + quantize/pack of its fp32 weights
+    for j, (N, K) in enumerate(S.MLP70B_SHAPES):
+        Wn, bits = S.channel_mix_weight(j)
+        W = torch.from_numpy(Wn).cuda()
+        del Wn
+        p = gq.quantize_pack(W, bits, 128)
+        torch.cuda.synchronize()
+        qt = GraphTimer(torch, lambda: gq.gq_quantize_pack(
+            p.layout, W.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(), p.zeros.data_ptr(),
+            p.flags.data_ptr()))
+        qt.run(2)
+        t, _ = qt.run(10)
+        qb = N * K * 4 + p.nbytes()
+        out[f"quantize_pack_mlp{j}"] = {"N": N, "K": K, "us": round(t / 10 * 1e6, 1),
+                                        "GBps": round(qb * 10 / t / 1e9, 1),
+                                        "frac_hbm": round(qb * 10 / t / 1e9 / HBM_PEAK_GBS, 3)}
+        del W
+        torch.cuda.empty_cache()
+        M = 2048
+        x = torch.from_numpy(S.channel_mix_x(j).view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = gq.workspace(gq.gq_linear_workspace_bytes(p.layout, M), "cuda")
+        gt = GraphTimer(torch, lambda: gq.linear(x, p, out=y, ws=ws))
+        gt.run(3)
+        t, _ = gt.run(20)
+        fl = 2.0 * M * N * K
+        tf = fl * 20 / t / 1e12
+        out[f"gemm_channel_mix_M2048_mlp{j}"] = {
+            "N": N, "K": K, "int4_blocks": int(sum(b == 4 for b in bits)), "blocks": len(bits),
+            "ms": round(t / 20 * 1e3, 4), "TFLOPS": round(tf, 1),
+            "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 3), "includes": "activation pre-pass + GEMM"}
+        del x, y, p
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_gemm_groupwise_amd as gq
+    import synth as S
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gq.load_library()
+    torch.cuda.set_device(0)
+    copies = args.copies
+    steps = args.steps
+    log(f"bench: building INT4 decode weights ({copies} rotated copies)")
+    sets, xs, ys, nbytes = build_decode(torch, gq, S, 4, 1, copies)
+    log("bench: timing decode steps")
+    t, wall = time_steps(torch, gq, sets, xs, ys, copies, steps, args.warmup)
+    value = nbytes * steps / t / 1e9
+    log(f"bench: {value:.1f} GB/s ({t / steps * 1e6:.2f} us/step, wall {wall / steps * 1e6:.2f} us/step)")
+
+    # roofline: the up/gate GEMV kernel (largest launch of the step)
+    N, K = S.LLAMA3_8B_SHAPE_LIST[0]
+    per_launch = decode_bytes(N, K, 4, 1)
+    avg = kernel_avg(torch, gq, sets, xs, ys, 0, copies)
+    achieved = per_launch / avg / 1e9
+    per_linear = {}
+    for j, name in enumerate(("up_gate", "down", "q_o", "k_v")):
+        Nj, Kj = S.LLAMA3_8B_SHAPE_LIST[j]
+        a = avg if j == 0 else kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=20)
+        per_linear[name] = {"us": round(a * 1e6, 2), "GBps": round(decode_bytes(Nj, Kj, 4, 1) / a / 1e9, 1)}
+    log(f"bench: up/gate GEMV {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
+                "kernel": "gemv_kernel<bf16, M=1, R=8, INT4> on N=14336 K=4096",
+                "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3)}
+    del sets, xs, ys
+    torch.cuda.empty_cache()
+
+    sec = None
+    if not args.no_secondary:
+        log("bench: secondary measurements")
+        sec = secondary(torch, gq, S, args)
+        sec["int4_M1_per_linear"] = per_linear
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(S, args.cpu_steps)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(t / steps * 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-3-8B decode step: 4 linears (N x K = 14336x4096, 4096x14336, "
+                               "4096x4096, 1024x4096), INT4 g128 weights, M=1 bf16 activations",
+                   "bits": 4, "group": 128, "M": 1, "bytes_per_step": nbytes,
+                   "rotated_weight_copies": copies, "frac_hbm": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": sec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * gq.h -- C ABI of libgq: group-wise asymmetric MinMax weight quantization
+ * (INT4 with groups of 128, INT2 with groups of 64) and the weight-only
+ * low-bit matmul that consumes the packed format, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources the operations follow (page title, then the part of the page):
+ *   GreenBitAI, "只需单卡 RTX 3090 低比特量化训练就能实现 LLaMA-3 8B 全参微调":
+ *     two-stage quantization -- a group-wise MinMax quantizer with
+ *     round-to-nearest, INT4 (group size 128) and INT2 (group size 64) as the
+ *     only base representations; Layer-mix (one bit-width per linear) and
+ *     Channel-mix (bit-width per block of output channels) layouts.
+ *   "大模型量化实战：从原理到4-bit部署的完整指南", section 2.2 -- the affine
+ *     quantizer Q(x) = round(x/s) + z, s = (x_max - x_min)/(q_max - q_min),
+ *     z = round(0 - x_min/s), z kept inside the integer range.
+ *   "Low-bit Quantization: Slimming Large Models to the Extreme", "Zero
+ *     Point" -- dequantized value = (quantized value - zero_point) x scale.
+ *   "A Survey of Low-bit Large Language Models" (paper review), sections
+ *     5.2 and 6.2 -- weight-only quantization dequantizes and then runs an
+ *     FP16 matmul; its speed-up comes from moving fewer weight bytes.
+ *
+ * Conventions for every entry point
+ *   - W is the weight of a linear layer y = x . W^T, stored [N][K] row-major
+ *     (N output channels, K input channels, K contiguous).  Groups run along
+ *     K.  x is [M][K] and y is [M][N], both row-major.
+ *   - Per group of g weights: lo = min, hi = max (fp32);
+ *     s32 = (hi - lo) / (2^b - 1) (fp32, correctly rounded);
+ *     S = fp16(s32) rounded to nearest even, replaced by 1.0 if it is zero;
+ *     z = clamp(rint(-lo / S), 0, 2^b - 1) stored as uint8;
+ *     code = clamp(rint(w / S) + z, 0, 2^b - 1); rint rounds half to even
+ *     and the divisions are correctly rounded fp32 divisions.
+ *   - Packed codes: each row of a block is K*b/8 bytes; uint32 word j of a
+ *     row holds codes k = j*32/b + i at bits [b*i, b*i + b), little-endian.
+ *     Scales (fp16 bit patterns) and zeros (uint8) are [rows][K/g] per block.
+ *     Blocks are stored back to back in block order: block i's codes start at
+ *     byte sum_{j<i} block_n*K*b_j/8 and its scales/zeros at group
+ *     sum_{j<i} block_n*K/g_j.
+ *   - Pointers marked DEVICE are device (HBM) memory of the current HIP
+ *     device; HOST pointers are read during the call only.  The caller owns
+ *     every buffer; the library allocates nothing and keeps no per-call state.
+ *   - All GPU work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream) and is asynchronous: a GQ_OK return means the work was
+ *     enqueued.  Calls are reentrant; calls that share an output buffer must
+ *     be ordered by the caller.
+ *   - Errors: argument checks run on the host before anything is enqueued and
+ *     return a non-zero gq_status without side effects.  A failed kernel
+ *     launch returns GQ_ERR_HIP.  No exception crosses the ABI, nothing is
+ *     printed and nothing aborts.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gq_status {
+  GQ_OK = 0,
+  GQ_ERR_NULL_ARG = 1,   /* a required pointer is NULL                          */
+  GQ_ERR_SHAPE = 2,      /* K<=0, N<0, M<0, N % block_n, K % g, too many blocks */
+  GQ_ERR_BITS = 3,       /* a bit-width other than 2 or 4                       */
+  GQ_ERR_ALIGNMENT = 4,  /* a device pointer is not 16-byte aligned             */
+  GQ_ERR_DTYPE = 5,      /* unsupported dtype for this argument                 */
+  GQ_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required             */
+  GQ_ERR_HIP = 7         /* the HIP runtime refused a launch                    */
+} gq_status;
+
+typedef enum gq_dtype { GQ_BF16 = 0, GQ_FP16 = 1, GQ_FP32 = 2 } gq_dtype;
+
+/* Device flag bits OR-ed into *flags by gq_quantize_pack. */
+#define GQ_FLAG_NONFINITE 1u      /* a group held NaN or Inf; its codes are unspecified   */
+#define GQ_FLAG_SCALE_OVERFLOW 2u /* (hi-lo)/(2^b-1) rounded to fp16 infinity (> 65504)   */
+
+/* Largest number of bit-width blocks in one layout. */
+#define GQ_MAX_BLOCKS 1024
+
+/* Bit-width map of one linear (the mixed-precision layouts of GreenBitAI's
+ * two-stage quantization).  N/block_n blocks of block_n consecutive output
+ * channels; bits[i] in {4, 2} is block i's width (INT4 uses groups of 128,
+ * INT2 groups of 64).  A uniform linear (Layer-mix) has block_n == N and one
+ * entry; Channel-mix uses block_n == 128.  Rules: N % block_n == 0; when there
+ * is more than one block, block_n % 128 == 0; K is a positive multiple of 128
+ * if any block is INT4, else of 64.  `bits` is a HOST array. */
+typedef struct gq_layout {
+  int32_t K;
+  int32_t N;
+  int32_t block_n;
+  const uint8_t *bits;
+} gq_layout;
+
+/* Sizes of the three packed buffers for `layout`, in bytes (HOST outputs).
+ * codes: sum over blocks of block_n*K*b/8; scales: 2 bytes per group;
+ * zeros: 1 byte per group.  Pure host computation. */
+gq_status gq_packed_bytes(const gq_layout *layout, size_t *codes_bytes,
+                          size_t *scales_bytes, size_t *zeros_bytes);
+
+/* Quantize W and pack it (GreenBitAI group-wise MinMax; section 2.2 of the
+ * 4-bit deployment guide).
+ *   w      DEVICE fp32 [N][K], 16-byte aligned, read only.
+ *   codes  DEVICE, gq_packed_bytes codes bytes, 16-byte aligned, written.
+ *   scales DEVICE fp16 bit patterns, 2-byte aligned, written.
+ *   zeros  DEVICE uint8, written.
+ *   flags  DEVICE uint32 or NULL; GQ_FLAG_* bits are OR-ed in (never cleared).
+ * Codes, scales and zeros are bit-identical to the definition above.  A group
+ * holding NaN/Inf sets GQ_FLAG_NONFINITE and gets unspecified codes. */
+gq_status gq_quantize_pack(const gq_layout *layout, const float *w, uint32_t *codes,
+                           uint16_t *scales, uint8_t *zeros, uint32_t *flags, void *stream);
+
+/* Dequantize: w_out[n][k] = (code - z) * S ("Zero Point" of the low-bit
+ * tutorial).  The value is exact in fp32; GQ_BF16 and GQ_FP16 outputs are
+ * that value rounded to nearest even.
+ *   codes/scales/zeros  DEVICE, as written by gq_quantize_pack.
+ *   w_out  DEVICE [N][K] of out_dtype, 16-byte aligned. */
+gq_status gq_dequant(const gq_layout *layout, const uint32_t *codes, const uint16_t *scales,
+                     const uint8_t *zeros, gq_dtype out_dtype, void *w_out, void *stream);
+
+/* Workspace gq_linear needs for this layout, M and activation dtype (HOST
+ * output *bytes; may be 0).  Pure host computation. */
+gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
+                                    size_t *bytes);
+
+/* Weight-only low-bit matmul y = x . W_hat^T with W_hat = (code - z) * S
+ * (the survey review, sections 5.2 and 6.2: dequantize, then a floating-point
+ * matmul; dequantization happens in registers, W_hat never reaches memory).
+ *   act    GQ_BF16 or GQ_FP16: dtype of x and y.
+ *   x      DEVICE [M][K] act, 16-byte aligned.
+ *   y      DEVICE [M][N] act, 2-byte aligned, written (bf16/fp16 rounded to
+ *          nearest even from an fp32 accumulator).
+ *   workspace  DEVICE, 256-byte aligned, at least gq_linear_workspace_bytes;
+ *          may be NULL when that is 0.  Overwritten; calls that share a
+ *          workspace must be ordered on one stream.
+ * M < 64 uses a bandwidth-bound dot-product kernel that applies (code - z)
+ * and S exactly in fp32; larger M uses an MFMA kernel that rounds each
+ * dequantized weight once to fp16 (the FP16 matmul of the survey review) and
+ * activations are rescaled per row by a power of two so that their fp16 form
+ * is exact.  Results agree with the fp64 product of the dequantized weights
+ * to about the bf16 output rounding (normwise relative error <= 2e-3). */
+gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
+                    const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                    void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *gq_status_string(gq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQ_H */

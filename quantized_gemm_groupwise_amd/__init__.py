@@ -1,0 +1,247 @@
+"""Python binding of libgq: group-wise INT4/INT2 quantization and the
+weight-only low-bit matmul on AMD Instinct MI355X (gfx950).
+
+The functions named gq_* mirror the C ABI in include/gq.h one to one and only
+marshal arguments: every step of the computation runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.
+
+Convenience layer:
+    packed = quantize_pack(w, bits, block_n=None)   # w: fp32 cuda [N][K]
+    y = linear(x, packed)                           # x: bf16/fp16 cuda [M][K]
+    w_hat = dequant(packed, torch.float32)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # noqa: F401  -- load torch's HIP runtime before libgq
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgq.so")
+
+GQ_OK, GQ_ERR_NULL_ARG, GQ_ERR_SHAPE, GQ_ERR_BITS, GQ_ERR_ALIGNMENT, GQ_ERR_DTYPE, \
+    GQ_ERR_WORKSPACE, GQ_ERR_HIP = range(8)
+GQ_BF16, GQ_FP16, GQ_FP32 = 0, 1, 2
+GQ_FLAG_NONFINITE = 1
+GQ_FLAG_SCALE_OVERFLOW = 2
+GQ_MAX_BLOCKS = 1024
+GROUP = {4: 128, 2: 64}
+
+# Every symbol include/gq.h declares.
+EXPORTS = ("gq_packed_bytes", "gq_quantize_pack", "gq_dequant", "gq_linear_workspace_bytes",
+           "gq_linear", "gq_status_string")
+
+
+class GqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {gq_status_string(status)}")
+        self.status = status
+
+
+class gq_layout(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("bits", ctypes.POINTER(ctypes.c_uint8))]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgq.so (built by quantized_gemm_groupwise_amd._build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m quantized_gemm_groupwise_amd._build`")
+    lib = ctypes.CDLL(path)
+    P, S, I32, VP = ctypes.POINTER, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p
+    L = P(gq_layout)
+    sig = {
+        "gq_packed_bytes": ([L, P(S), P(S), P(S)], ctypes.c_int),
+        "gq_quantize_pack": ([L, VP, VP, VP, VP, VP, VP], ctypes.c_int),
+        "gq_dequant": ([L, VP, VP, VP, ctypes.c_int, VP, VP], ctypes.c_int),
+        "gq_linear_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
+        "gq_linear": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
+        "gq_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def make_layout(K: int, N: int, block_n: int, bits) -> gq_layout:
+    arr = (ctypes.c_uint8 * max(1, len(bits)))(*[int(b) for b in bits])
+    lay = gq_layout(int(K), int(N), int(block_n), ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8)))
+    lay._keep = arr  # keep the host array alive with the struct
+    return lay
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ------------------------------------------------ one-to-one ABI wrappers
+
+def gq_status_string(status: int) -> str:
+    return load_library().gq_status_string(int(status)).decode()
+
+
+def gq_packed_bytes(layout: gq_layout):
+    c, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = load_library().gq_packed_bytes(ctypes.byref(layout), ctypes.byref(c), ctypes.byref(s),
+                                        ctypes.byref(z))
+    if st != GQ_OK:
+        raise GqError(st, "gq_packed_bytes")
+    return c.value, s.value, z.value
+
+
+def gq_quantize_pack(layout, w_ptr, codes_ptr, scales_ptr, zeros_ptr, flags_ptr=None,
+                     stream=None) -> int:
+    return load_library().gq_quantize_pack(ctypes.byref(layout), w_ptr, codes_ptr, scales_ptr,
+                                           zeros_ptr, flags_ptr, _stream(stream))
+
+
+def gq_dequant(layout, codes_ptr, scales_ptr, zeros_ptr, out_dtype, out_ptr, stream=None) -> int:
+    return load_library().gq_dequant(ctypes.byref(layout), codes_ptr, scales_ptr, zeros_ptr,
+                                     int(out_dtype), out_ptr, _stream(stream))
+
+
+def gq_linear_workspace_bytes(layout, M: int, act: int = GQ_BF16) -> int:
+    b = ctypes.c_size_t()
+    st = load_library().gq_linear_workspace_bytes(ctypes.byref(layout), int(M), int(act),
+                                                  ctypes.byref(b))
+    if st != GQ_OK:
+        raise GqError(st, "gq_linear_workspace_bytes")
+    return b.value
+
+
+def gq_linear(layout, M, act, x_ptr, codes_ptr, scales_ptr, zeros_ptr, y_ptr, ws_ptr, ws_bytes,
+              stream=None) -> int:
+    return load_library().gq_linear(ctypes.byref(layout), int(M), int(act), x_ptr, codes_ptr,
+                                    scales_ptr, zeros_ptr, y_ptr, ws_ptr, int(ws_bytes),
+                                    _stream(stream))
+
+
+# ------------------------------------------------------ tensor-level API
+
+_DT = {torch.bfloat16: GQ_BF16, torch.float16: GQ_FP16, torch.float32: GQ_FP32}
+
+
+@dataclass
+class Packed:
+    """Packed weights of one linear: codes, fp16 scales and uint8 zeros as
+    flat device tensors plus the bit map."""
+    K: int
+    N: int
+    block_n: int
+    bits: list
+    codes: torch.Tensor    # uint8, 16-byte aligned
+    scales: torch.Tensor   # int16 holding fp16 bit patterns
+    zeros: torch.Tensor    # uint8
+    flags: torch.Tensor    # int32 [1]
+
+    @property
+    def layout(self) -> gq_layout:
+        lay = getattr(self, "_layout", None)
+        if lay is None:
+            lay = make_layout(self.K, self.N, self.block_n, self.bits)
+            self._layout = lay
+        return lay
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel() * 2 + self.zeros.numel()
+
+
+def _check(st: int, where: str):
+    if st != GQ_OK:
+        raise GqError(st, where)
+
+
+def _cuda(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def empty_packed(K: int, N: int, bits, block_n: int | None = None, device="cuda") -> Packed:
+    bits = [int(bits)] if isinstance(bits, int) else [int(b) for b in bits]
+    block_n = N if block_n is None else int(block_n)
+    lay = make_layout(K, N, block_n, bits)
+    cb, sb, zb = gq_packed_bytes(lay)
+    p = Packed(K, N, block_n, bits,
+               torch.empty(max(cb, 16), dtype=torch.uint8, device=device),
+               torch.empty(max(sb // 2, 1), dtype=torch.int16, device=device),
+               torch.empty(max(zb, 1), dtype=torch.uint8, device=device),
+               torch.zeros(1, dtype=torch.int32, device=device))
+    p._layout = lay
+    return p
+
+
+def quantize_pack(w: torch.Tensor, bits, block_n: int | None = None, stream=None) -> Packed:
+    """Quantize fp32 weights w [N][K] group-wise (INT4 g128 / INT2 g64).
+
+    bits: 4, 2, or a list with one entry per block of block_n output channels."""
+    _cuda(w, "w")
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor [N][K]")
+    N, K = w.shape
+    nb = 1 if isinstance(bits, int) else len(bits)
+    if block_n is None:
+        block_n = N // nb if nb else N
+    block_n = max(1, int(block_n))
+    p = empty_packed(K, N, bits, block_n, device=w.device)
+    _check(gq_quantize_pack(p.layout, w.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
+                            p.zeros.data_ptr(), p.flags.data_ptr(), stream), "gq_quantize_pack")
+    return p
+
+
+def dequant(p: Packed, dtype=torch.float32, stream=None) -> torch.Tensor:
+    out = torch.empty((p.N, p.K), dtype=dtype, device=p.codes.device)
+    _check(gq_dequant(p.layout, p.codes.data_ptr(), p.scales.data_ptr(), p.zeros.data_ptr(),
+                      _DT[dtype], out.data_ptr(), stream), "gq_dequant")
+    return out
+
+
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A cached device workspace of at least nbytes (per device)."""
+    if nbytes == 0:
+        return None
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def linear(x: torch.Tensor, p: Packed, out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """y = x . W_hat^T for bf16 or fp16 x [M][K]; y has x's dtype."""
+    _cuda(x, "x")
+    if x.dim() != 2 or x.shape[1] != p.K:
+        raise ValueError(f"x must be [M][{p.K}]")
+    act = _DT.get(x.dtype)
+    if act not in (GQ_BF16, GQ_FP16):
+        raise ValueError("x must be bfloat16 or float16")
+    M = x.shape[0]
+    y = torch.empty((M, p.N), dtype=x.dtype, device=x.device) if out is None else out
+    need = gq_linear_workspace_bytes(p.layout, M, act)
+    if ws is None:
+        ws = workspace(need, x.device)
+    wptr = ws.data_ptr() if ws is not None else None
+    wbytes = ws.numel() if ws is not None else 0
+    _check(gq_linear(p.layout, M, act, x.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
+                     p.zeros.data_ptr(), y.data_ptr(), wptr, wbytes, stream), "gq_linear")
+    return y

@@ -1,0 +1,128 @@
+// C ABI of libgq (declared in include/gq.h): argument checks, then dispatch
+// to the kernels.  Every check happens on the host before anything is
+// enqueued; nothing here allocates, prints or aborts.
+#include <stdlib.h>
+
+#include "gq_internal.h"
+
+using namespace gq;
+
+namespace {
+
+gq_status launched(hipError_t e, hipStream_t s) {
+  if (e != hipSuccess) return GQ_ERR_HIP;
+  static const bool debug_sync = [] {
+    const char *v = getenv("GQ_DEBUG_SYNC");
+    return v && v[0] == '1';
+  }();
+  if (debug_sync) {
+    if (hipStreamSynchronize(s) != hipSuccess) return GQ_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return GQ_ERR_HIP;
+  }
+  return GQ_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+gq_status gq_packed_bytes(const gq_layout *layout, size_t *codes_bytes, size_t *scales_bytes,
+                          size_t *zeros_bytes) {
+  if (!codes_bytes || !scales_bytes || !zeros_bytes) return GQ_ERR_NULL_ARG;
+  LayoutDev L;
+  const gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  size_t cb = 0, ng = 0;
+  for (int i = 0; i < L.nblocks; ++i) {
+    const int b = layout->bits[i];
+    cb += (size_t)L.block_n * (size_t)L.K * (size_t)b / 8u;
+    ng += (size_t)L.block_n * (size_t)L.K / (b == 4 ? 128u : 64u);
+  }
+  *codes_bytes = cb;
+  *scales_bytes = ng * 2u;
+  *zeros_bytes = ng;
+  return GQ_OK;
+}
+
+gq_status gq_quantize_pack(const gq_layout *layout, const float *w, uint32_t *codes,
+                           uint16_t *scales, uint8_t *zeros, uint32_t *flags, void *stream) {
+  LayoutDev L;
+  gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  if (L.N == 0) return GQ_OK;
+  if ((st = check_ptr16(w)) != GQ_OK) return st;
+  if ((st = check_ptr16(codes)) != GQ_OK) return st;
+  if (!scales || !zeros) return GQ_ERR_NULL_ARG;
+  if ((uintptr_t)scales & 1u) return GQ_ERR_ALIGNMENT;
+  if (flags && ((uintptr_t)flags & 3u)) return GQ_ERR_ALIGNMENT;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launched(launch_quantize_pack(L, w, codes, scales, zeros, flags, s), s);
+}
+
+gq_status gq_dequant(const gq_layout *layout, const uint32_t *codes, const uint16_t *scales,
+                     const uint8_t *zeros, gq_dtype out_dtype, void *w_out, void *stream) {
+  LayoutDev L;
+  gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  if (out_dtype != GQ_BF16 && out_dtype != GQ_FP16 && out_dtype != GQ_FP32) return GQ_ERR_DTYPE;
+  if (L.N == 0) return GQ_OK;
+  if ((st = check_ptr16(codes)) != GQ_OK) return st;
+  if ((st = check_ptr16(w_out)) != GQ_OK) return st;
+  if (!scales || !zeros) return GQ_ERR_NULL_ARG;
+  if ((uintptr_t)scales & 1u) return GQ_ERR_ALIGNMENT;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launched(launch_dequant(L, codes, scales, zeros, out_dtype, w_out, s), s);
+}
+
+gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
+                                    size_t *bytes) {
+  if (!bytes) return GQ_ERR_NULL_ARG;
+  LayoutDev L;
+  const gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  if (M < 0) return GQ_ERR_SHAPE;
+  if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  *bytes = linear_workspace_bytes(L, M, act);
+  return GQ_OK;
+}
+
+gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
+                    const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                    void *y, void *workspace, size_t workspace_bytes, void *stream) {
+  LayoutDev L;
+  gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  if (M < 0) return GQ_ERR_SHAPE;
+  if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  if (M == 0 || L.N == 0) return GQ_OK;
+  if ((st = check_ptr16(x)) != GQ_OK) return st;
+  if ((st = check_ptr16(codes)) != GQ_OK) return st;
+  if (!scales || !zeros || !y) return GQ_ERR_NULL_ARG;
+  if (((uintptr_t)scales & 1u) || ((uintptr_t)y & 1u)) return GQ_ERR_ALIGNMENT;
+  const size_t need = linear_workspace_bytes(L, M, act);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return GQ_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255u) return GQ_ERR_ALIGNMENT;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (M <= kGemvMaxM)
+    return launched(launch_gemv(L, M, act, x, codes, scales, zeros, y, s), s);
+  return launched(launch_gemm(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
+}
+
+const char *gq_status_string(gq_status status) {
+  switch (status) {
+    case GQ_OK: return "GQ_OK: success";
+    case GQ_ERR_NULL_ARG: return "GQ_ERR_NULL_ARG: a required pointer is NULL";
+    case GQ_ERR_SHAPE: return "GQ_ERR_SHAPE: invalid K, N, M or block layout";
+    case GQ_ERR_BITS: return "GQ_ERR_BITS: bit-widths must be 2 or 4";
+    case GQ_ERR_ALIGNMENT: return "GQ_ERR_ALIGNMENT: a device pointer is misaligned";
+    case GQ_ERR_DTYPE: return "GQ_ERR_DTYPE: unsupported dtype";
+    case GQ_ERR_WORKSPACE: return "GQ_ERR_WORKSPACE: workspace missing or too small";
+    case GQ_ERR_HIP: return "GQ_ERR_HIP: the HIP runtime refused a launch";
+  }
+  return "unknown gq_status";
+}
+
+}  // extern "C"

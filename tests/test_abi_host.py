@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/gq.h declares, sizes buffers like the oracle's layout,
+and rejects bad arguments before anything is enqueued.
+
+Pointer arguments in the error-path tests are fake addresses: every checked
+error returns before any device memory is touched or any kernel launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+
+gq = pytest.importorskip("quantized_gemm_groupwise_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gq.load_library()
+
+
+def test_exports_match_header(lib):
+    hdr = open(os.path.join(ROOT, "include", "gq.h")).read()
+    declared = set(re.findall(r"^\S.*?\b(gq_[a-z_]+)\s*\(", hdr, flags=re.M))
+    assert declared == set(gq.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_single_hip_runtime_mapped(lib):
+    maps = {l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l}
+    assert len(maps) == 1, maps
+
+
+@pytest.mark.parametrize("K,N,block_n,bits", [
+    (512, 512, 512, [4]), (4096, 14336, 14336, [4]), (14336, 4096, 4096, [2]),
+    (8192, 28672, 128, [4, 2] * 112), (256, 384, 128, [2, 4, 2]), (64, 5, 5, [2]),
+])
+def test_packed_sizes_match_oracle_layout(K, N, block_n, bits):
+    cb, sb, zb = gq.gq_packed_bytes(gq.make_layout(K, N, block_n, bits))
+    ocb, ons, onz = O.Layout(K, N, block_n, bits).sizes()
+    assert (cb, sb, zb) == (ocb, 2 * ons, onz)
+
+
+def _st(f, *a):
+    return f(*a)
+
+
+def test_layout_validation(lib):
+    P = gq.make_layout
+    c, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    def pb(lay):
+        return lib.gq_packed_bytes(ctypes.byref(lay), ctypes.byref(c), ctypes.byref(s), ctypes.byref(z))
+    assert pb(P(512, 512, 512, [4])) == gq.GQ_OK
+    assert pb(P(512, 512, 512, [3])) == gq.GQ_ERR_BITS
+    assert pb(P(512, 512, 512, [8])) == gq.GQ_ERR_BITS
+    assert pb(P(192, 512, 512, [4])) == gq.GQ_ERR_SHAPE      # K % 128
+    assert pb(P(192, 512, 512, [2])) == gq.GQ_OK              # K % 64 ok for INT2
+    assert pb(P(100, 512, 512, [2])) == gq.GQ_ERR_SHAPE
+    assert pb(P(0, 512, 512, [4])) == gq.GQ_ERR_SHAPE
+    assert pb(P(512, 500, 128, [4] * 4)) == gq.GQ_ERR_SHAPE   # N % block_n
+    assert pb(P(512, 256, 64, [4] * 4)) == gq.GQ_ERR_SHAPE    # multi-block needs 128 | block_n
+    assert pb(P(512, 1025 * 128, 128, [4] * 1025)) == gq.GQ_ERR_SHAPE   # too many blocks
+    assert pb(P(512, 0, 1, [])) == gq.GQ_OK
+    assert lib.gq_packed_bytes(None, ctypes.byref(c), ctypes.byref(s), ctypes.byref(z)) == gq.GQ_ERR_NULL_ARG
+    lay = gq.gq_layout(512, 512, 512, None)
+    assert pb(lay) == gq.GQ_ERR_NULL_ARG
+
+
+def test_argument_errors_before_launch(lib):
+    lay = gq.make_layout(512, 256, 256, [4])
+    A = 0x10000        # aligned fake address
+    bad = 0x10008      # 8-byte aligned only
+    Q = lambda *a: lib.gq_quantize_pack(ctypes.byref(lay), *a)
+    assert Q(None, A, A, A, None, None) == gq.GQ_ERR_NULL_ARG
+    assert Q(bad, A, A, A, None, None) == gq.GQ_ERR_ALIGNMENT
+    assert Q(A, bad, A, A, None, None) == gq.GQ_ERR_ALIGNMENT
+    assert Q(A, A, A + 1, A, None, None) == gq.GQ_ERR_ALIGNMENT
+    assert Q(A, A, None, A, None, None) == gq.GQ_ERR_NULL_ARG
+    assert Q(A, A, A, A, A + 2, None) == gq.GQ_ERR_ALIGNMENT
+    D = lambda *a: lib.gq_dequant(ctypes.byref(lay), *a)
+    assert D(A, A, A, 7, A, None) == gq.GQ_ERR_DTYPE
+    assert D(A, A, A, gq.GQ_FP32, bad, None) == gq.GQ_ERR_ALIGNMENT
+    assert D(None, A, A, gq.GQ_FP32, A, None) == gq.GQ_ERR_NULL_ARG
+    Lf = lambda M, act, x, y, ws, wsb: lib.gq_linear(ctypes.byref(lay), M, act, x, A, A, A, y, ws, wsb, None)
+    assert Lf(-1, gq.GQ_BF16, A, A, None, 0) == gq.GQ_ERR_SHAPE
+    assert Lf(1, gq.GQ_FP32, A, A, None, 0) == gq.GQ_ERR_DTYPE
+    assert Lf(1, gq.GQ_BF16, bad, A, None, 0) == gq.GQ_ERR_ALIGNMENT
+    assert Lf(1, gq.GQ_BF16, A, A + 1, None, 0) == gq.GQ_ERR_ALIGNMENT
+    assert Lf(1, gq.GQ_BF16, A, None, None, 0) == gq.GQ_ERR_NULL_ARG
+    need = gq.gq_linear_workspace_bytes(lay, 100)
+    assert need > 0
+    assert Lf(100, gq.GQ_BF16, A, A, None, 0) == gq.GQ_ERR_WORKSPACE
+    assert Lf(100, gq.GQ_BF16, A, A, A, need - 1) == gq.GQ_ERR_WORKSPACE
+    assert Lf(100, gq.GQ_BF16, A, A, A + 16, need) == gq.GQ_ERR_ALIGNMENT
+    # empty work is a no-op that succeeds without touching any pointer
+    assert Lf(0, gq.GQ_BF16, None, None, None, 0) == gq.GQ_OK
+    lay0 = gq.make_layout(512, 0, 1, [])
+    assert lib.gq_quantize_pack(ctypes.byref(lay0), None, None, None, None, None, None) == gq.GQ_OK
+
+
+def test_workspace_sizes():
+    lay = gq.make_layout(4096, 14336, 14336, [4])
+    for M in (0, 1, 4):
+        assert gq.gq_linear_workspace_bytes(lay, M) == 0
+    for M in (5, 64, 2048):
+        ws = gq.gq_linear_workspace_bytes(lay, M)
+        assert ws >= M * 4096 * 2 + M * 4 and ws % 256 == 0
+
+
+def test_status_strings():
+    for st in range(8):
+        assert gq.gq_status_string(st).startswith("GQ_")
+    assert "unknown" in gq.gq_status_string(99)
+
+
+def test_product_path_refuses_missing_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("quantized_gemm_groupwise_amd")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load_library(str(tmp_path / "nope.so"))
+    finally:
+        mod._lib = saved
