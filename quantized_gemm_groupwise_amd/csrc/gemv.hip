@@ -2,16 +2,30 @@
 //
 // Weight-only quantization moves b-bit codes instead of 16-bit weights and
 // dequantizes on chip ("A Survey of Low-bit Large Language Models" review,
-// section 6.2: dequantization cost must stay below the transfer time it
-// saves).  This kernel is bound by HBM bandwidth: every packed byte is read
-// once with a 128-bit load, unpacked in registers and never written back.
+// section 6.2: dequantization must cost less than the transfer it saves).
+// This kernel is bound by HBM bandwidth: every packed byte is read once with
+// a 128-bit load, unpacked in registers and never written back.
 //
-// Exactness: a code q (4 or 2 bits) ORed into the low mantissa bits of the
-// constant 128.0 (bf16) or 1024.0 (fp16) is the exact value 128+q / 1024+q.
-// A packed pair of such values feeds v_dot2 against the matching pair of
-// activations, so the inner loop computes P = sum x*(B+q) in fp32.  Per group
-// the zero point and scale are applied as s * (P - (B+z) * sum x), which is
-// sum x*(q-z)*s with fp32 rounding only.
+// Work split.  A workgroup of 4 waves owns 4R consecutive output channels,
+// each wave R of them.  A packed row is cut into 1 KB slices; lane l reads
+// bytes [1024 i + 16 l, +16) of slice i of each of its R rows, i.e. the
+// codes of KPL = 128/b consecutive k.  Code, scale and zero loads for NL
+// slices are issued as one group, and the next group is issued before the
+// current one is computed, so each slice waits only for its own bytes.
+//
+// Activations.  The workgroup stages x in LDS once, already arranged as the
+// code pairs come out of a packed word and laid out lane-major so reads are
+// conflict-free, together with the per-lane sums sum_k x_k that the zero
+// point needs.  LDS traffic has its own counter, so reading x never waits for
+// outstanding code loads.
+//
+// Exactness.  A code q ORed into the low mantissa bits of 128.0 (bf16) or
+// 1024.0 (fp16) is exactly 128+q / 1024+q; a 2-bit code two or four bits
+// higher reads as 128+4q or 128+16q.  Pairs of such values feed v_dot2
+// against the matching activation pairs with fp32 accumulation, one
+// accumulator per position class.  Per group the zero point and scale are
+// applied as s * (sum x*q - z * sum x), i.e. sum x*(q-z)*s up to fp32
+// rounding.
 #include "gq_internal.h"
 
 namespace gq {
@@ -22,6 +36,9 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kLanes = 64;
 constexpr int kWaves = 4;
+constexpr int kThreads = kLanes * kWaves;
+constexpr int kStageUnits = 2;             // x units staged per thread per chunk
+constexpr int kLdsBytes = 65536;
 
 template <int ACT>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -33,8 +50,15 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                   c, false);
 }
 
-// Pair of activations (x[i], x[i + half]) for code pair i of a word, from
-// registers holding consecutive activation pairs.
+// (a & m) | o in one VALU op (the three operands in VGPRs; gfx9 VOP3 cannot
+// take two literal constants).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// (x[i], x[i + half]) from registers holding consecutive activation pairs.
 __device__ __forceinline__ uint32_t pair_lo(uint32_t hi_reg, uint32_t lo_reg) {
   return __builtin_amdgcn_perm(hi_reg, lo_reg, 0x05040100u);
 }
@@ -42,199 +66,478 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t hi_reg, uint32_t lo_reg) {
   return __builtin_amdgcn_perm(hi_reg, lo_reg, 0x07060302u);
 }
 
-template <int BITS, int ACT, int M, int R>
-__device__ __forceinline__ void gemv_rows(const LayoutDev &L, const BlockInfo &bi, int blk, int n0,
-                                          const uint16_t *__restrict__ x,
-                                          const uint8_t *__restrict__ codes,
-                                          const uint16_t *__restrict__ scales,
-                                          const uint8_t *__restrict__ zeros,
-                                          uint16_t *__restrict__ y) {
-  constexpr int G = BITS == 4 ? 128 : 64;
-  constexpr int KPL = 128 / BITS;            // weights per lane per 16-byte load
-  constexpr int XR = KPL / 2;                // activation registers (pairs) per row of x
-  constexpr uint32_t BIAS = ACT == 0 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0
-  constexpr uint32_t ONES = ACT == 0 ? 0x3f803f80u : 0x3c003c00u;   // 1.0, 1.0
+// LDS barrier for data written to LDS only: waits for this wave's LDS
+// operations, not for its outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Sum V per-lane values over the 64 lanes of a wave.  Halving exchanges first
+// (each lane keeps half of the values and adds its partner's copy of that
+// half), then a butterfly on the last value.  Afterwards lane l holds the
+// total of value index  sum_b bit(l, 5-b) * V/2^(b+1)  (b = 0..log2 V - 1).
+template <int V>
+__device__ __forceinline__ float wave_reduce_multi(const float (&v)[V], int lane) {
+  constexpr int LOGV = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : 4;
+  static_assert((1 << LOGV) == V, "V must be a power of two <= 16");
+  float cur[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) cur[i] = v[i];
+  int n = V;
+#pragma unroll
+  for (int b = 0; b < LOGV; ++b) {
+    const int off = 32 >> b;
+    const bool upper = (lane & off) != 0;
+    n >>= 1;
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      if (i < n) {
+        const float keep = upper ? cur[i + n] : cur[i];
+        const float send = upper ? cur[i] : cur[i + n];
+        cur[i] = keep + __shfl_xor(send, off);
+      }
+    }
+  }
+  float s = cur[0];
+#pragma unroll
+  for (int off = 32 >> LOGV; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
+template <int V>
+__device__ __forceinline__ int reduced_index(int lane) {
+  int idx = 0, n = V;
+#pragma unroll
+  for (int b = 0; (1 << b) < V; ++b) {
+    n >>= 1;
+    if (lane & (32 >> b)) idx += n;
+  }
+  return idx;
+}
+
+// Geometry of one bit-width.
+template <int BITS>
+struct Geo {
+  static constexpr int G = BITS == 4 ? 128 : 64;       // group size
+  static constexpr int KPL = 128 / BITS;                // k per lane per slice
+  static constexpr int SK = KPL * kLanes;               // k per slice
+  static constexpr int PW = KPL / 2;                    // activation pair words per lane-slice
+  static constexpr int NSUM = BITS == 4 ? 1 : 2;        // floats per lane-slice in the sum table
+};
+
+// Stage x[:, k0 : k0 + nslice*SK] into LDS:
+//   pairs: uint4 [m][slice][quad q][lane]  words 4q..4q+3 of the lane's pair list
+//   sums:  float [m][slice][s][lane]       INT4: sum x; INT2: sum x and B*(X1+X4/4+X16/16)
+// Units are (m, slice, lane) triples of KPL activations; each thread stages
+// up to kStageUnits of them.  stage_x_load issues the global loads,
+// stage_x_store waits for them and writes LDS, so code loads issued in
+// between are not waited for.
+template <int BITS>
+struct StageRegs {
+  uint32_t raw[kStageUnits][Geo<BITS>::PW];
+};
+
+template <int BITS, int M>
+__device__ __forceinline__ void stage_x_load(StageRegs<BITS> &st, const uint16_t *__restrict__ x,
+                                             int K, int k0, int nslice) {
+  using Gm = Geo<BITS>;
+  const int units = M * nslice * kLanes;
+#pragma unroll
+  for (int u = 0; u < kStageUnits; ++u) {
+    const int unit = (int)threadIdx.x + u * kThreads;
+    const int lane = unit & (kLanes - 1);
+    const int ms = unit >> 6;                   // m * nslice + slice
+    const int m = ms / nslice, sl = ms - m * nslice;
+    const int kk = k0 + sl * Gm::SK + lane * Gm::KPL;
+    const bool ok = unit < units && kk < K;     // K is a multiple of KPL
+    // branch-free: an invalid unit loads x[0][0..] and is zeroed (zero pairs
+    // and sums)
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (ok ? (int64_t)m * K + kk : 0));
+    const uint32_t keep = ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int v = 0; v < Gm::PW / 4; ++v) {
+      const uint4 t = src[v];
+      st.raw[u][4 * v + 0] = t.x & keep; st.raw[u][4 * v + 1] = t.y & keep;
+      st.raw[u][4 * v + 2] = t.z & keep; st.raw[u][4 * v + 3] = t.w & keep;
+    }
+  }
+}
+
+template <int BITS, int ACT, int M>
+__device__ __forceinline__ void stage_x_store(const StageRegs<BITS> &st, int nslice, uint4 *pairs,
+                                              float *sums) {
+  using Gm = Geo<BITS>;
+  constexpr uint32_t ONES = ACT == 0 ? 0x3f803f80u : 0x3c003c00u;
   constexpr float BIASF = ACT == 0 ? 128.f : 1024.f;
-  constexpr uint32_t MASK = BITS == 4 ? 0x000f000fu : 0x00030003u;
+  const int units = M * nslice * kLanes;
+#pragma unroll
+  for (int u = 0; u < kStageUnits; ++u) {
+    const int unit = (int)threadIdx.x + u * kThreads;
+    if (unit < units) {                         // LDS slot exists
+      const int lane = unit & (kLanes - 1);
+      const int ms = unit >> 6;
+      uint4 *dst = pairs + (ms * (Gm::PW / 4)) * kLanes + lane;
+      float *sdst = sums + (ms * Gm::NSUM) * kLanes + lane;
+      uint32_t p[Gm::PW];
+      if constexpr (BITS == 4) {
+        // word w covers k 8w..8w+7: pairs (k_t, k_{t+4}), t = 0..3
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t *q = &st.raw[u][4 * w];
+          p[4 * w + 0] = pair_lo(q[2], q[0]);
+          p[4 * w + 1] = pair_hi(q[2], q[0]);
+          p[4 * w + 2] = pair_lo(q[3], q[1]);
+          p[4 * w + 3] = pair_hi(q[3], q[1]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s = dot2<ACT>(p[4 * w + t], ONES, s);
+        }
+        sdst[0] = s;
+      } else {
+        // word w covers k 16w..16w+15: pairs (k_i, k_{i+8}); classes by
+        // position in the word: i = 0,3,6 -> 1x, 1,4,7 -> 4x, 2,5 -> 16x
+        float s1 = 0.f, s4 = 0.f, s16 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t *q = &st.raw[u][8 * w];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            p[8 * w + 2 * a] = pair_lo(q[a + 4], q[a]);        // (x_{2a}, x_{2a+8})
+            p[8 * w + 2 * a + 1] = pair_hi(q[a + 4], q[a]);    // (x_{2a+1}, x_{2a+9})
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (i % 3 == 0) s1 = dot2<ACT>(p[8 * w + i], ONES, s1);
+            else if (i % 3 == 1) s4 = dot2<ACT>(p[8 * w + i], ONES, s4);
+            else s16 = dot2<ACT>(p[8 * w + i], ONES, s16);
+          }
+        }
+        sdst[0] = s1 + s4 + s16;
+        sdst[kLanes] = BIASF * fmaf(s16, 0.0625f, fmaf(s4, 0.25f, s1));
+      }
+#pragma unroll
+      for (int q = 0; q < Gm::PW / 4; ++q)
+        dst[q * kLanes] = make_uint4(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+    }
+  }
+}
+
+template <int BITS, int R, int NL>
+struct LoadGroup {
+  uint4 cw[NL][R];
+  uint32_t sb[NL][R];
+  uint32_t zb[NL][R];
+};
+
+template <int BITS, int R, int NL>
+__device__ __forceinline__ void issue_group(LoadGroup<BITS, R, NL> &g, int slice0, int nslice_row,
+                                            int rb, int lane, const uint8_t *const (&crow)[R],
+                                            const uint16_t *const (&srow)[R],
+                                            const uint8_t *const (&zrow)[R]) {
+  using Gm = Geo<BITS>;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int sl = slice0 + i;
+    const int off = sl * 1024 + lane * 16;
+    const bool ok = sl < nslice_row && off < rb;      // lanes past the row end read nothing
+    const int gi = ok ? (sl * Gm::SK + lane * Gm::KPL) / Gm::G : 0;
+    // branch-free: an invalid lane loads the row's first bytes and then
+    // zeroes them (scale 0 makes its contribution exactly 0)
+    // (the loaded values are always consumed, through a mask, so the loads
+    // stay unconditional and the wait counts stay exact)
+    const int offc = ok ? off : 0;
+    const uint32_t keep = ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint4 c = *reinterpret_cast<const uint4 *>(crow[r] + offc);
+      const uint32_t sv = srow[r][gi], zv = zrow[r][gi];
+      g.cw[i][r] = make_uint4(c.x & keep, c.y & keep, c.z & keep, c.w & keep);
+      g.sb[i][r] = sv & keep;
+      g.zb[i][r] = zv & keep;
+    }
+  }
+}
+
+template <int BITS, int ACT, int M, int R, int NL>
+__device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, int slice0,
+                                              int nslice_row, int chunk_slice0, int lane,
+                                              const uint4 *pairs, const float *sums,
+                                              int chunk_nslice, float (&acc)[R][M]) {
+  using Gm = Geo<BITS>;
+  constexpr uint32_t BIAS = ACT == 0 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
+  constexpr float BIASF = ACT == 0 ? 128.f : 1024.f;
+  const uint32_t bias = BIAS;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int sl = slice0 + i;
+    if (sl < nslice_row) {
+    const int lsl = sl - chunk_slice0;          // slice within the staged chunk
+    uint32_t xp[M][Gm::PW];
+    float xs[M], xb[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int ms = m * chunk_nslice + lsl;
+      const uint4 *src = pairs + (ms * (Gm::PW / 4)) * kLanes + lane;
+#pragma unroll
+      for (int q = 0; q < Gm::PW / 4; ++q) {
+        const uint4 t = src[q * kLanes];
+        xp[m][4 * q + 0] = t.x; xp[m][4 * q + 1] = t.y;
+        xp[m][4 * q + 2] = t.z; xp[m][4 * q + 3] = t.w;
+      }
+      const float *s = sums + (ms * Gm::NSUM) * kLanes + lane;
+      xs[m] = s[0];
+      if constexpr (BITS == 2) xb[m] = s[kLanes];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t wv[4] = {g.cw[i][r].x, g.cw[i][r].y, g.cw[i][r].z, g.cw[i][r].w};
+      const float S = f16_bits_to_f32((uint16_t)g.sb[i][r]);
+      const float zz = (float)g.zb[i][r];
+      if constexpr (BITS == 4) {
+        const uint32_t mask = 0x000f000fu;
+        float p[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) p[m] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t qp = and_or(wv[w] >> (4 * t), mask, bias);
+#pragma unroll
+            for (int m = 0; m < M; ++m) p[m] = dot2<ACT>(qp, xp[m][4 * w + t], p[m]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          acc[r][m] = fmaf(S, fmaf(-(BIASF + zz), xs[m], p[m]), acc[r][m]);
+      } else {
+        const uint32_t m1 = 0x00030003u, m4 = 0x000c000cu, m16 = 0x00300030u;
+        float p1[M], p4[M], p16[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) p1[m] = p4[m] = p16[m] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t w0 = wv[w], w6 = wv[w] >> 6, w12 = wv[w] >> 12;
+          const uint32_t q0 = and_or(w0, m1, bias), q1 = and_or(w0, m4, bias);
+          const uint32_t q2 = and_or(w0, m16, bias), q3 = and_or(w6, m1, bias);
+          const uint32_t q4 = and_or(w6, m4, bias), q5 = and_or(w6, m16, bias);
+          const uint32_t q6 = and_or(w12, m1, bias), q7 = and_or(w12, m4, bias);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const uint32_t *xq = &xp[m][8 * w];
+            p1[m] = dot2<ACT>(q0, xq[0], p1[m]);
+            p4[m] = dot2<ACT>(q1, xq[1], p4[m]);
+            p16[m] = dot2<ACT>(q2, xq[2], p16[m]);
+            p1[m] = dot2<ACT>(q3, xq[3], p1[m]);
+            p4[m] = dot2<ACT>(q4, xq[4], p4[m]);
+            p16[m] = dot2<ACT>(q5, xq[5], p16[m]);
+            p1[m] = dot2<ACT>(q6, xq[6], p1[m]);
+            p4[m] = dot2<ACT>(q7, xq[7], p4[m]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          // sum x*q = p1 + p4/4 + p16/16 - B*(X1 + X4/4 + X16/16)
+          const float xq = fmaf(p16[m], 0.0625f, fmaf(p4[m], 0.25f, p1[m])) - xb[m];
+          acc[r][m] = fmaf(S, fmaf(-zz, xs[m], xq), acc[r][m]);
+        }
+      }
+    }
+    }
+  }
+}
+
+// Slices per staged chunk for a bit-width and M: each thread stages at most
+// kStageUnits units and the chunk fits kLdsBytes.
+__host__ __device__ constexpr int chunk_slices(int bits, int M) {
+  const int pw = bits == 4 ? 16 : 32, nsum = bits == 4 ? 1 : 2;
+  const int by_units = kStageUnits * kThreads / (M * kLanes);
+  const int by_lds = kLdsBytes / (M * kLanes * 4 * (pw + nsum));
+  return by_units < by_lds ? by_units : by_lds;
+}
+
+__host__ __device__ constexpr int stage_bytes(int bits, int M, int nslice_row) {
+  const int pw = bits == 4 ? 16 : 32, nsum = bits == 4 ? 1 : 2;
+  const int ch = chunk_slices(bits, M);
+  const int c = nslice_row < ch ? nslice_row : ch;
+  return M * c * kLanes * 4 * (pw + nsum);
+}
+
+// One workgroup: stage x chunk by chunk, stream the wave's R rows.
+template <int BITS, int ACT, int M, int R, int NL>
+__device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &bi, int blk,
+                                           int n0, bool active, const uint16_t *__restrict__ x,
+                                           const uint8_t *__restrict__ codes,
+                                           const uint16_t *__restrict__ scales,
+                                           const uint8_t *__restrict__ zeros,
+                                           uint16_t *__restrict__ y, uint32_t *lds) {
+  using Gm = Geo<BITS>;
   const int lane = threadIdx.x & (kLanes - 1);
   const int K = L.K;
   const int RB = K * BITS / 8;               // bytes per packed row
-  const int GPR = K / G;                     // groups per row
+  const int GPR = K / Gm::G;                 // groups per row
+  const int nslice_row = (RB + 1023) >> 10;
+  // slices per staged chunk: every thread stages at most kStageUnits units
+  // and the chunk fits the LDS budget
+  constexpr int CHUNK = chunk_slices(BITS, M);
+  static_assert(CHUNK >= 1, "chunk");
+  static_assert(CHUNK * M * kLanes * 4 * (Gm::PW + Gm::NSUM) <= kLdsBytes, "lds");
   const int r0 = n0 - blk * L.block_n;
   const uint8_t *crow[R];
   const uint16_t *srow[R];
   const uint8_t *zrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int rr = (n0 + r < L.N) ? r0 + r : r0;     // ragged tail: recompute row 0
+    // rows past N (ragged tail, or a wave past the end) read a valid row and
+    // never store
+    const int rr = (n0 + r < L.N) ? r0 + r : (r0 < L.block_n && n0 < L.N ? r0 : 0);
     crow[r] = codes + bi.code_off + (uint64_t)rr * (uint64_t)RB;
     srow[r] = scales + bi.grp_off + (uint64_t)rr * (uint64_t)GPR;
     zrow[r] = zeros + bi.grp_off + (uint64_t)rr * (uint64_t)GPR;
   }
+  // the LDS arena holds min(CHUNK, nslice_row) slices: pairs, then sums
+  const int cslices = nslice_row < CHUNK ? nslice_row : CHUNK;
+  uint4 *pairs = reinterpret_cast<uint4 *>(lds);
+  float *sums = reinterpret_cast<float *>(lds + M * cslices * Gm::PW * kLanes);
   float acc[R][M];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
-  for (int off = lane * 16; off < RB; off += kLanes * 16) {
-    const int k0 = off * (8 / BITS);
-    const int gi = k0 / G;
-    uint4 cw[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) cw[r] = *reinterpret_cast<const uint4 *>(crow[r] + off);
-    uint32_t xr[M][XR];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint4 *xp = reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k0);
-#pragma unroll
-      for (int v = 0; v < XR / 4; ++v) {
-        const uint4 t = xp[v];
-        xr[m][4 * v + 0] = t.x; xr[m][4 * v + 1] = t.y;
-        xr[m][4 * v + 2] = t.z; xr[m][4 * v + 3] = t.w;
+  if (nslice_row <= NL && nslice_row <= CHUNK) {
+    // whole row in one load group and one staged chunk: straight-line code,
+    // so slice i waits only for the loads issued before it
+    LoadGroup<BITS, R, NL> g;
+    StageRegs<BITS> st;
+    stage_x_load<BITS, M>(st, x, K, 0, nslice_row);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_group<BITS, R, NL>(g, 0, nslice_row, RB, lane, crow, srow, zrow);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_x_store<BITS, ACT, M>(st, nslice_row, pairs, sums);
+    lds_barrier();
+    compute_group<BITS, ACT, M, R, NL>(g, 0, nslice_row, 0, lane, pairs, sums, nslice_row, acc);
+  } else {
+    for (int c0 = 0; c0 < nslice_row; c0 += CHUNK) {
+      const int cn = nslice_row - c0 < CHUNK ? nslice_row - c0 : CHUNK;
+      const int cend = c0 + cn;
+      if (c0 > 0) lds_barrier();               // previous chunk fully read
+      LoadGroup<BITS, R, NL> g;
+      StageRegs<BITS> st;
+      stage_x_load<BITS, M>(st, x, K, c0 * Gm::SK, cn);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_group<BITS, R, NL>(g, c0, cend, RB, lane, crow, srow, zrow);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_x_store<BITS, ACT, M>(st, cn, pairs, sums);
+      lds_barrier();
+      for (int s = c0;;) {
+        compute_group<BITS, ACT, M, R, NL>(g, s, cend, c0, lane, pairs, sums, cn, acc);
+        s += NL;
+        if (s >= cend) break;
+        issue_group<BITS, R, NL>(g, s, cend, RB, lane, crow, srow, zrow);
       }
-    }
-    float sc[R], zb[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      sc[r] = f16_bits_to_f32(srow[r][gi]);
-      zb[r] = BIASF + (float)zrow[r][gi];
-    }
-    // activation pairs in the order the code pairs come out of a word, and
-    // the sum of the lane's activations per row of x.
-    uint32_t xp[M][XR];
-    float xs[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t *q = &xr[m][w * (XR / 4)];
-        if constexpr (BITS == 4) {
-          xp[m][4 * w + 0] = pair_lo(q[2], q[0]);
-          xp[m][4 * w + 1] = pair_hi(q[2], q[0]);
-          xp[m][4 * w + 2] = pair_lo(q[3], q[1]);
-          xp[m][4 * w + 3] = pair_hi(q[3], q[1]);
-        } else {
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            xp[m][8 * w + 2 * a + 0] = pair_lo(q[a + 4], q[a]);
-            xp[m][8 * w + 2 * a + 1] = pair_hi(q[a + 4], q[a]);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < XR / 4; ++i) s = dot2<ACT>(q[i], ONES, s);
-      }
-      xs[m] = s;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t wv[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
-      float p[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) p[m] = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int i = 0; i < 32 / BITS / 2; ++i) {
-          const uint32_t qp = ((wv[w] >> (BITS * i)) & MASK) | BIAS;
-#pragma unroll
-          for (int m = 0; m < M; ++m) p[m] = dot2<ACT>(qp, xp[m][(32 / BITS / 2) * w + i], p[m]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc[r], fmaf(-zb[r], xs[m], p[m]), acc[r][m]);
     }
   }
-  // wave reduction, then lane 0 stores
+  if (!active) return;
+  // wave reduction of the R*M partial sums, then one lane per value stores
+  constexpr int V0 = R * M;
+  constexpr int V = V0 <= 1 ? 1 : V0 <= 2 ? 2 : V0 <= 4 ? 4 : V0 <= 8 ? 8 : 16;
+  float vals[V];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float v = acc[r][m];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-      acc[r][m] = v;
-    }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (n0 + r >= L.N) break;
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float v = acc[r][m];
-        y[(int64_t)m * L.N + n0 + r] = ACT == 0 ? f32_to_bf16_rne(v) : f32_to_f16_bits(v);
-      }
-    }
+  for (int v = 0; v < V; ++v) vals[v] = v < V0 ? acc[v / M][v % M] : 0.f;
+  const float tot = wave_reduce_multi<V>(vals, lane);
+  const int idx = reduced_index<V>(lane);
+  if ((lane & ((64 / V) - 1)) == 0 && idx < V0) {
+    const int r = idx / M, m = idx % M;
+    if (n0 + r < L.N)
+      y[(int64_t)m * L.N + n0 + r] = ACT == 0 ? f32_to_bf16_rne(tot) : f32_to_f16_bits(tot);
   }
 }
 
 // BITSEL: 4 or 2 for a uniform (Layer-mix) linear, 0 for a Channel-mix
-// layout where each wave reads its block's width from the bit mask.
-template <int ACT, int M, int R, int BITSEL>
-__global__ __launch_bounds__(kWaves * kLanes) void gemv_kernel(LayoutDev L,
-                                                               const uint16_t *__restrict__ x,
-                                                               const uint8_t *__restrict__ codes,
-                                                               const uint16_t *__restrict__ scales,
-                                                               const uint8_t *__restrict__ zeros,
-                                                               uint16_t *__restrict__ y) {
+// layout where the workgroup reads its block's width from the bit mask (the
+// 4R rows of a workgroup never straddle two blocks).
+template <int ACT, int M, int R, int NL, int BITSEL>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint16_t *__restrict__ x,
+                                                        const uint8_t *__restrict__ codes,
+                                                        const uint16_t *__restrict__ scales,
+                                                        const uint8_t *__restrict__ zeros,
+                                                        uint16_t *__restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-  const int n0 = ((int)blockIdx.x * kWaves + wave) * R;
-  if (n0 >= L.N) return;
+  const int nb = (int)blockIdx.x * kWaves * R;
+  const int n0 = nb + wave * R;
+  const bool active = n0 < L.N;                // inactive waves still stage x
   if constexpr (BITSEL == 4) {
     BlockInfo bi = {4, 0, 0};
-    gemv_rows<4, ACT, M, R>(L, bi, 0, n0, x, codes, scales, zeros, y);
+    gemv_block<4, ACT, M, R, NL>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
   } else if constexpr (BITSEL == 2) {
     BlockInfo bi = {2, 0, 0};
-    gemv_rows<2, ACT, M, R>(L, bi, 0, n0, x, codes, scales, zeros, y);
+    gemv_block<2, ACT, M, R, NL>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
   } else {
-    const int blk = n0 / L.block_n;
+    const int blk = nb / L.block_n;
     const BlockInfo bi = block_info(L, blk);
     if (__builtin_amdgcn_readfirstlane(bi.bits) == 4)
-      gemv_rows<4, ACT, M, R>(L, bi, blk, n0, x, codes, scales, zeros, y);
+      gemv_block<4, ACT, M, R, NL>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
     else
-      gemv_rows<2, ACT, M, R>(L, bi, blk, n0, x, codes, scales, zeros, y);
+      gemv_block<2, ACT, M, R, NL>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
   }
 }
 
-template <int ACT, int M, int R>
-hipError_t launch_rows(const LayoutDev &L, const void *x, const uint32_t *codes,
+template <int ACT, int M, int R, int NL>
+hipError_t launch_rows(const LayoutDev &L, int bitsel, const void *x, const uint32_t *codes,
                        const uint16_t *scales, const uint8_t *zeros, void *y, hipStream_t s) {
-  const int waves = (L.N + R - 1) / R;
-  const int blocks = (waves + kWaves - 1) / kWaves;
+  const int blocks = (L.N + kWaves * R - 1) / (kWaves * R);
   const uint16_t *xp = reinterpret_cast<const uint16_t *>(x);
   const uint8_t *cp = reinterpret_cast<const uint8_t *>(codes);
   uint16_t *yp = reinterpret_cast<uint16_t *>(y);
-  // uniform layouts get a kernel specialised on the bit-width
-  uint32_t any4 = 0, all4 = ~0u;
-  for (int i = 0; i < L.nblocks; ++i) {
-    const uint32_t b = (L.int4_mask[i >> 5] >> (i & 31)) & 1u;
-    any4 |= b;
-    all4 &= b;
-  }
-  if (all4)
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, 4>), dim3(blocks), dim3(kWaves * kLanes), 0, s, L, xp,
-                       cp, scales, zeros, yp);
-  else if (!any4)
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, 2>), dim3(blocks), dim3(kWaves * kLanes), 0, s, L, xp,
-                       cp, scales, zeros, yp);
+  const dim3 g(blocks), b(kThreads);
+  const int s4 = stage_bytes(4, M, (L.K * 4 / 8 + 1023) / 1024);
+  const int s2 = stage_bytes(2, M, (L.K * 2 / 8 + 1023) / 1024);
+  if (bitsel == 4)
+    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 4>), g, b, s4, s, L, xp, cp, scales, zeros, yp);
+  else if (bitsel == 2)
+    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
   else
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, 0>), dim3(blocks), dim3(kWaves * kLanes), 0, s, L, xp,
-                       cp, scales, zeros, yp);
+    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0>), g, b, s4 > s2 ? s4 : s2, s, L, xp, cp, scales,
+                       zeros, yp);
   return hipGetLastError();
 }
 
 template <int ACT, int M>
 hipError_t launch_m(const LayoutDev &L, const void *x, const uint32_t *codes,
                     const uint16_t *scales, const uint8_t *zeros, void *y, hipStream_t s) {
-  // Rows per wave: as many as keep >= 1024 waves in flight (4 per CU), so
-  // each activation load is shared by several packed rows; fewer rows for
-  // larger M to bound the accumulator registers.
-  constexpr int RMAX = M <= 2 ? 8 : 4;
-  if (RMAX >= 8 && (L.N + 7) / 8 >= 1024) return launch_rows<ACT, M, 8>(L, x, codes, scales, zeros, y, s);
-  if ((L.N + 3) / 4 >= 1024) return launch_rows<ACT, M, 4>(L, x, codes, scales, zeros, y, s);
-  if ((L.N + 1) / 2 >= 1024) return launch_rows<ACT, M, 2>(L, x, codes, scales, zeros, y, s);
-  return launch_rows<ACT, M, 1>(L, x, codes, scales, zeros, y, s);
+  uint32_t any4 = 0, all4 = ~0u;
+  for (int i = 0; i < L.nblocks; ++i) {
+    const uint32_t b = (L.int4_mask[i >> 5] >> (i & 31)) & 1u;
+    any4 |= b;
+    all4 &= b;
+  }
+  const int bitsel = all4 ? 4 : (any4 ? 0 : 2);
+  // slices per row (of the widest block) decide the load-group size NL; rows
+  // per wave R keep R*NL <= 16 loads of 16 bytes in flight per lane and, when
+  // possible, >= 1024 waves on the chip
+  const int ns = (L.K * (any4 ? 4 : 2) / 8 + 1023) / 1024;
+  const int waves4 = (L.N + 3) / 4, waves2 = (L.N + 1) / 2;
+  if (ns <= 1) {
+    if (waves4 >= 1024) return launch_rows<ACT, M, 4, 1>(L, bitsel, x, codes, scales, zeros, y, s);
+    if (waves2 >= 1024) return launch_rows<ACT, M, 2, 1>(L, bitsel, x, codes, scales, zeros, y, s);
+    return launch_rows<ACT, M, 1, 1>(L, bitsel, x, codes, scales, zeros, y, s);
+  }
+  if (ns <= 2) {
+    if (waves4 >= 1024) return launch_rows<ACT, M, 4, 2>(L, bitsel, x, codes, scales, zeros, y, s);
+    if (waves2 >= 1024) return launch_rows<ACT, M, 2, 2>(L, bitsel, x, codes, scales, zeros, y, s);
+    return launch_rows<ACT, M, 1, 2>(L, bitsel, x, codes, scales, zeros, y, s);
+  }
+  if (ns <= 4) {
+    if (waves4 >= 1024) return launch_rows<ACT, M, 4, 4>(L, bitsel, x, codes, scales, zeros, y, s);
+    if (waves2 >= 1024) return launch_rows<ACT, M, 2, 4>(L, bitsel, x, codes, scales, zeros, y, s);
+    return launch_rows<ACT, M, 1, 4>(L, bitsel, x, codes, scales, zeros, y, s);
+  }
+  if (waves2 >= 1024) return launch_rows<ACT, M, 2, 8>(L, bitsel, x, codes, scales, zeros, y, s);
+  return launch_rows<ACT, M, 1, 8>(L, bitsel, x, codes, scales, zeros, y, s);
 }
 
 template <int ACT>
