@@ -91,89 +91,114 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
 
 // ------------------------------------------------------------------- GEMM
 
+// (a & m) | o in one VALU op (operands in VGPRs; gfx9 VOP3 takes no
+// literal constants).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// LDS-only barrier: waits for this wave's LDS traffic, not for its
+// outstanding global loads (the next tile's prefetch stays in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Unpack the 8 codes of one 8-k chunk into 4 packed fp16 pairs (q - z) * s,
 // pair i holding chunk elements (i, i + 4).  `t` carries the chunk's codes
 // with element i at bits [B*i, B*i + B) of its low half (elements 0..3) and
 // element 4 + i at the same bits of its high half.
 template <int B>
 __device__ __forceinline__ void unpack_chunk(uint32_t t, half2v cz, half2v s2, half8 &out) {
-  constexpr uint32_t MASK = B == 4 ? 0x000f000fu : 0x00030003u;
+  const uint32_t mask = B == 4 ? 0x000f000fu : 0x00030003u;
+  const uint32_t bias = 0x64006400u;                             // 1024.0 pairs
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t p = ((t >> (B * i)) & MASK) | 0x64006400u;   // 1024 + q, exact
+    const uint32_t p = and_or(t >> (B * i), mask, bias);         // 1024 + q, exact
     half2v v = __builtin_bit_cast(half2v, p);
-    v = (v + cz) * s2;                                          // (q - z) exact, then * s
+    v = (v + cz) * s2;                                           // (q - z) exact, then * s
     out[2 * i] = v.x;
     out[2 * i + 1] = v.y;
   }
 }
 
+constexpr int KT = 128;                   // k per main-loop step
+constexpr int LDA = KT + 8;               // halfs per LDS row (conflict-free b128 reads)
+
 struct GemmArgs {
   int K, N, M, m0, nw;
+  int kt0, nkt;                           // first k step and number of k steps
   const uint16_t *xa;
   const int *rexp;
-  uint16_t *y;
+  uint16_t *y;                            // bf16/fp16 output (split == 0)
+  float *part;                            // fp32 partial [M][N] of this split (split != 0)
   int out_fp16;
 };
 
 // Main loop and epilogue of one wave; BITS is the bit-width of the wave's
 // 64 columns (one Channel-mix block never splits a wave).  Every wave of the
-// workgroup runs the same number of k steps and barriers, including waves
+// workgroup runs the same number of steps and barriers, including waves
 // whose columns lie beyond N (they only help load the x tile).
-template <int BITS, int MB>
-__device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 * MB * 72],
+template <int BITS, int MB, bool SPLIT>
+__device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 * MB * LDA],
                                           bool wave_active, const uint8_t *const *crow,
                                           const uint16_t *const *srow, const uint8_t *const *zrow,
                                           const bool *cvalid) {
-  constexpr int LDA = 72;                 // halfs per LDS row: 64 + 8 padding
+  constexpr int RPP = 256 / 16;           // A rows per load pass (16 threads per 256-byte row)
+  constexpr int PASSES = 32 * MB / RPP;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = lane & 31;
   const int h = lane >> 5;
   const int K = g.K;
 
-  // A tile loads: thread -> (row = p*32 + tid/8, 16-byte chunk tid%8)
-  const int arow = tid >> 3;
-  const int achunk = tid & 7;
-  uint4 areg[MB];
+  // A tile loads: thread -> (row = p*16 + tid/16, 16-byte chunk tid%16)
+  const int arow = tid >> 4;
+  const int achunk = tid & 15;
+  uint4 areg[PASSES];
   auto load_a = [&](int kt) {
 #pragma unroll
-    for (int p = 0; p < MB; ++p) {
-      const int m = g.m0 + p * 32 + arow;
-      if (m < g.M)
-        areg[p] = *reinterpret_cast<const uint4 *>(g.xa + (int64_t)m * K + kt * 64 + achunk * 8);
-      else
-        areg[p] = make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < PASSES; ++p) {
+      const int m = g.m0 + p * RPP + arow;
+      const int kk = kt * KT + achunk * 8;
+      const bool ok = m < g.M && kk < K;              // rows past M, k past K (INT2 tail) read 0
+      const int mc = m < g.M ? m : g.M - 1;           // clamped: always a valid address
+      const uint4 v = *reinterpret_cast<const uint4 *>(g.xa + (int64_t)mc * K + (kk < K ? kk : 0));
+      const uint32_t keep = ok ? 0xffffffffu : 0u;
+      areg[p] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < MB; ++p)
-      *reinterpret_cast<uint4 *>(&As[buf][(p * 32 + arow) * LDA + achunk * 8]) = areg[p];
+    for (int p = 0; p < PASSES; ++p)
+      *reinterpret_cast<uint4 *>(&As[buf][(p * RPP + arow) * LDA + achunk * 8]) = areg[p];
   };
-  // B code loads: lane half h takes chunks 4h..4h+3 of the 64-deep k step.
-  uint4 bcur[2], bnext[2];
-  auto load_b = [&](int kt, uint4 *dst) {
+  // B codes: lane half h takes chunks 8h..8h+7 of the step (INT4: 8 words,
+  // INT2: 4 words); both halves of an INT4 step share one group, each INT2
+  // half lies in its own group.
+  constexpr int BW = BITS == 4 ? 8 : 4;   // code words per lane per step
+  uint32_t bcur[2][BW], bnext[2][BW];
+  uint32_t scur[2], snext[2], zcur[2], znext[2];
+  auto load_b = [&](int kt, uint32_t (*dst)[BW], uint32_t *sd, uint32_t *zd) {
+    // the half step past K (INT2 layers with K % 128 == 64) reads row start
+    // and gets scale 0, so it adds exactly 0
+    const bool kok = kt * KT + h * (KT / 2) < K;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      if constexpr (BITS == 4) {
-        dst[nb] = *reinterpret_cast<const uint4 *>(crow[nb] + kt * 32 + h * 16);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2 *>(crow[nb] + kt * 16 + h * 8);
-        dst[nb] = make_uint4(v.x, v.y, 0, 0);
+      const uint8_t *src = crow[nb] + (kok ? (size_t)kt * (KT * BITS / 8) + h * (BW * 4) : 0);
+#pragma unroll
+      for (int q = 0; q < BW / 4; ++q) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(src + 16 * q);
+        dst[nb][4 * q + 0] = v.x; dst[nb][4 * q + 1] = v.y;
+        dst[nb][4 * q + 2] = v.z; dst[nb][4 * q + 3] = v.w;
       }
-    }
-  };
-  half2v cz[2], s2[2];
-  auto load_scale = [&](int kt) {
-    const int gi = BITS == 4 ? (kt >> 1) : kt;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint16_t sb = cvalid[nb] ? srow[nb][gi] : (uint16_t)0;
-      const float z = (float)zrow[nb][gi];
-      const uint16_t zb = f32_to_f16_bits(-(1024.f + z));
-      s2[nb] = __builtin_bit_cast(half2v, (uint32_t)sb | ((uint32_t)sb << 16));
-      cz[nb] = __builtin_bit_cast(half2v, (uint32_t)zb | ((uint32_t)zb << 16));
+      const int gi = kok ? (BITS == 4 ? kt : 2 * kt + h) : 0;
+      const uint32_t keep = (cvalid[nb] && kok) ? 0xffffffffu : 0u;   // invalid: scale 0
+      sd[nb] = (uint32_t)srow[nb][gi] & keep;
+      zd[nb] = (uint32_t)zrow[nb][gi];
     }
   };
 
@@ -185,53 +210,63 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
 
-  const int KT = K / 64;
-  load_a(0);
-  if (wave_active) load_b(0, bcur);
+  const int kend = g.kt0 + g.nkt;
+  load_a(g.kt0);
+  load_b(g.kt0, bcur, scur, zcur);
   store_a(0);
-  __syncthreads();
+  lds_barrier();
   int cur = 0;
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a(kt + 1);
-      if (wave_active) load_b(kt + 1, bnext);
+  for (int kt = g.kt0; kt < kend; ++kt) {
+    // prefetch the next step; on the last step reload the same step (the
+    // loads stay unconditional so the wait counts are exact)
+    const int kn = kt + 1 < kend ? kt + 1 : kt;
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kn);
+    load_b(kn, bnext, snext, znext);
+    __builtin_amdgcn_sched_barrier(0);
+    half2v cz[2], s2[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint16_t zb = f32_to_f16_bits(-(1024.f + (float)zcur[nb]));
+      s2[nb] = __builtin_bit_cast(half2v, scur[nb] | (scur[nb] << 16));
+      cz[nb] = __builtin_bit_cast(half2v, (uint32_t)zb | ((uint32_t)zb << 16));
     }
-    if (wave_active) {
-      load_scale(kt);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        half8 bf[2];
+    for (int t = 0; t < 8; ++t) {
+      half8 bf[2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          if constexpr (BITS == 4) {
-            const uint32_t wv[4] = {bcur[nb].x, bcur[nb].y, bcur[nb].z, bcur[nb].w};
-            unpack_chunk<4>(wv[t], cz[nb], s2[nb], bf[nb]);
-          } else {
-            const uint32_t wv = (t >> 1) ? bcur[nb].y : bcur[nb].x;
-            // bytes (b0, b0, b1, b1) for the low chunk, (b2, b2, b3, b3) for the high one
-            const uint32_t tc = __builtin_amdgcn_perm(wv, wv, (t & 1) ? 0x03030202u : 0x01010000u);
-            unpack_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
-          }
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const half8 af =
-              *reinterpret_cast<const half8 *>(&As[cur][(mb * 32 + j) * LDA + (4 * h + t) * 8]);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb], acc[mb][nb], 0, 0, 0);
+      for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (BITS == 4) {
+          unpack_chunk<4>(bcur[nb][t], cz[nb], s2[nb], bf[nb]);
+        } else {
+          const uint32_t wv = bcur[nb][t >> 1];
+          // bytes (b0, b0, b1, b1) for the low chunk, (b2, b2, b3, b3) for the high one
+          const uint32_t tc = __builtin_amdgcn_perm(wv, wv, (t & 1) ? 0x03030202u : 0x01010000u);
+          unpack_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
         }
       }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const half8 af =
+            *reinterpret_cast<const half8 *>(&As[cur][(mb * 32 + j) * LDA + (8 * h + t) * 8]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb], acc[mb][nb], 0, 0, 0);
+      }
     }
-    if (more) store_a(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(cur ^ 1);
+    lds_barrier();
     cur ^= 1;
-    if (more && wave_active) {
-      bcur[0] = bnext[0];
-      bcur[1] = bnext[1];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int w = 0; w < BW; ++w) bcur[nb][w] = bnext[nb][w];
+      scur[nb] = snext[nb];
+      zcur[nb] = znext[nb];
     }
   }
+  (void)wave_active;
 
   if (!wave_active) return;
   // epilogue: lane (j, h) holds column nw + 32nb + j and rows 8(e/4) + 4h + e%4
@@ -241,75 +276,130 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
     for (int e = 0; e < 16; ++e) {
       const int m = g.m0 + mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
       if (m >= g.M) continue;
-      const int ex = g.rexp[m];
+      const int ex = SPLIT ? 0 : g.rexp[m];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int n = g.nw + 32 * nb + j;
         if (n >= g.N) continue;
-        const float v = ldexpf(acc[mb][nb][e], ex);
-        g.y[(int64_t)m * g.N + n] = g.out_fp16 ? f32_to_f16_bits(v) : f32_to_bf16_rne(v);
+        if constexpr (SPLIT) {
+          g.part[(int64_t)m * g.N + n] = acc[mb][nb][e];
+        } else {
+          const float v = ldexpf(acc[mb][nb][e], ex);
+          g.y[(int64_t)m * g.N + n] = g.out_fp16 ? f32_to_f16_bits(v) : f32_to_bf16_rne(v);
+        }
       }
     }
   }
 }
 
-template <int MB>
-__global__ __launch_bounds__(256) void gemm_kernel(LayoutDev L, int M, int m_tiles,
+template <int MB, bool SPLIT>
+__global__ __launch_bounds__(256) void gemm_kernel(LayoutDev L, int M, int m_tiles, int n_tiles,
+                                                   int ksteps_per_split,
                                                    const uint16_t *__restrict__ xa,
                                                    const int *__restrict__ rexp,
                                                    const uint8_t *__restrict__ codes,
                                                    const uint16_t *__restrict__ scales,
                                                    const uint8_t *__restrict__ zeros,
-                                                   uint16_t *__restrict__ y, int out_fp16) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][32 * MB * 72];
+                                                   uint16_t *__restrict__ y, float *__restrict__ part,
+                                                   int out_fp16) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][32 * MB * LDA];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = threadIdx.x & 31;
-  const int m_tile = (int)blockIdx.x % m_tiles;
-  const int n_tile = (int)blockIdx.x / m_tiles;
+  // tile order: m fastest, so the workgroups resident at one time share the
+  // same packed-weight columns
+  const int tile = (int)blockIdx.x;
+  const int m_tile = tile % m_tiles;
+  const int n_tile = tile / m_tiles;
+  const int split = (int)blockIdx.y;
   GemmArgs g;
   g.K = L.K; g.N = L.N; g.M = M;
   g.m0 = m_tile * 32 * MB;
   g.nw = n_tile * 256 + wave * 64;
+  const int ksteps = (L.K + KT - 1) / KT;
+  g.kt0 = split * ksteps_per_split;
+  g.nkt = ksteps - g.kt0 < ksteps_per_split ? ksteps - g.kt0 : ksteps_per_split;
   g.xa = xa; g.rexp = rexp; g.y = y; g.out_fp16 = out_fp16;
+  g.part = part + (int64_t)split * M * L.N;
   const bool wave_active = g.nw < L.N;
 
   int bits = 4;
-  const uint8_t *crow[2] = {codes, codes};
-  const uint16_t *srow[2] = {scales, scales};
-  const uint8_t *zrow[2] = {zeros, zeros};
-  bool cvalid[2] = {false, false};
-  if (wave_active) {
-    const int blk = g.nw / L.block_n;
-    const BlockInfo bi = block_info(L, blk);
-    bits = __builtin_amdgcn_readfirstlane(bi.bits);
-    const int RB = L.K * bits / 8;
-    const int GPR = bits == 4 ? L.K / 128 : L.K / 64;
+  const uint8_t *crow[2];
+  const uint16_t *srow[2];
+  const uint8_t *zrow[2];
+  bool cvalid[2];
+  // waves past N read column 0's block (valid memory) and never store
+  const int nref = wave_active ? g.nw : 0;
+  const int blk = nref / L.block_n;
+  const BlockInfo bi = block_info(L, blk);
+  bits = __builtin_amdgcn_readfirstlane(bi.bits);
+  const int RB = L.K * bits / 8;
+  const int GPR = bits == 4 ? L.K / 128 : L.K / 64;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int n = g.nw + 32 * nb + j;
-      cvalid[nb] = n < L.N;
-      const int r = (cvalid[nb] ? n : g.nw) - blk * L.block_n;
-      crow[nb] = codes + bi.code_off + (uint64_t)r * (uint64_t)RB;
-      srow[nb] = scales + bi.grp_off + (uint64_t)r * (uint64_t)GPR;
-      zrow[nb] = zeros + bi.grp_off + (uint64_t)r * (uint64_t)GPR;
-    }
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = nref + 32 * nb + j;
+    cvalid[nb] = wave_active && n < L.N;
+    const int r = (cvalid[nb] ? n : nref) - blk * L.block_n;
+    crow[nb] = codes + bi.code_off + (uint64_t)r * (uint64_t)RB;
+    srow[nb] = scales + bi.grp_off + (uint64_t)r * (uint64_t)GPR;
+    zrow[nb] = zeros + bi.grp_off + (uint64_t)r * (uint64_t)GPR;
   }
+  (void)n_tiles;
   if (bits == 4)
-    gemm_wave<4, MB>(g, As, wave_active, crow, srow, zrow, cvalid);
+    gemm_wave<4, MB, SPLIT>(g, As, wave_active, crow, srow, zrow, cvalid);
   else
-    gemm_wave<2, MB>(g, As, wave_active, crow, srow, zrow, cvalid);
+    gemm_wave<2, MB, SPLIT>(g, As, wave_active, crow, srow, zrow, cvalid);
+}
+
+// Sum the split-K partials in split order, rescale by 2^e, round.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int splits,
+                                                            int M, int N, const int *__restrict__ rexp,
+                                                            uint16_t *__restrict__ y, int out_fp16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)M * N;
+  if (i >= total) return;
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + i];
+  const int m = (int)(i / N);
+  const float v = ldexpf(s, rexp[m]);
+  y[i] = out_fp16 ? f32_to_f16_bits(v) : f32_to_bf16_rne(v);
 }
 
 template <int MB>
-hipError_t launch_tiles(const LayoutDev &L, int M, const uint16_t *xa, const int *rexp,
+hipError_t launch_tiles(const LayoutDev &L, int M, int splits, const uint16_t *xa, const int *rexp,
                         const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
-                        void *y, int out_fp16, hipStream_t s) {
+                        void *y, float *part, int out_fp16, hipStream_t s) {
   const int m_tiles = (M + 32 * MB - 1) / (32 * MB);
   const int n_tiles = (L.N + 255) / 256;
-  hipLaunchKernelGGL(gemm_kernel<MB>, dim3(m_tiles * n_tiles), dim3(256), 0, s, L, M, m_tiles,
-                     xa, rexp, reinterpret_cast<const uint8_t *>(codes), scales, zeros,
-                     reinterpret_cast<uint16_t *>(y), out_fp16);
+  const int ksteps = (L.K + KT - 1) / KT;
+  const int per = (ksteps + splits - 1) / splits;
+  const int nsplit = (ksteps + per - 1) / per;
+  const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);
+  uint16_t *yp = reinterpret_cast<uint16_t *>(y);
+  if (nsplit == 1) {
+    hipLaunchKernelGGL((gemm_kernel<MB, false>), dim3(m_tiles * n_tiles, 1), dim3(256), 0, s, L, M,
+                       m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_kernel<MB, true>), dim3(m_tiles * n_tiles, nsplit), dim3(256), 0, s, L, M,
+                     m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)M * L.N;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     part, nsplit, M, L.N, rexp, yp, out_fp16);
   return hipGetLastError();
+}
+
+// Split-K factor: enough workgroups to cover the CUs twice when the tile
+// grid alone is small; the K range of a split stays >= 4 steps.
+inline int choose_splits(const LayoutDev &L, int M, int mb) {
+  const int m_tiles = (M + 32 * mb - 1) / (32 * mb);
+  const int n_tiles = (L.N + 255) / 256;
+  const int tiles = m_tiles * n_tiles;
+  const int ksteps = (L.K + KT - 1) / KT;
+  int sp = 1;
+  while (tiles * sp < 512 && ksteps / (sp * 2) >= 4 && sp < 16) sp *= 2;
+  return sp;
 }
 
 }  // namespace
@@ -318,8 +408,10 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
                        const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                        void *y, void *workspace, hipStream_t s) {
   const size_t a_bytes = ((size_t)M * (size_t)L.K * 2u + 255u) & ~(size_t)255u;
+  const size_t e_bytes = ((size_t)M * 4u + 255u) & ~(size_t)255u;
   uint16_t *xa = reinterpret_cast<uint16_t *>(workspace);
   int *rexp = reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) + a_bytes);
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + a_bytes + e_bytes);
   const uint16_t *xin = reinterpret_cast<const uint16_t *>(x);
   if (act == GQ_BF16)
     hipLaunchKernelGGL(prep_x_kernel<0>, dim3(M), dim3(256), 0, s, xin, L.K, xa, rexp);
@@ -328,9 +420,19 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int out_fp16 = act == GQ_FP16 ? 1 : 0;
-  if (M <= 32) return launch_tiles<1>(L, M, xa, rexp, codes, scales, zeros, y, out_fp16, s);
-  if (M <= 64) return launch_tiles<2>(L, M, xa, rexp, codes, scales, zeros, y, out_fp16, s);
-  return launch_tiles<4>(L, M, xa, rexp, codes, scales, zeros, y, out_fp16, s);
+  const int mb = gemm_mb(M);
+  const int sp = choose_splits(L, M, mb);
+  if (mb == 1) return launch_tiles<1>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  if (mb == 2) return launch_tiles<2>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  return launch_tiles<4>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+}
+
+size_t gemm_workspace_bytes(const LayoutDev &L, int M) {
+  const size_t a_bytes = ((size_t)M * (size_t)L.K * 2u + 255u) & ~(size_t)255u;
+  const size_t e_bytes = ((size_t)M * 4u + 255u) & ~(size_t)255u;
+  const int sp = choose_splits(L, M, gemm_mb(M));
+  const size_t p_bytes = sp > 1 ? (size_t)sp * (size_t)M * (size_t)L.N * 4u : 0u;
+  return a_bytes + e_bytes + p_bytes;
 }
 
 }  // namespace gq

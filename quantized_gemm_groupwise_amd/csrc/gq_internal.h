@@ -63,6 +63,11 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 // Largest M served by the dot-product (GEMV) kernel; larger M goes to MFMA.
 constexpr int kGemvMaxM = 4;
 
+// MFMA tile rows per workgroup, in 32-row blocks, for a given M.
+inline int gemm_mb(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
+// Workspace of the MFMA path: fp16 activations, row exponents, split-K partials.
+size_t gemm_workspace_bytes(const LayoutDev &L, int M);
+
 // ----------------------------------------------------------- device helpers
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.

@@ -40,11 +40,7 @@ gq_status check_ptr16(const void *p) {
 size_t linear_workspace_bytes(const LayoutDev &L, int M, gq_dtype act) {
   (void)act;
   if (M <= kGemvMaxM || L.N == 0) return 0;
-  // fp16 copy of the activations (rescaled per row, permuted inside each
-  // 8-element chunk) followed by one int32 exponent per row.
-  const size_t a = (size_t)M * (size_t)L.K * 2u;
-  const size_t a_al = (a + 255u) & ~(size_t)255u;
-  return a_al + (((size_t)M * 4u + 255u) & ~(size_t)255u);
+  return gemm_workspace_bytes(L, M);
 }
 
 }  // namespace gq

@@ -156,6 +156,8 @@ def test_linear_gemv(M, N, K, block_n, bits):
 @pytest.mark.parametrize("M", [5, 17, 32, 33, 64, 65, 130, 300])
 @pytest.mark.parametrize("N,K,block_n,bits", [
     (512, 512, 512, [4]), (200, 1024, 200, [2]), (384, 768, 128, [2, 4, 2]),
+    (136, 576, 136, [2]),          # K % 128 == 64: half k-step at the end
+    (256, 4096, 128, [4, 2]),      # long K: split-K partials for small M
 ])
 def test_linear_gemm(M, N, K, block_n, bits):
     W = S.decode_weight(3, N=N, K=K)
