@@ -142,13 +142,14 @@ struct GemmArgs {
 // 64 columns (one Channel-mix block never splits a wave).  Every wave of the
 // workgroup runs the same number of steps and barriers, including waves
 // whose columns lie beyond N (they only help load the x tile).
-template <int BITS, int MB, bool SPLIT>
+template <int BITS, int MB, int NW, bool SPLIT>
 __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 * MB * LDA],
                                           bool wave_active, const uint8_t *const *crow,
                                           const uint16_t *const *srow, const uint8_t *const *zrow,
                                           const bool *cvalid) {
-  constexpr int RPP = 256 / 16;           // A rows per load pass (16 threads per 256-byte row)
+  constexpr int RPP = 64 * NW / 16;       // A rows per load pass (16 threads per 256-byte row)
   constexpr int PASSES = 32 * MB / RPP;
+  static_assert(PASSES * RPP == 32 * MB, "A tile rows");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = lane & 31;
@@ -231,9 +232,15 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
       s2[nb] = __builtin_bit_cast(half2v, scur[nb] | (scur[nb] << 16));
       cz[nb] = __builtin_bit_cast(half2v, (uint32_t)zb | ((uint32_t)zb << 16));
     }
+    // software pipeline over the 8 sub-steps of 16 k: the A fragments and
+    // the unpacked B fragments of sub-step t+1 are produced while the MFMAs
+    // of sub-step t run
+    auto read_a = [&](int t, half8 *af) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      half8 bf[2];
+      for (int mb = 0; mb < MB; ++mb)
+        af[mb] = *reinterpret_cast<const half8 *>(&As[cur][(mb * 32 + j) * LDA + (8 * h + t) * 8]);
+    };
+    auto make_b = [&](int t, half8 *bf) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if constexpr (BITS == 4) {
@@ -245,14 +252,19 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
           unpack_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
         }
       }
+    };
+    half8 af[MB], bf[2][2];
+    make_b(0, bf[0]);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const half8 af =
-            *reinterpret_cast<const half8 *>(&As[cur][(mb * 32 + j) * LDA + (8 * h + t) * 8]);
+    for (int t = 0; t < 8; ++t) {
+      const int c = t & 1, n = c ^ 1;
+      read_a(t, af);
+      if (t + 1 < 8) make_b(t + 1, bf[n]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb], acc[mb][nb], 0, 0, 0);
-      }
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bf[c][nb], acc[mb][nb], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     store_a(cur ^ 1);
@@ -292,8 +304,8 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
   }
 }
 
-template <int MB, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_kernel(LayoutDev L, int M, int m_tiles, int n_tiles,
+template <int MB, int NW, bool SPLIT>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(LayoutDev L, int M, int m_tiles, int n_tiles,
                                                    int ksteps_per_split,
                                                    const uint16_t *__restrict__ xa,
                                                    const int *__restrict__ rexp,
@@ -314,7 +326,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(LayoutDev L, int M, int m_til
   GemmArgs g;
   g.K = L.K; g.N = L.N; g.M = M;
   g.m0 = m_tile * 32 * MB;
-  g.nw = n_tile * 256 + wave * 64;
+  g.nw = n_tile * (64 * NW) + wave * 64;
   const int ksteps = (L.K + KT - 1) / KT;
   g.kt0 = split * ksteps_per_split;
   g.nkt = ksteps - g.kt0 < ksteps_per_split ? ksteps - g.kt0 : ksteps_per_split;
@@ -345,9 +357,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LayoutDev L, int M, int m_til
   }
   (void)n_tiles;
   if (bits == 4)
-    gemm_wave<4, MB, SPLIT>(g, As, wave_active, crow, srow, zrow, cvalid);
+    gemm_wave<4, MB, NW, SPLIT>(g, As, wave_active, crow, srow, zrow, cvalid);
   else
-    gemm_wave<2, MB, SPLIT>(g, As, wave_active, crow, srow, zrow, cvalid);
+    gemm_wave<2, MB, NW, SPLIT>(g, As, wave_active, crow, srow, zrow, cvalid);
 }
 
 // Sum the split-K partials in split order, rescale by 2^e, round.
@@ -364,24 +376,24 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   y[i] = out_fp16 ? f32_to_f16_bits(v) : f32_to_bf16_rne(v);
 }
 
-template <int MB>
+template <int MB, int NW>
 hipError_t launch_tiles(const LayoutDev &L, int M, int splits, const uint16_t *xa, const int *rexp,
                         const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                         void *y, float *part, int out_fp16, hipStream_t s) {
   const int m_tiles = (M + 32 * MB - 1) / (32 * MB);
-  const int n_tiles = (L.N + 255) / 256;
+  const int n_tiles = (L.N + 64 * NW - 1) / (64 * NW);
   const int ksteps = (L.K + KT - 1) / KT;
   const int per = (ksteps + splits - 1) / splits;
   const int nsplit = (ksteps + per - 1) / per;
   const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);
   uint16_t *yp = reinterpret_cast<uint16_t *>(y);
   if (nsplit == 1) {
-    hipLaunchKernelGGL((gemm_kernel<MB, false>), dim3(m_tiles * n_tiles, 1), dim3(256), 0, s, L, M,
-                       m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
+    hipLaunchKernelGGL((gemm_kernel<MB, NW, false>), dim3(m_tiles * n_tiles, 1), dim3(64 * NW), 0, s, L,
+                       M, m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_kernel<MB, true>), dim3(m_tiles * n_tiles, nsplit), dim3(256), 0, s, L, M,
-                     m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
+  hipLaunchKernelGGL((gemm_kernel<MB, NW, true>), dim3(m_tiles * n_tiles, nsplit), dim3(64 * NW), 0, s,
+                     L, M, m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = (int64_t)M * L.N;
@@ -394,7 +406,8 @@ hipError_t launch_tiles(const LayoutDev &L, int M, int splits, const uint16_t *x
 // grid alone is small; the K range of a split stays >= 4 steps.
 inline int choose_splits(const LayoutDev &L, int M, int mb) {
   const int m_tiles = (M + 32 * mb - 1) / (32 * mb);
-  const int n_tiles = (L.N + 255) / 256;
+  const int nt = mb == 4 ? 512 : 256;
+  const int n_tiles = (L.N + nt - 1) / nt;
   const int tiles = m_tiles * n_tiles;
   const int ksteps = (L.K + KT - 1) / KT;
   int sp = 1;
@@ -422,9 +435,9 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
   const int out_fp16 = act == GQ_FP16 ? 1 : 0;
   const int mb = gemm_mb(M);
   const int sp = choose_splits(L, M, mb);
-  if (mb == 1) return launch_tiles<1>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
-  if (mb == 2) return launch_tiles<2>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
-  return launch_tiles<4>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  if (mb == 1) return launch_tiles<1, 4>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  if (mb == 2) return launch_tiles<2, 4>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  return launch_tiles<4, 8>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
 }
 
 size_t gemm_workspace_bytes(const LayoutDev &L, int M) {
