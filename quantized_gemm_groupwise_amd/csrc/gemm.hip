@@ -265,9 +265,12 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bf[c][nb], acc[mb][nb], 0, 0, 0);
+      // the next step's x tile goes to the other LDS buffer half-way through
+      // this step (that buffer was released by the previous barrier), so the
+      // LDS writes overlap the remaining MFMAs
+      if (t == 3) store_a(cur ^ 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_a(cur ^ 1);
     lds_barrier();
     cur ^= 1;
 #pragma unroll
