@@ -1,0 +1,167 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (one gq_quantize_pack / gq_linear call per linear).
+
+Full-size outputs are checked on samples the CPU oracle can compute row by
+row: packed codes, scales and zeros of sampled output channels (byte
+identical) and y[m][n] at sampled (m, n) (normwise relative error <= 2e-3 on
+the sample, plus the elementwise bound of test_gpu_parity).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth as S
+
+pytestmark = pytest.mark.gpu
+
+gq = pytest.importorskip("quantized_gemm_groupwise_amd")
+from tests.gpu_util import bf16_dev, y_bits  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.load_library()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def sample_rows(N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=min(n, N), replace=False).tolist())
+    rows |= {0, N - 1}
+    return sorted(rows)
+
+
+def check_packed_rows(p, W, block_n, bits, rows):
+    """Bytes of the GPU packing for `rows` against the oracle on those rows."""
+    L = O.Layout(W.shape[1], W.shape[0], block_n, list(bits))
+    K = W.shape[1]
+    codes = p.codes.cpu().numpy()
+    scales = p.scales.cpu().numpy().view(np.uint16)
+    zeros = p.zeros.cpu().numpy()
+    for blk, r0, b, g, coff, goff in L.blocks():
+        sel = [r for r in rows if r0 <= r < r0 + block_n]
+        if not sel:
+            continue
+        q = O.quantize_groups(W[sel].reshape(-1, g), b)
+        words = O.pack(q["codes"].reshape(len(sel), K), b)
+        rb, gpr = K * b // 8, K // g
+        for i, r in enumerate(sel):
+            rr = r - r0
+            got_c = codes[coff + rr * rb: coff + (rr + 1) * rb]
+            assert np.array_equal(got_c, words[i].astype("<u4").view(np.uint8)), f"codes row {r}"
+            got_s = scales[goff + rr * gpr: goff + (rr + 1) * gpr]
+            assert np.array_equal(got_s, q["scale"].view(np.uint16)[i * gpr:(i + 1) * gpr]), f"scales row {r}"
+            got_z = zeros[goff + rr * gpr: goff + (rr + 1) * gpr]
+            assert np.array_equal(got_z, q["zero"][i * gpr:(i + 1) * gpr].astype(np.uint8)), f"zeros row {r}"
+
+
+def oracle_packed_rows(W, block_n, bits, rows):
+    """Oracle packing of just `rows` (a layout of len(rows) uniform rows per
+    block width), with a map row -> position."""
+    out = {}
+    K = W.shape[1]
+    for r in rows:
+        b = bits[r // block_n]
+        p = O.quantize_pack(W[r:r + 1], O.Layout(K, 1, 1, [b]))
+        out[r] = p
+    return out
+
+
+def check_linear_sample(y, x_bits, W, block_n, bits, rows, ms):
+    yb = y_bits(y)
+    refs = oracle_packed_rows(W, block_n, bits, rows)
+    y_ref = np.zeros((len(ms), len(rows)))
+    bound_w = np.zeros((len(ms), len(rows)))
+    xs = x_bits[ms]
+    xa = np.abs(O.bf16_bits_to_f64(xs))
+    for i, r in enumerate(rows):
+        y_ref[:, i] = O.linear(xs, refs[r])[:, 0]
+        bound_w[:, i] = xa @ np.abs(O.dequant(refs[r]).astype(np.float64))[0]
+    yg = O.bf16_bits_to_f64(yb[np.ix_(ms, rows)])
+    normwise = np.linalg.norm(yg - y_ref) / np.linalg.norm(y_ref)
+    assert normwise <= 2e-3, normwise
+    bound = 2.0 ** -8 * np.abs(y_ref) + 2.0 ** -10 * bound_w
+    assert np.all(np.abs(yg - y_ref) <= bound), int((np.abs(yg - y_ref) > bound).sum())
+    return normwise
+
+
+def test_small_layer_config():
+    """K = N = 512, INT4 g128, M = 4: full comparison."""
+    d = S.small_layer()
+    ref = O.quantize_pack(d["W"], O.Layout(512, 512, 512, [4]))
+    p = gq.quantize_pack(torch.from_numpy(d["W"]).cuda(), 4)
+    torch.cuda.synchronize()
+    cb, sb, zb = gq.gq_packed_bytes(p.layout)
+    assert np.array_equal(p.codes.cpu().numpy()[:cb], ref.codes)
+    assert np.array_equal(p.scales.cpu().numpy().view(np.uint16)[: sb // 2], ref.scales)
+    assert np.array_equal(p.zeros.cpu().numpy()[:zb], ref.zeros)
+    y = gq.linear(bf16_dev(d["x"]), p)
+    torch.cuda.synchronize()
+    r = O.compare_linear(y_bits(y), O.linear(d["x"], ref))
+    assert r["normwise"] <= 2e-3 and r["max_ulp"] <= 1
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("j", [0, 1, 2, 3])
+def test_llama3_8b_decode_layers(j, bits):
+    """Llama-3-8B-shaped layers, INT4 (M = 1) and INT2 (M in {1, 4, 16})."""
+    N, K = S.LLAMA3_8B_SHAPE_LIST[j]
+    W = S.decode_weight(j)
+    _say("decode layer", j, N, K, "INT", bits)
+    p = gq.quantize_pack(torch.from_numpy(W).cuda(), bits)
+    torch.cuda.synchronize()
+    assert int(p.flags.cpu().item()) == 0
+    rows = sample_rows(N, 48, 10 + j)
+    check_packed_rows(p, W, N, [bits], rows)
+    for M in ((1,) if bits == 4 else (1, 4, 16)):
+        x = S.decode_x(j, M)
+        y = gq.linear(bf16_dev(x), p)
+        torch.cuda.synchronize()
+        check_linear_sample(y, x, W, N, [bits], rows, list(range(M)))
+
+
+@pytest.mark.parametrize("pick", [0, 61, 223])
+def test_layer_mix_linears(pick):
+    """Sampled linears of the 224-linear Layer-mix model at M in {1, 8, 32}."""
+    assign = S.layer_mix_assignment()
+    l, name, N, K, bits = assign[pick]
+    idx = [n for (n, _, _) in S.LLAMA3_8B_LAYER].index(name)
+    W = S.layer_mix_weight(l, idx, N, K)
+    _say("layer-mix", pick, l, name, N, K, bits)
+    p = gq.quantize_pack(torch.from_numpy(W).cuda(), bits)
+    rows = sample_rows(N, 24, 100 + pick)
+    check_packed_rows(p, W, N, [bits], rows)
+    for M in (1, 8, 32):
+        x = S.layer_mix_x(K, M)
+        y = gq.linear(bf16_dev(x), p)
+        torch.cuda.synchronize()
+        check_linear_sample(y, x, W, N, [bits], rows, list(range(M)))
+
+
+@pytest.mark.parametrize("j", [0, 1])
+def test_channel_mix_prefill(j):
+    """70B-class MLP, Channel-mix INT4/INT2 blocks of 128 channels, M = 2048."""
+    N, K = S.MLP70B_SHAPES[j]
+    W, bits = S.channel_mix_weight(j)
+    _say("channel-mix", j, N, K, sum(b == 4 for b in bits), "INT4 blocks of", len(bits))
+    p = gq.quantize_pack(torch.from_numpy(W).cuda(), bits, 128)
+    torch.cuda.synchronize()
+    assert int(p.flags.cpu().item()) == 0
+    # sample rows from INT4 and INT2 blocks
+    rng = np.random.default_rng(30 + j)
+    b4 = [i for i, b in enumerate(bits) if b == 4]
+    b2 = [i for i, b in enumerate(bits) if b == 2]
+    rows = sorted({int(128 * rng.choice(b4) + rng.integers(128)) for _ in range(12)} |
+                  {int(128 * rng.choice(b2) + rng.integers(128)) for _ in range(12)} | {0, N - 1})
+    check_packed_rows(p, W, 128, bits, rows)
+    x = S.channel_mix_x(j)
+    y = gq.linear(bf16_dev(x), p)
+    torch.cuda.synchronize()
+    ms = sorted(set(rng.choice(2048, 24, replace=False).tolist()) | {0, 2047})
+    check_linear_sample(y, x, W, 128, bits, rows, ms)
