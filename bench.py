@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy (PMC byte-counter calibration)")
     return ap.parse_args()
 
 
@@ -299,7 +301,7 @@ def secondary(torch, gq, S, args):
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         ws = gq.workspace(gq.gq_linear_workspace_bytes(p.layout, M), "cuda")
         gt = GraphTimer(torch, lambda: gq.linear(x, p, out=y, ws=ws))
-        gt.run(3)
+        gt.run(20)                                   # warm clocks
         t, _ = gt.run(20)
         fl = 2.0 * M * N * K
         tf = fl * 20 / t / 1e12
@@ -328,6 +330,14 @@ def main():
         sys.exit(1)
     gq.load_library()
     torch.cuda.set_device(0)
+    if args.calibration_copy:
+        # a plain copy of known size: 256 MiB read + 256 MiB written per launch
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     copies = args.copies
     steps = args.steps
     log(f"bench: building INT4 decode weights ({copies} rotated copies)")
@@ -350,7 +360,7 @@ def main():
     log(f"bench: up/gate GEMV {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
-                "kernel": "gemv_kernel<bf16, M=1, R=8, INT4> on N=14336 K=4096",
+                "kernel": "gemv_kernel<bf16, M=1, R=4 rows/wave, NL=2 slices, INT4> on N=14336 K=4096",
                 "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3)}
     del sets, xs, ys
     torch.cuda.empty_cache()
