@@ -132,11 +132,12 @@ gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype
  *   workspace  DEVICE, 256-byte aligned, at least gq_linear_workspace_bytes;
  *          may be NULL when that is 0.  Overwritten; calls that share a
  *          workspace must be ordered on one stream.
- * M < 64 uses a bandwidth-bound dot-product kernel that applies (code - z)
+ * M <= 4 uses a bandwidth-bound dot-product kernel that applies (code - z)
  * and S exactly in fp32; larger M uses an MFMA kernel that rounds each
- * dequantized weight once to fp16 (the FP16 matmul of the survey review) and
- * activations are rescaled per row by a power of two so that their fp16 form
- * is exact.  Results agree with the fp64 product of the dequantized weights
+ * dequantized weight once to fp16 (the FP16 matmul of the survey review);
+ * its activations are rescaled per row by a power of two so that their fp16
+ * form is exact, and small M splits K across workgroups (fp32 partials in
+ * the workspace, summed in a fixed order, so results are deterministic).  Results agree with the fp64 product of the dequantized weights
  * to about the bf16 output rounding (normwise relative error <= 2e-3). */
 gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
