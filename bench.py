@@ -360,7 +360,7 @@ def main():
     log(f"bench: up/gate GEMV {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
-                "kernel": "gemv_kernel<bf16, M=1, R=4 rows/wave, NL=2 slices, INT4> on N=14336 K=4096",
+                "kernel": "gemv_kernel<bf16, M=1, R=2 rows/wave, NL=2 slices, INT4> on N=14336 K=4096",
                 "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3)}
     del sets, xs, ys
     torch.cuda.empty_cache()

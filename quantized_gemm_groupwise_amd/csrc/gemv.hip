@@ -13,6 +13,12 @@
 // slices are issued as one group, and the next group is issued before the
 // current one is computed, so each slice waits only for its own bytes.
 //
+// Loads go through buffer resources, one per row for codes, scales and
+// zeros, whose size is the row's own length (0 for rows past N).  A lane
+// past the end of a row, or of x, gets zeros from the hardware range check
+// instead of a load, and zero scales make its contribution exactly 0, so the
+// kernel needs neither masks nor 64-bit address arithmetic per load.
+//
 // Activations.  The workgroup stages x in LDS once, already arranged as the
 // code pairs come out of a packed word and laid out lane-major so reads are
 // conflict-free, together with the per-lane sums sum_k x_k that the zero
@@ -37,7 +43,7 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kLanes = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kLanes * kWaves;
-constexpr int kStageUnits = 2;             // x units staged per thread per chunk
+constexpr int kStageSub = 4;               // x sub-units staged per thread per chunk
 constexpr int kLdsBytes = 65536;
 
 template <int ACT>
@@ -58,6 +64,33 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return r;
 }
 
+// Both 32-bit halves of a 64-bit value shifted right by S (one VALU op for
+// two words of codes; the bits that cross into the low word are masked off
+// by the caller).
+template <int S>
+__device__ __forceinline__ uint64_t shr64(uint64_t a) {
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(a));
+  return r;
+}
+
+// Raw buffer resource over [p, p + bytes): loads at offsets >= bytes return 0.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 // (x[i], x[i + half]) from registers holding consecutive activation pairs.
 __device__ __forceinline__ uint32_t pair_lo(uint32_t hi_reg, uint32_t lo_reg) {
   return __builtin_amdgcn_perm(hi_reg, lo_reg, 0x05040100u);
@@ -74,6 +107,26 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// v read from another lane of the same row of 16 (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Exchange halves between two registers (gfx950 lane swaps):
+//   swap32: lanes 32..63 of a  <->  lanes 0..31 of b
+//   swap16: odd rows of 16 lanes of a  <->  even rows of b
+// Afterwards a + b holds, in lanes whose bit 5 (bit 4) is clear, the sum of
+// a over the two halves, and in the others the sum of b.  The leading s_nop
+// covers the wait states the swap needs after a VALU write of its operands.
+__device__ __forceinline__ void swap32(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 // Sum V per-lane values over the 64 lanes of a wave.  Halving exchanges first
 // (each lane keeps half of the values and adds its partner's copy of that
 // half), then a butterfly on the last value.  Afterwards lane l holds the
@@ -85,24 +138,50 @@ __device__ __forceinline__ float wave_reduce_multi(const float (&v)[V], int lane
   float cur[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) cur[i] = v[i];
-  int n = V;
-#pragma unroll
-  for (int b = 0; b < LOGV; ++b) {
-    const int off = 32 >> b;
-    const bool upper = (lane & off) != 0;
-    n >>= 1;
+  if constexpr (LOGV >= 1) {                   // offset 32
 #pragma unroll
     for (int i = 0; i < V / 2; ++i) {
-      if (i < n) {
-        const float keep = upper ? cur[i + n] : cur[i];
-        const float send = upper ? cur[i] : cur[i + n];
-        cur[i] = keep + __shfl_xor(send, off);
-      }
+      swap32(cur[i], cur[i + V / 2]);
+      cur[i] += cur[i + V / 2];
     }
   }
-  float s = cur[0];
+  if constexpr (LOGV >= 2) {                   // offset 16
 #pragma unroll
-  for (int off = 32 >> LOGV; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    for (int i = 0; i < V / 4; ++i) {
+      swap16(cur[i], cur[i + V / 4]);
+      cur[i] += cur[i + V / 4];
+    }
+  }
+#pragma unroll
+  for (int b = 2; b < LOGV; ++b) {             // offsets 8, 4
+    const int off = 32 >> b;
+    const int n = V >> (b + 1);
+    const bool upper = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      const float keep = upper ? cur[i + n] : cur[i];
+      const float send = upper ? cur[i] : cur[i + n];
+      cur[i] = keep + (off == 8 ? dpp<0x128>(send) : __shfl_xor(send, off));
+    }
+  }
+  // butterfly over the remaining G = 64/V lanes (every lane of the group
+  // ends with the group total); inside a row of 16 lanes with DPP
+  constexpr int G = 64 >> LOGV;
+  float s = cur[0];
+  if constexpr (G >= 64) {
+    float t = s;
+    swap32(s, t);
+    s += t;
+  }
+  if constexpr (G >= 32) {
+    float t = s;
+    swap16(s, t);
+    s += t;
+  }
+  if constexpr (G >= 16) s += dpp<0x128>(s);   // row_ror:8
+  if constexpr (G >= 8) s += dpp<0x141>(s);    // row_half_mirror
+  if constexpr (G >= 4) s += dpp<0x4e>(s);     // quad_perm [2,3,0,1]
+  if constexpr (G >= 2) s += dpp<0xb1>(s);     // quad_perm [1,0,3,2]
   return s;
 }
 
@@ -125,43 +204,43 @@ struct Geo {
   static constexpr int SK = KPL * kLanes;               // k per slice
   static constexpr int PW = KPL / 2;                    // activation pair words per lane-slice
   static constexpr int NSUM = BITS == 4 ? 1 : 2;        // floats per lane-slice in the sum table
+  static constexpr int SPU = KPL / 16;                  // staging sub-units per lane-slice
 };
 
 // Stage x[:, k0 : k0 + nslice*SK] into LDS:
 //   pairs: uint4 [m][slice][quad q][lane]  words 4q..4q+3 of the lane's pair list
 //   sums:  float [m][slice][s][lane]       INT4: sum x; INT2: sum x and B*(X1+X4/4+X16/16)
-// Units are (m, slice, lane) triples of KPL activations; each thread stages
-// up to kStageUnits of them.  stage_x_load issues the global loads,
-// stage_x_store waits for them and writes LDS, so code loads issued in
-// between are not waited for.
+// Units are (m, slice, lane) triples of KPL activations, each cut into SPU
+// sub-units of 16 activations (one INT2 code word, two INT4 code words).
+// Thread t stages sub-units t, t + 256, ...; the SPU sub-units of a unit sit
+// in consecutive lanes, which combine their partial sums with DPP.  The
+// loads of all kStageSub sub-units are issued unconditionally (sub-units
+// past the end read out of range and get zeros), so the wait before the
+// stores counts exactly; stage_x_store skips the arithmetic of sub-units no
+// thread of the workgroup owns.
 template <int BITS>
 struct StageRegs {
-  uint32_t raw[kStageUnits][Geo<BITS>::PW];
+  uint32_t raw[kStageSub][8];
 };
 
 template <int BITS, int M>
-__device__ __forceinline__ void stage_x_load(StageRegs<BITS> &st, const uint16_t *__restrict__ x,
-                                             int K, int k0, int nslice) {
+__device__ __forceinline__ void stage_x_load(StageRegs<BITS> &st, Rsrc xr, uint32_t xbytes, int K,
+                                             int k0, int nslice) {
   using Gm = Geo<BITS>;
-  const int units = M * nslice * kLanes;
+  const int subs = M * nslice * kLanes * Gm::SPU;
 #pragma unroll
-  for (int u = 0; u < kStageUnits; ++u) {
-    const int unit = (int)threadIdx.x + u * kThreads;
+  for (int j = 0; j < kStageSub; ++j) {
+    const int su = (int)threadIdx.x + j * kThreads;
+    const int unit = su / Gm::SPU, part = su % Gm::SPU;
     const int lane = unit & (kLanes - 1);
     const int ms = unit >> 6;                   // m * nslice + slice
     const int m = ms / nslice, sl = ms - m * nslice;
-    const int kk = k0 + sl * Gm::SK + lane * Gm::KPL;
-    const bool ok = unit < units && kk < K;     // K is a multiple of KPL
-    // branch-free: an invalid unit loads x[0][0..] and is zeroed (zero pairs
-    // and sums)
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + (ok ? (int64_t)m * K + kk : 0));
-    const uint32_t keep = ok ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int v = 0; v < Gm::PW / 4; ++v) {
-      const uint4 t = src[v];
-      st.raw[u][4 * v + 0] = t.x & keep; st.raw[u][4 * v + 1] = t.y & keep;
-      st.raw[u][4 * v + 2] = t.z & keep; st.raw[u][4 * v + 3] = t.w & keep;
-    }
+    const int kk = k0 + sl * Gm::SK + lane * Gm::KPL + part * 16;
+    const bool ok = su < subs && kk < K;        // K is a multiple of 64
+    const uint32_t off = ok ? ((uint32_t)m * (uint32_t)K + (uint32_t)kk) * 2u : xbytes;
+    const uint4 a = ld128(xr, off), b = ld128(xr, off + 16u);
+    st.raw[j][0] = a.x; st.raw[j][1] = a.y; st.raw[j][2] = a.z; st.raw[j][3] = a.w;
+    st.raw[j][4] = b.x; st.raw[j][5] = b.y; st.raw[j][6] = b.z; st.raw[j][7] = b.w;
   }
 }
 
@@ -171,55 +250,62 @@ __device__ __forceinline__ void stage_x_store(const StageRegs<BITS> &st, int nsl
   using Gm = Geo<BITS>;
   constexpr uint32_t ONES = ACT == 0 ? 0x3f803f80u : 0x3c003c00u;
   constexpr float BIASF = ACT == 0 ? 128.f : 1024.f;
-  const int units = M * nslice * kLanes;
+  const int subs = M * nslice * kLanes * Gm::SPU;
 #pragma unroll
-  for (int u = 0; u < kStageUnits; ++u) {
-    const int unit = (int)threadIdx.x + u * kThreads;
-    if (unit < units) {                         // LDS slot exists
-      const int lane = unit & (kLanes - 1);
-      const int ms = unit >> 6;
-      uint4 *dst = pairs + (ms * (Gm::PW / 4)) * kLanes + lane;
-      float *sdst = sums + (ms * Gm::NSUM) * kLanes + lane;
-      uint32_t p[Gm::PW];
-      if constexpr (BITS == 4) {
-        // word w covers k 8w..8w+7: pairs (k_t, k_{t+4}), t = 0..3
-        float s = 0.f;
+  for (int j = 0; j < kStageSub; ++j) {
+    if (j * kThreads >= subs) break;            // uniform: nothing left to stage
+    const int su = (int)threadIdx.x + j * kThreads;
+    const int unit = su / Gm::SPU, part = su % Gm::SPU;
+    const int lane = unit & (kLanes - 1);
+    const int ms = unit >> 6;
+    const uint32_t *q = st.raw[j];
+    uint32_t p[8];
+    float s0, s1;
+    if constexpr (BITS == 4) {
+      // code word w covers k 8w..8w+7: pairs (k_t, k_{t+4}), t = 0..3
+      float s = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t *q = &st.raw[u][4 * w];
-          p[4 * w + 0] = pair_lo(q[2], q[0]);
-          p[4 * w + 1] = pair_hi(q[2], q[0]);
-          p[4 * w + 2] = pair_lo(q[3], q[1]);
-          p[4 * w + 3] = pair_hi(q[3], q[1]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) s = dot2<ACT>(p[4 * w + t], ONES, s);
-        }
-        sdst[0] = s;
-      } else {
-        // word w covers k 16w..16w+15: pairs (k_i, k_{i+8}); classes by
-        // position in the word: i = 0,3,6 -> 1x, 1,4,7 -> 4x, 2,5 -> 16x
-        float s1 = 0.f, s4 = 0.f, s16 = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t *q = &st.raw[u][8 * w];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            p[8 * w + 2 * a] = pair_lo(q[a + 4], q[a]);        // (x_{2a}, x_{2a+8})
-            p[8 * w + 2 * a + 1] = pair_hi(q[a + 4], q[a]);    // (x_{2a+1}, x_{2a+9})
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            if (i % 3 == 0) s1 = dot2<ACT>(p[8 * w + i], ONES, s1);
-            else if (i % 3 == 1) s4 = dot2<ACT>(p[8 * w + i], ONES, s4);
-            else s16 = dot2<ACT>(p[8 * w + i], ONES, s16);
-          }
-        }
-        sdst[0] = s1 + s4 + s16;
-        sdst[kLanes] = BIASF * fmaf(s16, 0.0625f, fmaf(s4, 0.25f, s1));
+      for (int w = 0; w < 2; ++w) {
+        p[4 * w + 0] = pair_lo(q[4 * w + 2], q[4 * w + 0]);
+        p[4 * w + 1] = pair_hi(q[4 * w + 2], q[4 * w + 0]);
+        p[4 * w + 2] = pair_lo(q[4 * w + 3], q[4 * w + 1]);
+        p[4 * w + 3] = pair_hi(q[4 * w + 3], q[4 * w + 1]);
       }
 #pragma unroll
-      for (int q = 0; q < Gm::PW / 4; ++q)
-        dst[q * kLanes] = make_uint4(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+      for (int t = 0; t < 8; ++t) s = dot2<ACT>(p[t], ONES, s);
+      s += dpp<0xb1>(s);                        // the other sub-unit of the unit
+      s0 = s;
+      s1 = 0.f;
+    } else {
+      // the code word covers k 0..15: pairs (k_i, k_{i+8}); classes by
+      // position in the word: i = 0,3,6 -> 1x, 1,4,7 -> 4x, 2,5 -> 16x
+      float c1 = 0.f, c4 = 0.f, c16 = 0.f;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        p[2 * a] = pair_lo(q[a + 4], q[a]);         // (x_{2a}, x_{2a+8})
+        p[2 * a + 1] = pair_hi(q[a + 4], q[a]);     // (x_{2a+1}, x_{2a+9})
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i % 3 == 0) c1 = dot2<ACT>(p[i], ONES, c1);
+        else if (i % 3 == 1) c4 = dot2<ACT>(p[i], ONES, c4);
+        else c16 = dot2<ACT>(p[i], ONES, c16);
+      }
+      // the four sub-units of the unit
+      c1 += dpp<0xb1>(c1); c4 += dpp<0xb1>(c4); c16 += dpp<0xb1>(c16);
+      c1 += dpp<0x4e>(c1); c4 += dpp<0x4e>(c4); c16 += dpp<0x4e>(c16);
+      s0 = c1 + c4 + c16;
+      s1 = BIASF * fmaf(c16, 0.0625f, fmaf(c4, 0.25f, c1));
+    }
+    if (su < subs) {                            // LDS slot exists
+      uint4 *dst = pairs + (ms * (Gm::PW / 4) + 2 * part) * kLanes + lane;
+      dst[0] = make_uint4(p[0], p[1], p[2], p[3]);
+      dst[kLanes] = make_uint4(p[4], p[5], p[6], p[7]);
+      if (part == 0) {
+        float *sdst = sums + (ms * Gm::NSUM) * kLanes + lane;
+        sdst[0] = s0;
+        if constexpr (BITS == 2) sdst[kLanes] = s1;
+      }
     }
   }
 }
@@ -231,31 +317,32 @@ struct LoadGroup {
   uint32_t zb[NL][R];
 };
 
-template <int BITS, int R, int NL>
-__device__ __forceinline__ void issue_group(LoadGroup<BITS, R, NL> &g, int slice0, int nslice_row,
-                                            int rb, int lane, const uint8_t *const (&crow)[R],
-                                            const uint16_t *const (&srow)[R],
-                                            const uint8_t *const (&zrow)[R]) {
+// Row resources of one wave: codes, scales and zeros of each of its R rows.
+template <int R>
+struct RowRsrc {
+  Rsrc c[R], s[R], z[R];
+};
+
+// Slices >= lim (LIM) are not loaded: they belong to the next staged chunk.
+constexpr uint32_t kOutOfRange = 0x80000000u;   // beyond any row resource
+
+template <int BITS, int R, int NL, bool LIM>
+__device__ __forceinline__ void issue_group(LoadGroup<BITS, R, NL> &g, int slice0, int lim,
+                                            int lane, const RowRsrc<R> &rr) {
   using Gm = Geo<BITS>;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int sl = slice0 + i;
-    const int off = sl * 1024 + lane * 16;
-    const bool ok = sl < nslice_row && off < rb;      // lanes past the row end read nothing
-    const int gi = ok ? (sl * Gm::SK + lane * Gm::KPL) / Gm::G : 0;
-    // branch-free: an invalid lane loads the row's first bytes and then
-    // zeroes them (scale 0 makes its contribution exactly 0)
-    // (the loaded values are always consumed, through a mask, so the loads
-    // stay unconditional and the wait counts stay exact)
-    const int offc = ok ? off : 0;
-    const uint32_t keep = ok ? 0xffffffffu : 0u;
+    // a lane past the row end reads nothing: its offsets are out of range
+    // of the row's resources, so codes, scale and zero come back as 0
+    uint32_t off = (uint32_t)(sl * 1024 + lane * 16);
+    uint32_t gi = (uint32_t)(sl * Gm::SK + lane * Gm::KPL) / Gm::G;
+    if (LIM && sl >= lim) off = gi = kOutOfRange;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint4 c = *reinterpret_cast<const uint4 *>(crow[r] + offc);
-      const uint32_t sv = srow[r][gi], zv = zrow[r][gi];
-      g.cw[i][r] = make_uint4(c.x & keep, c.y & keep, c.z & keep, c.w & keep);
-      g.sb[i][r] = sv & keep;
-      g.zb[i][r] = zv & keep;
+      g.cw[i][r] = ld128(rr.c[r], off);
+      g.sb[i][r] = ld16(rr.s[r], gi == kOutOfRange ? gi : 2u * gi);
+      g.zb[i][r] = ld8(rr.z[r], gi);
     }
   }
 }
@@ -296,22 +383,35 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
       const float S = f16_bits_to_f32((uint16_t)g.sb[i][r]);
       const float zz = (float)g.zb[i][r];
       if constexpr (BITS == 4) {
+        // nibble t of each 16-bit half of word w gives the pair for
+        // activation pair 4w + t; words (0,1) and (2,3) are shifted as one
+        // 64-bit value, the bits that cross into the low word are masked off
         const uint32_t mask = 0x000f000fu;
-        float p[M];
+        float pa[M], pb[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) p[m] = 0.f;
+        for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int h = 0; h < 2; ++h) {
+          const uint64_t w64 = ((uint64_t)wv[2 * h + 1] << 32) | wv[2 * h];
+          uint64_t sh[4];
+          sh[0] = w64;
+          sh[1] = shr64<4>(w64);
+          sh[2] = shr64<8>(w64);
+          sh[3] = shr64<12>(w64);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const uint32_t qp = and_or(wv[w] >> (4 * t), mask, bias);
+            const uint32_t q0 = and_or((uint32_t)sh[t], mask, bias);
+            const uint32_t q1 = and_or((uint32_t)(sh[t] >> 32), mask, bias);
 #pragma unroll
-            for (int m = 0; m < M; ++m) p[m] = dot2<ACT>(qp, xp[m][4 * w + t], p[m]);
+            for (int m = 0; m < M; ++m) {
+              pa[m] = dot2<ACT>(q0, xp[m][4 * (2 * h) + t], pa[m]);
+              pb[m] = dot2<ACT>(q1, xp[m][4 * (2 * h + 1) + t], pb[m]);
+            }
           }
         }
 #pragma unroll
         for (int m = 0; m < M; ++m)
-          acc[r][m] = fmaf(S, fmaf(-(BIASF + zz), xs[m], p[m]), acc[r][m]);
+          acc[r][m] = fmaf(S, fmaf(-(BIASF + zz), xs[m], pa[m] + pb[m]), acc[r][m]);
       } else {
         const uint32_t m1 = 0x00030003u, m4 = 0x000c000cu, m16 = 0x00300030u;
         float p1[M], p4[M], p16[M];
@@ -350,10 +450,10 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
 }
 
 // Slices per staged chunk for a bit-width and M: each thread stages at most
-// kStageUnits units and the chunk fits kLdsBytes.
+// kStageSub sub-units and the chunk fits kLdsBytes.
 __host__ __device__ constexpr int chunk_slices(int bits, int M) {
   const int pw = bits == 4 ? 16 : 32, nsum = bits == 4 ? 1 : 2;
-  const int by_units = kStageUnits * kThreads / (M * kLanes);
+  const int by_units = kStageSub * kThreads / (M * kLanes * (bits == 4 ? 2 : 4));
   const int by_lds = kLdsBytes / (M * kLanes * 4 * (pw + nsum));
   return by_units < by_lds ? by_units : by_lds;
 }
@@ -379,24 +479,25 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
   const int RB = K * BITS / 8;               // bytes per packed row
   const int GPR = K / Gm::G;                 // groups per row
   const int nslice_row = (RB + 1023) >> 10;
-  // slices per staged chunk: every thread stages at most kStageUnits units
+  // slices per staged chunk: every thread stages at most kStageSub sub-units
   // and the chunk fits the LDS budget
   constexpr int CHUNK = chunk_slices(BITS, M);
   static_assert(CHUNK >= 1, "chunk");
   static_assert(CHUNK * M * kLanes * 4 * (Gm::PW + Gm::NSUM) <= kLdsBytes, "lds");
   const int r0 = n0 - blk * L.block_n;
-  const uint8_t *crow[R];
-  const uint16_t *srow[R];
-  const uint8_t *zrow[R];
+  RowRsrc<R> rr;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    // rows past N (ragged tail, or a wave past the end) read a valid row and
-    // never store
-    const int rr = (n0 + r < L.N) ? r0 + r : (r0 < L.block_n && n0 < L.N ? r0 : 0);
-    crow[r] = codes + bi.code_off + (uint64_t)rr * (uint64_t)RB;
-    srow[r] = scales + bi.grp_off + (uint64_t)rr * (uint64_t)GPR;
-    zrow[r] = zeros + bi.grp_off + (uint64_t)rr * (uint64_t)GPR;
+    // rows past N (ragged tail, or a wave past the end) get empty resources:
+    // they load zeros and never store
+    const bool live = n0 + r < L.N;
+    const uint64_t row = live ? (uint64_t)(r0 + r) : 0u;
+    rr.c[r] = make_rsrc(codes + bi.code_off + row * (uint64_t)RB, live ? (uint32_t)RB : 0u);
+    rr.s[r] = make_rsrc(scales + bi.grp_off + row * (uint64_t)GPR, live ? 2u * GPR : 0u);
+    rr.z[r] = make_rsrc(zeros + bi.grp_off + row * (uint64_t)GPR, live ? (uint32_t)GPR : 0u);
   }
+  const uint32_t xbytes = (uint32_t)(M * K) * 2u;
+  const Rsrc xr = make_rsrc(x, xbytes);
   // the LDS arena holds min(CHUNK, nslice_row) slices: pairs, then sums
   const int cslices = nslice_row < CHUNK ? nslice_row : CHUNK;
   uint4 *pairs = reinterpret_cast<uint4 *>(lds);
@@ -412,9 +513,9 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
     // so slice i waits only for the loads issued before it
     LoadGroup<BITS, R, NL> g;
     StageRegs<BITS> st;
-    stage_x_load<BITS, M>(st, x, K, 0, nslice_row);
+    stage_x_load<BITS, M>(st, xr, xbytes, K, 0, nslice_row);
     __builtin_amdgcn_sched_barrier(0);
-    issue_group<BITS, R, NL>(g, 0, nslice_row, RB, lane, crow, srow, zrow);
+    issue_group<BITS, R, NL, false>(g, 0, nslice_row, lane, rr);
     __builtin_amdgcn_sched_barrier(0);
     stage_x_store<BITS, ACT, M>(st, nslice_row, pairs, sums);
     lds_barrier();
@@ -426,9 +527,9 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
       if (c0 > 0) lds_barrier();               // previous chunk fully read
       LoadGroup<BITS, R, NL> g;
       StageRegs<BITS> st;
-      stage_x_load<BITS, M>(st, x, K, c0 * Gm::SK, cn);
+      stage_x_load<BITS, M>(st, xr, xbytes, K, c0 * Gm::SK, cn);
       __builtin_amdgcn_sched_barrier(0);
-      issue_group<BITS, R, NL>(g, c0, cend, RB, lane, crow, srow, zrow);
+      issue_group<BITS, R, NL, true>(g, c0, cend, lane, rr);
       __builtin_amdgcn_sched_barrier(0);
       stage_x_store<BITS, ACT, M>(st, cn, pairs, sums);
       lds_barrier();
@@ -436,7 +537,7 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
         compute_group<BITS, ACT, M, R, NL>(g, s, cend, c0, lane, pairs, sums, cn, acc);
         s += NL;
         if (s >= cend) break;
-        issue_group<BITS, R, NL>(g, s, cend, RB, lane, crow, srow, zrow);
+        issue_group<BITS, R, NL, true>(g, s, cend, lane, rr);
       }
     }
   }
@@ -516,28 +617,17 @@ hipError_t launch_m(const LayoutDev &L, const void *x, const uint32_t *codes,
     all4 &= b;
   }
   const int bitsel = all4 ? 4 : (any4 ? 0 : 2);
-  // slices per row (of the widest block) decide the load-group size NL; rows
-  // per wave R keep R*NL <= 16 loads of 16 bytes in flight per lane and, when
-  // possible, >= 1024 waves on the chip
+  // Load groups of two 1 KB slices (one for rows of a single slice), issued
+  // one group ahead; two rows per wave once N gives >= 2048 waves.  Measured
+  // on MI355X over the Llama-3-8B decode shapes: issuing a whole long row at
+  // once, or more rows per wave, leaves fewer waves to cover HBM latency.
   const int ns = (L.K * (any4 ? 4 : 2) / 8 + 1023) / 1024;
-  const int waves4 = (L.N + 3) / 4, waves2 = (L.N + 1) / 2;
-  if (ns <= 1) {
-    if (waves4 >= 1024) return launch_rows<ACT, M, 4, 1>(L, bitsel, x, codes, scales, zeros, y, s);
-    if (waves2 >= 1024) return launch_rows<ACT, M, 2, 1>(L, bitsel, x, codes, scales, zeros, y, s);
-    return launch_rows<ACT, M, 1, 1>(L, bitsel, x, codes, scales, zeros, y, s);
-  }
-  if (ns <= 2) {
-    if (waves4 >= 1024) return launch_rows<ACT, M, 4, 2>(L, bitsel, x, codes, scales, zeros, y, s);
-    if (waves2 >= 1024) return launch_rows<ACT, M, 2, 2>(L, bitsel, x, codes, scales, zeros, y, s);
-    return launch_rows<ACT, M, 1, 2>(L, bitsel, x, codes, scales, zeros, y, s);
-  }
-  if (ns <= 4) {
-    if (waves4 >= 1024) return launch_rows<ACT, M, 4, 4>(L, bitsel, x, codes, scales, zeros, y, s);
-    if (waves2 >= 1024) return launch_rows<ACT, M, 2, 4>(L, bitsel, x, codes, scales, zeros, y, s);
-    return launch_rows<ACT, M, 1, 4>(L, bitsel, x, codes, scales, zeros, y, s);
-  }
-  if (waves2 >= 1024) return launch_rows<ACT, M, 2, 8>(L, bitsel, x, codes, scales, zeros, y, s);
-  return launch_rows<ACT, M, 1, 8>(L, bitsel, x, codes, scales, zeros, y, s);
+  const bool two = L.N >= 4096;
+  if (ns <= 1)
+    return two ? launch_rows<ACT, M, 2, 1>(L, bitsel, x, codes, scales, zeros, y, s)
+               : launch_rows<ACT, M, 1, 1>(L, bitsel, x, codes, scales, zeros, y, s);
+  return two ? launch_rows<ACT, M, 2, 2>(L, bitsel, x, codes, scales, zeros, y, s)
+             : launch_rows<ACT, M, 1, 2>(L, bitsel, x, codes, scales, zeros, y, s);
 }
 
 template <int ACT>
