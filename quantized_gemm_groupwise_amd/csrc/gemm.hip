@@ -19,6 +19,7 @@
 // 32*MB rows.  The x tile goes through LDS (double buffered, one barrier per
 // 64-deep k step); the packed codes of the wave's own columns go straight
 // from HBM to registers, so every code is unpacked exactly once per tile.
+#include "gq_device.h"
 #include "gq_internal.h"
 
 namespace gq {
@@ -31,15 +32,22 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- pre-pass
 
-// One workgroup per row of x: largest magnitude, exponent, rescale, convert,
-// permute.  act 0: bf16 input (rescaled), act 1: fp16 input (copied).
+// One workgroup per row of the padded activation matrix xa [Mp][Kp]: largest
+// magnitude, exponent, rescale, convert, permute.  Rows m >= M and columns
+// k >= K are written as zeros, so the GEMM reads whole tiles without masks.
+// act 0: bf16 input (rescaled), act 1: fp16 input (copied).
 template <int ACT>
-__global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict__ x, int K,
-                                                     uint16_t *__restrict__ xa,
+__global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict__ x, int M, int K,
+                                                     int Kp, uint16_t *__restrict__ xa,
                                                      int *__restrict__ rexp) {
   const int m = blockIdx.x;
+  uint16_t *out = xa + (int64_t)m * Kp;
+  if (m >= M) {
+    for (int c = threadIdx.x * 8; c < Kp; c += 256 * 8)
+      *reinterpret_cast<uint4 *>(out + c) = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   const uint16_t *row = x + (int64_t)m * K;
-  uint16_t *out = xa + (int64_t)m * K;
   __shared__ float red[4];
   int e = 0;
   if (ACT == 0) {
@@ -65,7 +73,11 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
     }
   }
   if (threadIdx.x == 0) rexp[m] = e;
-  for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
+  for (int c = threadIdx.x * 8; c < Kp; c += 256 * 8) {
+    if (c >= K) {
+      *reinterpret_cast<uint4 *>(out + c) = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
     const uint4 v = *reinterpret_cast<const uint4 *>(row + c);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint16_t h[8];
@@ -91,22 +103,6 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
 
 // ------------------------------------------------------------------- GEMM
 
-// (a & m) | o in one VALU op (operands in VGPRs; gfx9 VOP3 takes no
-// literal constants).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
-// LDS-only barrier: waits for this wave's LDS traffic, not for its
-// outstanding global loads (the next tile's prefetch stays in flight).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Unpack the 8 codes of one 8-k chunk into 4 packed fp16 pairs (q - z) * s,
 // pair i holding chunk elements (i, i + 4).  `t` carries the chunk's codes
 // with element i at bits [B*i, B*i + B) of its low half (elements 0..3) and
@@ -129,7 +125,7 @@ constexpr int KT = 128;                   // k per main-loop step
 constexpr int LDA = KT + 8;               // halfs per LDS row (conflict-free b128 reads)
 
 struct GemmArgs {
-  int K, N, M, m0, nw;
+  int K, Kp, N, M, m0, nw;
   int kt0, nkt;                           // first k step and number of k steps
   const uint16_t *xa;
   const int *rexp;
@@ -167,7 +163,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
       const int kk = kt * KT + achunk * 8;
       const bool ok = m < g.M && kk < K;              // rows past M, k past K (INT2 tail) read 0
       const int mc = m < g.M ? m : g.M - 1;           // clamped: always a valid address
-      const uint4 v = *reinterpret_cast<const uint4 *>(g.xa + (int64_t)mc * K + (kk < K ? kk : 0));
+      const uint4 v = *reinterpret_cast<const uint4 *>(g.xa + (int64_t)mc * g.Kp + (kk < K ? kk : 0));
       const uint32_t keep = ok ? 0xffffffffu : 0u;
       areg[p] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
@@ -308,7 +304,7 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
 }
 
 template <int MB, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(LayoutDev L, int M, int m_tiles, int n_tiles,
+__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(LayoutDev L, int M, int Kp, int m_tiles, int n_tiles,
                                                    int ksteps_per_split,
                                                    const uint16_t *__restrict__ xa,
                                                    const int *__restrict__ rexp,
@@ -327,7 +323,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(LayoutDev L, int M, in
   const int n_tile = tile / m_tiles;
   const int split = (int)blockIdx.y;
   GemmArgs g;
-  g.K = L.K; g.N = L.N; g.M = M;
+  g.K = L.K; g.Kp = Kp; g.N = L.N; g.M = M;
   g.m0 = m_tile * 32 * MB;
   g.nw = n_tile * (64 * NW) + wave * 64;
   const int ksteps = (L.K + KT - 1) / KT;
@@ -365,6 +361,258 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(LayoutDev L, int M, in
     gemm_wave<2, MB, NW, SPLIT>(g, As, wave_active, crow, srow, zrow, cvalid);
 }
 
+// ------------------------------------------------------- large-M GEMM
+//
+// M >= 256: a workgroup of 4 waves (one per SIMD) computes a 256 x 256 tile.
+// Wave w owns columns [64w, 64w + 64) as two 32-column MFMA blocks and all
+// 256 rows as eight 32-row blocks, so each unpacked code pair feeds eight
+// MFMAs (half the dequantization work per MFMA of the 128-row tile).  The
+// 8 x 2 accumulator blocks (256 fp32 per lane) live in the AGPRs.
+//
+// The x tile of the next k step travels HBM/L2 -> LDS by buffer loads that
+// write LDS directly (no registers, no LDS store instructions), issued at
+// the start of the current step into the other of two LDS buffers; the
+// barrier at the end of the step is the only wait for it.  In LDS a tile is
+// 256 rows x 16 chunks of 16 bytes, chunk c of row r in slot
+// 16 r + (c ^ (r & 15)): the XOR spreads the MFMA operand reads (32
+// consecutive rows, one chunk) over all banks.  Codes, scales and zeros go
+// to registers through resources over the wave's Channel-mix block (columns
+// past N read out of range and get zeros), also one step ahead.
+constexpr int BIG_MB = 8;
+constexpr int BIG_NW = 4;
+constexpr int BIG_TM = 32 * BIG_MB;              // 256 rows
+constexpr int BIG_TN = 64 * BIG_NW;              // 256 columns
+constexpr int BIG_TILE_BYTES = BIG_TM * KT * 2;  // 64 KB
+constexpr int BIG_DMA = BIG_TILE_BYTES / (1024 * BIG_NW);   // 1 KB LDS loads per wave per tile
+constexpr uint32_t kOob = 0x80000000u;           // beyond every resource
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct BigArgs {
+  int K, Kp, N, M, m0, nkt;
+  const int *rexp;
+  uint16_t *y;
+  int out_fp16;
+};
+
+template <int BITS>
+__device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As1, Rsrc xr,
+                                         Rsrc cr, Rsrc sr, Rsrc zr, const uint32_t (&cbase)[2],
+                                         const uint32_t (&sbase)[2], const uint32_t (&zbase)[2],
+                                         bool wave_active, int wave, int ncol0) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+
+  // x tile DMA: load i (= BIG_DMA * wave + p) writes slots 64 i .. 64 i + 63,
+  // i.e. rows 4i .. 4i + 3; lane l -> row 4i + l/16, chunk (l%16) ^ (row & 15)
+  // with row & 15 = 4 (i & 3) + l/16
+  uint32_t dv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    dv[q] = (uint32_t)(((lane >> 4) * g.Kp + (((lane & 15) ^ (4 * q + (lane >> 4))) * 8)) * 2);
+  auto dma_a = [&](int kt, uint4 *dst) {
+#pragma unroll
+    for (int p = 0; p < BIG_DMA; ++p) {
+      const int i = BIG_DMA * wave + p;
+      const uint32_t soff = (uint32_t)(((g.m0 + 4 * i) * g.Kp + kt * KT) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(dst + 64 * i), 16, dv[p & 3], soff,
+                                               0, 0);
+    }
+  };
+  // MFMA operand reads: lane (j, h) of 32-row block mb, sub-step t reads row
+  // 32 mb + j, chunk 8h + t, i.e. slot chunk ((8h) ^ (j & 8)) | (t ^ (j & 7))
+  const uint32_t rb = (uint32_t)(j * 16 + ((8 * h) ^ (j & 8)));   // in 16-byte slots
+
+  // codes: lane half h takes chunks 8h..8h+7 of the step (INT4: 8 words,
+  // INT2: 4 words); INT4 steps are one group, INT2 halves one group each
+  constexpr int BW = BITS == 4 ? 8 : 4;
+  constexpr uint32_t STEPB = KT * BITS / 8;       // code bytes per column per step
+  constexpr uint32_t STEPG = BITS == 4 ? 1 : 2;   // groups per step
+  auto load_b = [&](int kt, uint32_t (*dst)[BW], uint32_t *sd, uint32_t *zd) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t co = cbase[nb] + (uint32_t)kt * STEPB;
+#pragma unroll
+      for (int q = 0; q < BW / 4; ++q) {
+        const uint4 v = ld128(cr, co + 16u * q);
+        dst[nb][4 * q + 0] = v.x; dst[nb][4 * q + 1] = v.y;
+        dst[nb][4 * q + 2] = v.z; dst[nb][4 * q + 3] = v.w;
+      }
+      sd[nb] = ld16(sr, sbase[nb] + (uint32_t)kt * (2 * STEPG));
+      zd[nb] = ld8(zr, zbase[nb] + (uint32_t)kt * STEPG);
+    }
+  };
+
+  floatx16 acc[BIG_MB][2];
+#pragma unroll
+  for (int mb = 0; mb < BIG_MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
+
+  // one k step from LDS tile `cur` with codes (bc, sc, zc); starts the
+  // next step's x DMA into `nxt` and its codes into (bn, sn, zn).  On the
+  // last step both reload the same step, so every load stays unconditional.
+  auto step = [&](int kt, const uint4 *cur, uint4 *nxt, const uint32_t (*bc)[BW],
+                  const uint32_t *sc, const uint32_t *zc, uint32_t (*bn)[BW], uint32_t *sn,
+                  uint32_t *zn) {
+    const int kn = kt + 1 < g.nkt ? kt + 1 : kt;
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(kn, nxt);
+    load_b(kn, bn, sn, zn);
+    __builtin_amdgcn_sched_barrier(0);
+    // the half step past K (INT2 rows with K % 128 == 64) gets scale 0;
+    // its x columns are zero padding
+    const bool kok = kt * KT + h * (KT / 2) < g.K;
+    half2v cz[2], s2[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t sv = kok ? sc[nb] : 0u;
+      const uint16_t zb = f32_to_f16_bits(-(1024.f + (float)zc[nb]));
+      s2[nb] = __builtin_bit_cast(half2v, sv | (sv << 16));
+      cz[nb] = __builtin_bit_cast(half2v, (uint32_t)zb | ((uint32_t)zb << 16));
+    }
+    auto read_a = [&](int t, half8 *af) {
+      const uint32_t slot = rb + (uint32_t)(t ^ (j & 7));
+#pragma unroll
+      for (int mb = 0; mb < BIG_MB; ++mb)
+        af[mb] = __builtin_bit_cast(half8, cur[mb * 512 + slot]);
+    };
+    auto make_b = [&](int t, half8 *bf) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (BITS == 4) {
+          unpack_chunk<4>(bc[nb][t], cz[nb], s2[nb], bf[nb]);
+        } else {
+          const uint32_t wv = bc[nb][t >> 1];
+          const uint32_t tc = __builtin_amdgcn_perm(wv, wv, (t & 1) ? 0x03030202u : 0x01010000u);
+          unpack_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
+        }
+      }
+    };
+    half8 af[2][BIG_MB], bf[2][2];
+    read_a(0, af[0]);
+    make_b(0, bf[0]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int c = t & 1, n = c ^ 1;
+      if (t + 1 < 8) {
+        read_a(t + 1, af[n]);
+        make_b(t + 1, bf[n]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < BIG_MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][mb], bf[c][nb], acc[mb][nb], 0, 0, 0);
+      // one wave per SIMD: the next sub-step's operand reads and unpacking
+      // must issue while this sub-step's MFMAs execute, so interleave them
+      // (MFMA, 2 VALU, 1 LDS read, MFMA, ...)
+#pragma unroll
+      for (int i = 0; i < 2 * BIG_MB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        if (t + 1 < 8) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);          // VALU
+          if (i < BIG_MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the next tile's DMA has landed in every wave's part once all waves
+    // pass this barrier
+    lds_barrier();
+  };
+
+  uint32_t b0[2][BW], b1[2][BW], s0[2], s1[2], z0[2], z1[2];
+  dma_a(0, As0);
+  load_b(0, b0, s0, z0);
+  lds_barrier();
+  // g.nkt is even: x is zero-padded to a multiple of 256 in k, and steps
+  // past K get scale 0
+  for (int kt = 0; kt < g.nkt; kt += 2) {
+    step(kt, As0, As1, b0, s0, z0, b1, s1, z1);
+    step(kt + 1, As1, As0, b1, s1, z1, b0, s0, z0);
+  }
+
+  if (!wave_active) return;
+  // epilogue: lane (j, h) holds column ncol0 + 32nb + j and rows
+  // 8(e/4) + 4h + e%4 of each 32-row block
+#pragma unroll
+  for (int mb = 0; mb < BIG_MB; ++mb) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = g.m0 + mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (m >= g.M) continue;
+      const int ex = g.rexp[m];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int n = ncol0 + 32 * nb + j;
+        if (n >= g.N) continue;
+        const float v = ldexpf(acc[mb][nb][e], ex);
+        g.y[(int64_t)m * g.N + n] = g.out_fp16 ? f32_to_f16_bits(v) : f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * BIG_NW, 1) void gemm_big_kernel(
+    LayoutDev L, int M, int Kp, uint32_t xa_bytes, int m_tiles, const uint16_t *__restrict__ xa,
+    const int *__restrict__ rexp, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    uint16_t *__restrict__ y, int out_fp16) {
+  __shared__ __attribute__((aligned(16))) uint4 As0[BIG_TILE_BYTES / 16];
+  __shared__ __attribute__((aligned(16))) uint4 As1[BIG_TILE_BYTES / 16];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  // tile order: m fastest, so the workgroups on one XCD (every 8th id)
+  // share one m tile of x in that XCD's L2
+  const int tile = (int)blockIdx.x;
+  const int m_tile = tile % m_tiles;
+  const int n_tile = tile / m_tiles;
+  BigArgs g;
+  g.K = L.K; g.Kp = Kp; g.N = L.N; g.M = M;
+  g.m0 = m_tile * BIG_TM;
+  g.nkt = Kp / KT;
+  g.rexp = rexp; g.y = y; g.out_fp16 = out_fp16;
+  const int ncol0 = n_tile * BIG_TN + wave * 64;
+  const bool wave_active = ncol0 < L.N;
+  // waves past N read column 0's block through empty offsets and never store
+  const int nref = wave_active ? ncol0 : 0;
+  const int blk = nref / L.block_n;
+  const BlockInfo bi = block_info(L, blk);
+  const int bits = __builtin_amdgcn_readfirstlane(bi.bits);
+  const uint32_t RB = (uint32_t)(L.K * bits / 8);
+  const uint32_t GPR = (uint32_t)(bits == 4 ? L.K / 128 : L.K / 64);
+  const Rsrc xr = make_rsrc(xa, xa_bytes);
+  const Rsrc cr = make_rsrc(codes + bi.code_off, (uint32_t)L.block_n * RB);
+  const Rsrc sr = make_rsrc(scales + bi.grp_off, (uint32_t)L.block_n * GPR * 2u);
+  const Rsrc zr = make_rsrc(zeros + bi.grp_off, (uint32_t)L.block_n * GPR);
+  uint32_t cbase[2], sbase[2], zbase[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = nref + 32 * nb + j;
+    const bool valid = wave_active && n < L.N;
+    const uint32_t r = (uint32_t)(n - blk * L.block_n);
+    if (bits == 4) {
+      cbase[nb] = valid ? r * RB + 32u * h : kOob;
+      sbase[nb] = valid ? r * GPR * 2u : kOob;
+      zbase[nb] = valid ? r * GPR : kOob;
+    } else {
+      cbase[nb] = valid ? r * RB + 16u * h : kOob;
+      sbase[nb] = valid ? (r * GPR + h) * 2u : kOob;
+      zbase[nb] = valid ? r * GPR + h : kOob;
+    }
+  }
+  if (bits == 4)
+    big_wave<4>(g, As0, As1, xr, cr, sr, zr, cbase, sbase, zbase, wave_active, wave, ncol0);
+  else
+    big_wave<2>(g, As0, As1, xr, cr, sr, zr, cbase, sbase, zbase, wave_active, wave, ncol0);
+}
+
 // Sum the split-K partials in split order, rescale by 2^e, round.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int splits,
                                                             int M, int N, const int *__restrict__ rexp,
@@ -380,7 +628,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 template <int MB, int NW>
-hipError_t launch_tiles(const LayoutDev &L, int M, int splits, const uint16_t *xa, const int *rexp,
+hipError_t launch_tiles(const LayoutDev &L, int M, int Kp, int splits, const uint16_t *xa, const int *rexp,
                         const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                         void *y, float *part, int out_fp16, hipStream_t s) {
   const int m_tiles = (M + 32 * MB - 1) / (32 * MB);
@@ -392,11 +640,11 @@ hipError_t launch_tiles(const LayoutDev &L, int M, int splits, const uint16_t *x
   uint16_t *yp = reinterpret_cast<uint16_t *>(y);
   if (nsplit == 1) {
     hipLaunchKernelGGL((gemm_kernel<MB, NW, false>), dim3(m_tiles * n_tiles, 1), dim3(64 * NW), 0, s, L,
-                       M, m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
+                       M, Kp, m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gemm_kernel<MB, NW, true>), dim3(m_tiles * n_tiles, nsplit), dim3(64 * NW), 0, s,
-                     L, M, m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
+                     L, M, Kp, m_tiles, n_tiles, per, xa, rexp, c, scales, zeros, yp, part, out_fp16);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = (int64_t)M * L.N;
@@ -420,35 +668,78 @@ inline int choose_splits(const LayoutDev &L, int M, int mb) {
 
 }  // namespace
 
+namespace {
+
+// Workspace layout: fp16 activations [Mp][Kp] (zero padded to whole
+// 256-row tiles and pairs of 128-k steps), row exponents [M], split-K
+// partials [S][M][N].
+struct Workspace {
+  int Mp, Kp;
+  size_t a_bytes, e_bytes, p_bytes;
+};
+
+inline size_t round256(size_t v) { return (v + 255u) & ~(size_t)255u; }
+
+// The 256 x 256 kernel needs M >= 256, enough tiles to fill the chip and
+// 32-bit buffer offsets (x and each Channel-mix block below 2 GiB).
+inline bool use_big(const LayoutDev &L, int M, const Workspace &w) {
+  if (M < BIG_TM) return false;
+  const int64_t tiles = (int64_t)((M + BIG_TM - 1) / BIG_TM) * ((L.N + BIG_TN - 1) / BIG_TN);
+  if (tiles < 128) return false;
+  if (w.a_bytes >= ((size_t)1 << 31)) return false;
+  if ((uint64_t)L.block_n * (uint64_t)L.K / 2u >= ((uint64_t)1 << 31)) return false;
+  return true;
+}
+
+inline Workspace workspace_of(const LayoutDev &L, int M) {
+  Workspace w;
+  w.Kp = (L.K + 2 * KT - 1) / (2 * KT) * (2 * KT);   // whole pairs of k steps
+  w.Mp = (M + BIG_TM - 1) / BIG_TM * BIG_TM;
+  w.a_bytes = round256((size_t)w.Mp * (size_t)w.Kp * 2u);
+  w.e_bytes = round256((size_t)M * 4u);
+  w.p_bytes = 0;
+  if (!use_big(L, M, w)) {
+    const int sp = choose_splits(L, M, gemm_mb(M));
+    if (sp > 1) w.p_bytes = (size_t)sp * (size_t)M * (size_t)L.N * 4u;
+  }
+  return w;
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
                        const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                        void *y, void *workspace, hipStream_t s) {
-  const size_t a_bytes = ((size_t)M * (size_t)L.K * 2u + 255u) & ~(size_t)255u;
-  const size_t e_bytes = ((size_t)M * 4u + 255u) & ~(size_t)255u;
+  const Workspace w = workspace_of(L, M);
   uint16_t *xa = reinterpret_cast<uint16_t *>(workspace);
-  int *rexp = reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) + a_bytes);
-  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + a_bytes + e_bytes);
+  int *rexp = reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) + w.a_bytes);
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + w.a_bytes + w.e_bytes);
   const uint16_t *xin = reinterpret_cast<const uint16_t *>(x);
   if (act == GQ_BF16)
-    hipLaunchKernelGGL(prep_x_kernel<0>, dim3(M), dim3(256), 0, s, xin, L.K, xa, rexp);
+    hipLaunchKernelGGL(prep_x_kernel<0>, dim3(w.Mp), dim3(256), 0, s, xin, M, L.K, w.Kp, xa, rexp);
   else
-    hipLaunchKernelGGL(prep_x_kernel<1>, dim3(M), dim3(256), 0, s, xin, L.K, xa, rexp);
+    hipLaunchKernelGGL(prep_x_kernel<1>, dim3(w.Mp), dim3(256), 0, s, xin, M, L.K, w.Kp, xa, rexp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int out_fp16 = act == GQ_FP16 ? 1 : 0;
+  if (use_big(L, M, w)) {
+    const int m_tiles = w.Mp / BIG_TM;
+    const int n_tiles = (L.N + BIG_TN - 1) / BIG_TN;
+    hipLaunchKernelGGL(gemm_big_kernel, dim3(m_tiles * n_tiles), dim3(64 * BIG_NW), 0, s, L, M, w.Kp,
+                       (uint32_t)w.a_bytes, m_tiles, xa, rexp, reinterpret_cast<const uint8_t *>(codes),
+                       scales, zeros, reinterpret_cast<uint16_t *>(y), out_fp16);
+    return hipGetLastError();
+  }
   const int mb = gemm_mb(M);
   const int sp = choose_splits(L, M, mb);
-  if (mb == 1) return launch_tiles<1, 4>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
-  if (mb == 2) return launch_tiles<2, 4>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
-  return launch_tiles<4, 8>(L, M, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  if (mb == 1) return launch_tiles<1, 4>(L, M, w.Kp, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  if (mb == 2) return launch_tiles<2, 4>(L, M, w.Kp, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
+  return launch_tiles<4, 8>(L, M, w.Kp, sp, xa, rexp, codes, scales, zeros, y, part, out_fp16, s);
 }
 
 size_t gemm_workspace_bytes(const LayoutDev &L, int M) {
-  const size_t a_bytes = ((size_t)M * (size_t)L.K * 2u + 255u) & ~(size_t)255u;
-  const size_t e_bytes = ((size_t)M * 4u + 255u) & ~(size_t)255u;
-  const int sp = choose_splits(L, M, gemm_mb(M));
-  const size_t p_bytes = sp > 1 ? (size_t)sp * (size_t)M * (size_t)L.N * 4u : 0u;
-  return a_bytes + e_bytes + p_bytes;
+  const Workspace w = workspace_of(L, M);
+  return w.a_bytes + w.e_bytes + w.p_bytes;
 }
 
 }  // namespace gq

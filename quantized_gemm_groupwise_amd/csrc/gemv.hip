@@ -32,6 +32,7 @@
 // accumulator per position class.  Per group the zero point and scale are
 // applied as s * (sum x*q - z * sum x), i.e. sum x*(q-z)*s up to fp32
 // rounding.
+#include "gq_device.h"
 #include "gq_internal.h"
 
 namespace gq {
@@ -56,14 +57,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                   c, false);
 }
 
-// (a & m) | o in one VALU op (the three operands in VGPRs; gfx9 VOP3 cannot
-// take two literal constants).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
 // Both 32-bit halves of a 64-bit value shifted right by S (one VALU op for
 // two words of codes; the bits that cross into the low word are masked off
 // by the caller).
@@ -74,37 +67,12 @@ __device__ __forceinline__ uint64_t shr64(uint64_t a) {
   return r;
 }
 
-// Raw buffer resource over [p, p + bytes): loads at offsets >= bytes return 0.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc make_rsrc(const void *p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
-}
-
 // (x[i], x[i + half]) from registers holding consecutive activation pairs.
 __device__ __forceinline__ uint32_t pair_lo(uint32_t hi_reg, uint32_t lo_reg) {
   return __builtin_amdgcn_perm(hi_reg, lo_reg, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t hi_reg, uint32_t lo_reg) {
   return __builtin_amdgcn_perm(hi_reg, lo_reg, 0x07060302u);
-}
-
-// LDS barrier for data written to LDS only: waits for this wave's LDS
-// operations, not for its outstanding global loads.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // v read from another lane of the same row of 16 (DPP control CTRL).

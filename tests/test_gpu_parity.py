@@ -171,6 +171,46 @@ def test_linear_gemm(M, N, K, block_n, bits):
     linear_gate(y_bits(y), O.linear(x, ref), x, ref)
 
 
+@pytest.mark.parametrize("M,N,K,block_n,bits", [
+    (260, 16448, 192, 16448, [2]),                     # ragged M and N, half k-step
+    (512, 16384, 256, 128, [4, 2, 2, 2] * 32),         # Channel-mix blocks
+    (256, 32768, 128, 32768, [4]),                     # one 256-row tile
+])
+def test_linear_gemm_large_tiles(M, N, K, block_n, bits):
+    """M >= 256 with >= 128 tiles: the 256 x 256 workgroup tile path."""
+    W = S.decode_weight(1, N=N, K=K)
+    L = O.Layout(K, N, block_n, bits)
+    ref = O.quantize_pack(W, L)
+    p = upload_packed(ref)
+    x = S.activations(M, K, 900 + M)
+    _say("gemm large tiles", M, N, K, len(bits), "blocks")
+    y = gq.linear(bf16_dev(x), p)
+    torch.cuda.synchronize()
+    linear_gate(y_bits(y), O.linear(x, ref), x, ref)
+
+
+def test_linear_exact_integer_case_large_tiles():
+    """The exact case of test_linear_exact_integer_case on the 256 x 256 path."""
+    rng = np.random.default_rng(77)
+    M, N, K = 300, 32768, 256
+    base = rng.integers(-7, 9, size=(N, K)).astype(np.float64)
+    base[:, 0::128] = -7
+    base[:, 1::128] = 8
+    W = (base * 2.0 ** -6).astype(np.float32)
+    ref = O.quantize_pack(W, O.Layout(K, N, N, [4]))
+    p = upload_packed(ref)
+    xi = np.zeros((M, K), dtype=np.float64)
+    for m in range(M):
+        pos = rng.choice(K, 31, replace=False)
+        xi[m, pos] = rng.choice([-1.0, 1.0], size=31)
+    x = S.bf16_bits(xi.astype(np.float32))
+    y = gq.linear(bf16_dev(x), p)
+    torch.cuda.synchronize()
+    exact = (xi @ base.T) * 2.0 ** -6          # small integers: exact in fp64
+    assert np.abs(exact).max() / 2 ** -6 < 256
+    assert np.array_equal(O.bf16_bits_to_f64(y_bits(y)), exact)
+
+
 @pytest.mark.parametrize("M", [2, 70])
 def test_linear_fp16_activations(M):
     N, K = 256, 512
