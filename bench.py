@@ -305,10 +305,23 @@ def secondary(torch, gq, S, args):
         t, _ = gt.run(20)
         fl = 2.0 * M * N * K
         tf = fl * 20 / t / 1e12
+        # context: a dense fp16 GEMM of the same shape through torch.matmul
+        # (hipBLASLt), i.e. what the MFMA units sustain here without any
+        # dequantization
+        xd = torch.randn((M, K), device="cuda", dtype=torch.float16)
+        wd = torch.randn((K, N), device="cuda", dtype=torch.float16)   # W^T, contiguous
+        yd = torch.empty((M, N), device="cuda", dtype=torch.float16)
+        dt = GraphTimer(torch, lambda: torch.matmul(xd, wd, out=yd))
+        dt.run(10)
+        td, _ = dt.run(20)
+        tfd = fl * 20 / td / 1e12
+        del xd, wd, yd
         out[f"gemm_channel_mix_M2048_mlp{j}"] = {
             "N": N, "K": K, "int4_blocks": int(sum(b == 4 for b in bits)), "blocks": len(bits),
             "ms": round(t / 20 * 1e3, 4), "TFLOPS": round(tf, 1),
-            "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 3), "includes": "activation pre-pass + GEMM"}
+            "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 3), "includes": "activation pre-pass + GEMM",
+            "dense_fp16_torch_matmul_TFLOPS": round(tfd, 1),
+            "frac_of_dense_fp16": round(tf / tfd, 3)}
         del x, y, p
         torch.cuda.empty_cache()
     return out

@@ -130,15 +130,24 @@ gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype
  *   y      DEVICE [M][N] act, 2-byte aligned, written (bf16/fp16 rounded to
  *          nearest even from an fp32 accumulator).
  *   workspace  DEVICE, 256-byte aligned, at least gq_linear_workspace_bytes;
- *          may be NULL when that is 0.  Overwritten; calls that share a
- *          workspace must be ordered on one stream.
- * M <= 4 uses a bandwidth-bound dot-product kernel that applies (code - z)
- * and S exactly in fp32; larger M uses an MFMA kernel that rounds each
- * dequantized weight once to fp16 (the FP16 matmul of the survey review);
- * its activations are rescaled per row by a power of two so that their fp16
- * form is exact, and small M splits K across workgroups (fp32 partials in
- * the workspace, summed in a fixed order, so results are deterministic).  Results agree with the fp64 product of the dequantized weights
- * to about the bf16 output rounding (normwise relative error <= 2e-3). */
+ *          may be NULL when that is 0.  Overwritten (needs no
+ *          initialisation); calls that share a workspace must be ordered on
+ *          one stream.
+ * Kernels by M:
+ *   M <= 4       bandwidth-bound dot-product kernel; (code - z) and S are
+ *                applied exactly in fp32.
+ *   4 < M <= 32  MFMA on the activations as given (bf16 or fp16) and the
+ *                codes as exact B + q values; each group's scale and zero
+ *                point are applied in fp32 after its MFMAs.  Long K is split
+ *                across workgroups (fp32 partials in the workspace, summed
+ *                in split order).
+ *   M > 32       MFMA GEMM that rounds each dequantized weight once to fp16
+ *                (the FP16 matmul of the survey review); activations are
+ *                rescaled per row by a power of two so that their fp16 form
+ *                is exact; small M splits K across workgroups.
+ * Every path is deterministic.  Results agree with the fp64 product of the
+ * dequantized weights to about the bf16 output rounding (normwise relative
+ * error <= 2e-3). */
 gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                     void *y, void *workspace, size_t workspace_bytes, void *stream);

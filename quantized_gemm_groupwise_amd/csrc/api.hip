@@ -108,6 +108,8 @@ gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (M <= kGemvMaxM)
     return launched(launch_gemv(L, M, act, x, codes, scales, zeros, y, s), s);
+  if (skinny_supported(L, M))
+    return launched(launch_skinny(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
   return launched(launch_gemm(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
 }
 

@@ -613,7 +613,8 @@ __global__ __launch_bounds__(64 * BIG_NW, 1) void gemm_big_kernel(
     big_wave<2>(g, As0, As1, xr, cr, sr, zr, cbase, sbase, zbase, wave_active, wave, ncol0);
 }
 
-// Sum the split-K partials in split order, rescale by 2^e, round.
+// Sum the split-K partials in split order, rescale by 2^e (rexp may be
+// null: no rescale), round.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int splits,
                                                             int M, int N, const int *__restrict__ rexp,
                                                             uint16_t *__restrict__ y, int out_fp16) {
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
   float s = 0.f;
   for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + i];
   const int m = (int)(i / N);
-  const float v = ldexpf(s, rexp[m]);
+  const float v = rexp ? ldexpf(s, rexp[m]) : s;
   y[i] = out_fp16 ? f32_to_f16_bits(v) : f32_to_bf16_rne(v);
 }
 
@@ -706,6 +707,14 @@ inline Workspace workspace_of(const LayoutDev &L, int M) {
 }
 
 }  // namespace
+
+hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, const int *rexp,
+                                uint16_t *y, int out_fp16, hipStream_t s) {
+  const int64_t total = (int64_t)M * N;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     part, splits, M, N, rexp, y, out_fp16);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
                        const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,

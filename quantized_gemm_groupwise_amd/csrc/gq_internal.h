@@ -62,6 +62,18 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 
 // Largest M served by the dot-product (GEMV) kernel; larger M goes to MFMA.
 constexpr int kGemvMaxM = 4;
+// Largest M served by the small-batch MFMA kernel (bf16/fp16 activations
+// used as they are, no pre-pass); larger M goes to the tiled GEMM.
+constexpr int kSkinnyMaxM = 32;
+bool skinny_supported(const LayoutDev &L, int M);
+size_t skinny_workspace_bytes(const LayoutDev &L, int M);
+hipError_t launch_skinny(const LayoutDev &L, int M, gq_dtype act, const void *x,
+                         const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                         void *y, void *workspace, hipStream_t s);
+// Sum split-K fp32 partials [splits][M][N] in split order, times 2^rexp[m]
+// when rexp is not null, rounded to bf16 (or fp16).
+hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, const int *rexp,
+                                uint16_t *y, int out_fp16, hipStream_t s);
 
 // MFMA tile rows per workgroup, in 32-row blocks, for a given M.
 inline int gemm_mb(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }

@@ -40,6 +40,7 @@ gq_status check_ptr16(const void *p) {
 size_t linear_workspace_bytes(const LayoutDev &L, int M, gq_dtype act) {
   (void)act;
   if (M <= kGemvMaxM || L.N == 0) return 0;
+  if (skinny_supported(L, M)) return skinny_workspace_bytes(L, M);
   return gemm_workspace_bytes(L, M);
 }
 

@@ -211,7 +211,7 @@ def test_linear_exact_integer_case_large_tiles():
     assert np.array_equal(O.bf16_bits_to_f64(y_bits(y)), exact)
 
 
-@pytest.mark.parametrize("M", [2, 70])
+@pytest.mark.parametrize("M", [2, 20, 70])
 def test_linear_fp16_activations(M):
     N, K = 256, 512
     W = S.decode_weight(3, N=N, K=K)
@@ -286,3 +286,22 @@ def test_repeat_is_bitwise_deterministic():
     assert np.array_equal(a, b)
     x1 = x[:3].contiguous()
     assert np.array_equal(y_bits(gq.linear(x1, p)), y_bits(gq.linear(x1, p)))
+
+
+def test_one_workspace_across_paths():
+    """Small-batch (split K), prefill and small-batch calls of two shapes
+    reuse one workspace in turn; every result stays within the bar."""
+    shapes = [(1024, 2048, [4]), (640, 4096, [2])]
+    packs = []
+    for N, K, bits in shapes:
+        W = S.decode_weight(2, N=N, K=K)
+        ref = O.quantize_pack(W, O.Layout(K, N, N, bits))
+        packs.append((K, ref, upload_packed(ref)))
+    need = max(gq.gq_linear_workspace_bytes(p.layout, M) for _, _, p in packs for M in (12, 24, 80))
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for M in (12, 80, 24, 12):
+        for K, ref, p in packs:
+            x = S.activations(M, K, 40 + M)
+            y = gq.linear(bf16_dev(x), p, ws=ws)
+            torch.cuda.synchronize()
+            linear_gate(y_bits(y), O.linear(x, ref), x, ref)
