@@ -103,7 +103,8 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, uint32_t x
                                             Rsrc sr, Rsrc zr, uint32_t RB, uint32_t GPR,
                                             uint4 *xbuf, uint16_t *sbuf, uint8_t *zbuf,
                                             uint32_t *cbuf) {
-  constexpr int XPT = 16 * MB * SK_S * 16 / (64 * SK_WAVES);   // 16-byte x units per thread
+  constexpr int XS = SK_S / MB;                                  // steps per x phase
+  constexpr int XPT = 16 * MB * XS * 16 / (64 * SK_WAVES);       // 16-byte x units per thread
   constexpr int GPS = BITS == 4 ? 1 : 2;                         // groups per step
   constexpr int NG = SK_S * GPS;                                 // groups per channel
   constexpr int GPT = 64 * NG / (64 * SK_WAVES);                 // scales per thread
@@ -118,21 +119,37 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, uint32_t x
   const int ch = 16 * wave + (lane & 15);            // the lane's channel in the tile
   const bool ch_ok = ch < a.nvalid;
 
-  // ---- x, read along k (1 KB per wave load): unit u -> row u / (16 S),
-  // chunk c of step st; staged at slot ((st * 4 + i) * MB + mb) * 64 + l of
-  // the MFMA operand that uses it, in pair order
+  // ---- x, read along k (1 KB per wave load), XS steps per phase: unit u ->
+  // row u / (16 XS), chunk c of step st; staged at slot
+  // ((st * 4 + i) * MB + mb) * 64 + l of the MFMA operand that uses it, in
+  // pair order
   uint4 xs[XPT];
+  auto load_x = [&](int ph) {
 #pragma unroll
-  for (int p = 0; p < XPT; ++p) {
-    const int u = tid + p * 64 * SK_WAVES;
-    const int row = u / (16 * SK_S);
-    const int cc = u % (16 * SK_S);
-    const int k = (a.st0 + (cc >> 4)) * SK_STEP + 8 * (cc & 15);
-    // rows past M and k past K read out of range: zeros
-    const uint32_t off = (row < a.M && k < a.K)
-                             ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)k) * 2u : xbytes;
-    xs[p] = ld128(xr, off);
-  }
+    for (int p = 0; p < XPT; ++p) {
+      const int u = tid + p * 64 * SK_WAVES;
+      const int row = u / (16 * XS);
+      const int cc = u % (16 * XS);
+      const int k = (a.st0 + ph * XS + (cc >> 4)) * SK_STEP + 8 * (cc & 15);
+      // rows past M and k past K read out of range: zeros
+      const uint32_t off = (row < a.M && k < a.K)
+                               ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)k) * 2u : xbytes;
+      xs[p] = ld128(xr, off);
+    }
+  };
+  auto store_x = [&]() {
+#pragma unroll
+    for (int p = 0; p < XPT; ++p) {
+      const int u = tid + p * 64 * SK_WAVES;
+      const int row = u / (16 * XS);
+      const int cc = u % (16 * XS);
+      int gg, ii;
+      sk_chunk_owner<BITS>(cc & 15, gg, ii);
+      const int slot = (((cc >> 4) * 4 + ii) * MB + (row >> 4)) * 64 + 16 * gg + (row & 15);
+      xbuf[slot] = chunk_order(xs[p]);
+    }
+  };
+  load_x(0);
   // ---- scales and zeros of the tile's channels, read along each channel
   uint32_t sv[GPT], zv[GPT];
 #pragma unroll
@@ -167,16 +184,7 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, uint32_t x
     }
   }
   // ---- to LDS (each wait covers only loads issued before the data it needs)
-#pragma unroll
-  for (int p = 0; p < XPT; ++p) {
-    const int u = tid + p * 64 * SK_WAVES;
-    const int row = u / (16 * SK_S);
-    const int cc = u % (16 * SK_S);
-    int gg, ii;
-    sk_chunk_owner<BITS>(cc & 15, gg, ii);
-    const int slot = (((cc >> 4) * 4 + ii) * MB + (row >> 4)) * 64 + 16 * gg + (row & 15);
-    xbuf[slot] = chunk_order(xs[p]);
-  }
+  store_x();
 #pragma unroll
   for (int p = 0; p < GPT; ++p) {
     const int u = tid + p * 64 * SK_WAVES;
@@ -193,6 +201,7 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, uint32_t x
     }
   }
   lds_barrier();
+  if constexpr (XS < SK_S) load_x(1);     // second x phase, into the free registers
 
   floatx4 yacc[MB];
 #pragma unroll
@@ -202,6 +211,15 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, uint32_t x
 
 #pragma unroll
   for (int st = 0; st < SK_S; ++st) {
+    if constexpr (XS < SK_S) {
+      static_assert(SK_S == 2 * XS, "two x phases");
+      if (st == XS) {
+        // second x phase: its loads were issued before the first computed
+        lds_barrier();
+        store_x();
+        lds_barrier();
+      }
+    }
     const int step = a.st0 + st;
     if (step >= a.nsteps) break;                     // uniform
     uint32_t w2[2];
@@ -229,7 +247,7 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, uint32_t x
       const bool first = BITS == 4 ? i == 0 : (i & 1) == 0;   // first MFMA of a group
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const uint4 av = xbuf[((st * 4 + i) * MB + mb) * 64 + lane];
+        const uint4 av = xbuf[(((st % XS) * 4 + i) * MB + mb) * 64 + lane];
         gacc[mb] = mfma16<ACT>(av, b, first ? zero4 : gacc[mb]);
         gsum[mb] = mfma16<ACT>(av, ones, first ? zero4 : gsum[mb]);
       }
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(LayoutDev L, int 
                                                               const uint8_t *__restrict__ zeros,
                                                               uint16_t *__restrict__ y,
                                                               float *__restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint4 xbuf[SK_S * 4 * MB * 64];
+  __shared__ __attribute__((aligned(16))) uint4 xbuf[SK_S * 4 * 64];   // one x phase
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[64 * SK_S * 2];
   __shared__ __attribute__((aligned(16))) uint8_t zbuf[64 * SK_S * 2];
   __shared__ __attribute__((aligned(16))) uint32_t cbuf[BITSEL == 4 ? 4 : 64 * SK_CSTRIDE];
