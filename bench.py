@@ -22,7 +22,6 @@ The same JSON line carries:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -50,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--copies", type=int, default=16, help="rotated weight copies (defeat MALL)")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only the Channel-mix M=2048 GEMM measurements (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--calibration-copy", action="store_true",
@@ -158,14 +159,6 @@ def kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=40):
     return t / (reps * copies)
 
 
-def source_digest(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "quantized_gemm_groupwise_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def pmc_traffic():
     """Calibrated HBM bytes per launch from the committed PMC summary, if the
     kernel source it was taken on is the current one."""
@@ -174,7 +167,8 @@ def pmc_traffic():
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_digest") != source_digest(["gemv.hip", "gq_internal.h"]):
+    from quantized_gemm_groupwise_amd.rocprof import source_digest
+    if d.get("source_digest") != source_digest():
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -278,7 +272,14 @@ def secondary(torch, gq, S, args):
     del packs
     torch.cuda.empty_cache()
 
-    # Channel-mix M=2048 GEMM on the 70B-class MLP + quantize/pack of its fp32 weights
+    out.update(channel_mix(torch, gq, S))
+    return out
+
+
+def channel_mix(torch, gq, S):
+    """Channel-mix M=2048 GEMM on the 70B-class MLP + quantize/pack of its fp32
+    weights (and a dense fp16 GEMM of the same shape for comparison)."""
+    out = {}
     for j, (N, K) in enumerate(S.MLP70B_SHAPES):
         Wn, bits = S.channel_mix_weight(j)
         W = torch.from_numpy(Wn).cuda()
@@ -351,6 +352,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.gemm_only:
+        print(json.dumps({"metric": METRIC, "gemm_only": channel_mix(torch, gq, S)}), flush=True)
+        return
     copies = args.copies
     steps = args.steps
     log(f"bench: building INT4 decode weights ({copies} rotated copies)")

@@ -19,10 +19,26 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
+import hashlib
+import json
 import os
 import re
 import statistics
 import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# sources whose text decides the decode GEMV kernel (its counters go stale
+# when any of them changes)
+GEMV_SOURCES = ("gemv.hip", "gq_internal.h", "gq_device.h")
+
+
+def source_digest(names=GEMV_SOURCES) -> str:
+    """First 16 hex digits of the SHA-256 of the named csrc files, in order."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _find(dirpath: str, suffix: str) -> list:
@@ -78,8 +94,10 @@ def summarize_dispatches(rows: list) -> dict:
             "median_us": statistics.median(d) / 1e3, "min_us": min(d) / 1e3, "max_us": max(d) / 1e3}
 
 
-def pmc_values(dirpath: str, counter: str, match: str) -> list:
-    """Per-dispatch values of one counter for kernels matching `match`."""
+def pmc_values(dirpath: str, counter: str, match: str, grid=None, first=None) -> list:
+    """Per-dispatch values of one counter for kernels matching `match` (and
+    launched with `grid` work-items, if given), in dispatch order; `first`
+    keeps only the first that many dispatches."""
     rx = re.compile(match)
     vals = {}
     for p in _find(dirpath, "counter_collection.csv"):
@@ -88,9 +106,12 @@ def pmc_values(dirpath: str, counter: str, match: str) -> list:
                 continue
             if not rx.search(r.get("Kernel_Name", "")):
                 continue
-            key = (p, r.get("Dispatch_Id"))
+            if grid is not None and int(r.get("Grid_Size", 0) or 0) != grid:
+                continue
+            key = (p, int(r.get("Dispatch_Id", 0) or 0))
             vals[key] = vals.get(key, 0.0) + float(r.get("Counter_Value", 0) or 0)
-    return list(vals.values())
+    out = [v for _, v in sorted(vals.items())]
+    return out[:first] if first else out
 
 
 def _main(argv=None):
@@ -107,8 +128,15 @@ def _main(argv=None):
     q.add_argument("fetch_dir")
     q.add_argument("write_dir")
     q.add_argument("--match", required=True)
+    q.add_argument("--grid", type=int, default=None, help="total work-items of the selected launches")
     q.add_argument("--calib-match", default=None, help="copy kernel regex for calibration")
+    q.add_argument("--calib-first", type=int, default=None,
+                   help="use only the first N matching copy dispatches (the calibration copies)")
     q.add_argument("--calib-bytes", type=float, default=None, help="bytes the copy kernel moves each way")
+    q.add_argument("--json", default=None, help="write the calibrated numbers to this file")
+    q.add_argument("--kernel-desc", default="", help="description of the kernel and shape (json)")
+    q.add_argument("--algo-bytes", type=float, default=None, help="algorithmic bytes per dispatch (json)")
+    q.add_argument("--command", action="append", default=[], help="profiling command (json, repeatable)")
     a = ap.parse_args(argv)
 
     if a.cmd == "stats":
@@ -127,13 +155,13 @@ def _main(argv=None):
             if a.flops:
                 print(f"achieved: {a.flops / (sm['avg_us'] * 1e-6) / 1e12:.1f} TFLOP/s at the average duration")
     else:
-        f = pmc_values(a.fetch_dir, "FETCH_SIZE", a.match)
-        w = pmc_values(a.write_dir, "WRITE_SIZE", a.match)
+        f = pmc_values(a.fetch_dir, "FETCH_SIZE", a.match, a.grid)
+        w = pmc_values(a.write_dir, "WRITE_SIZE", a.match, a.grid)
         print(f"FETCH_SIZE KiB per dispatch: n={len(f)} mean={statistics.fmean(f) if f else 0:.1f}")
         print(f"WRITE_SIZE KiB per dispatch: n={len(w)} mean={statistics.fmean(w) if w else 0:.1f}")
         if a.calib_match and a.calib_bytes:
-            cf = pmc_values(a.fetch_dir, "FETCH_SIZE", a.calib_match)
-            cw = pmc_values(a.write_dir, "WRITE_SIZE", a.calib_match)
+            cf = pmc_values(a.fetch_dir, "FETCH_SIZE", a.calib_match, first=a.calib_first)
+            cw = pmc_values(a.write_dir, "WRITE_SIZE", a.calib_match, first=a.calib_first)
             if cf and cw:
                 kf = a.calib_bytes / (statistics.fmean(cf) * 1024)
                 kw = a.calib_bytes / (statistics.fmean(cw) * 1024)
@@ -141,6 +169,28 @@ def _main(argv=None):
                 if f and w:
                     tb = statistics.fmean(f) * 1024 * kf + statistics.fmean(w) * 1024 * kw
                     print(f"calibrated HBM traffic per dispatch: {tb:.0f} bytes")
+                    if a.json:
+                        out = {
+                            "kernel": a.kernel_desc,
+                            "source_digest": source_digest(),
+                            "source_files": [f"quantized_gemm_groupwise_amd/csrc/{n}" for n in GEMV_SOURCES],
+                            "dispatches_fetch": len(f), "dispatches_write": len(w),
+                            "fetch_size_kib_per_dispatch": round(statistics.fmean(f), 1),
+                            "write_size_kib_per_dispatch": round(statistics.fmean(w), 1),
+                            "calibration": {
+                                "kernel": "hipMemcpy device-to-device (__amd_rocclr_copyBuffer) of 256 MiB",
+                                "bytes_each_way": int(a.calib_bytes),
+                                "fetch_size_kib": round(statistics.fmean(cf), 1),
+                                "write_size_kib": round(statistics.fmean(cw), 1),
+                                "fetch_factor": round(kf, 5), "write_factor": round(kw, 5)},
+                            "traffic_bytes_per_launch": int(round(tb)),
+                            "algorithmic_bytes_per_launch": int(a.algo_bytes) if a.algo_bytes else None,
+                            "traffic_over_algorithmic": round(tb / a.algo_bytes, 4) if a.algo_bytes else None,
+                            "commands": a.command,
+                        }
+                        with open(a.json, "w") as fo:
+                            json.dump(out, fo, indent=1)
+                        print(f"wrote {a.json}")
     return 0
 
 
