@@ -172,6 +172,29 @@ def test_linear_gemm(M, N, K, block_n, bits):
 
 
 @pytest.mark.parametrize("M,N,K,block_n,bits", [
+    (6, 16384, 256, 128, [4, 2] * 64),     # one k-way per workgroup, Channel-mix blocks
+    (24, 14368, 320, 14368, [2]),          # two row blocks, ragged last tile, half k-step
+    (12, 8192, 1152, 8192, [4]),           # two k-ways, last phase partly past the range
+    (20, 7168, 1088, 7168, [2]),           # two k-ways, two row blocks, half k-step
+    (9, 2048, 2944, 2048, [4]),            # four k-ways, ragged phases
+    (7, 512, 8192, 512, [4]),              # narrow and long: K split across workgroups
+    (30, 640, 1024, 128, [2, 4, 2, 2, 4]), # split K, Channel-mix, two row blocks
+])
+def test_linear_small_batch_shapes(M, N, K, block_n, bits):
+    """4 < M <= 32 over the small-batch kernel's launch shapes (k-ways per
+    workgroup, row blocks, split K) with ragged tails."""
+    W = S.decode_weight(5, N=N, K=K)
+    L = O.Layout(K, N, block_n, bits)
+    ref = O.quantize_pack(W, L)
+    p = upload_packed(ref)
+    x = S.activations(M, K, 900 + M)
+    _say("small batch", M, N, K, len(bits), "blocks")
+    y = gq.linear(bf16_dev(x), p)
+    torch.cuda.synchronize()
+    linear_gate(y_bits(y), O.linear(x, ref), x, ref)
+
+
+@pytest.mark.parametrize("M,N,K,block_n,bits", [
     (260, 16448, 192, 16448, [2]),                     # ragged M and N, half k-step
     (512, 16384, 256, 128, [4, 2, 2, 2] * 32),         # Channel-mix blocks
     (256, 32768, 128, 32768, [4]),                     # one 256-row tile
