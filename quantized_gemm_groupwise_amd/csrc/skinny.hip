@@ -6,12 +6,10 @@
 // weight-only quantization dequantizes the weights and multiplies them with
 // floating-point activations.  Here nothing is rounded on the way: a code q
 // ORed into the mantissa of 128.0 (bf16) or 1024.0 (fp16) is exactly B + q,
-// the MFMA forms sum_k x_k (B + q_k) for one quantization group with exact
-// products and fp32 accumulation, and the group's scale and zero point are
-// applied afterwards in fp32:
-//     y += s * (sum_k x_k (B + q_k) - (B + z) * sum_k x_k).
-// The group sums of x come from a second MFMA with an all-ones operand.
-// bf16 activations are used as they are (no conversion pass).
+// and -(B + z) is exact too, so for one quantization group the MFMAs form
+//     sum_k x_k (B + q_k) + sum_k x_k * -(B + z) = sum_k x_k (q_k - z)
+// with exact products and fp32 accumulation; the group's scale is applied
+// afterwards in fp32.  bf16 activations are used as they are.
 //
 // MFMA v_mfma_f32_16x16x32: A = x (16 rows of M per block), B = codes of 16
 // output channels.  Lane l holds channel / row l % 16 and a chunk of 8
@@ -29,15 +27,16 @@
 // one wave) times KW k-ways (CW * KW = 4).  Wide layers use KW = 1 (64
 // channels share every staged x tile); narrow ones use KW = 2 or 4, the
 // k-ways' partial sums meeting in LDS at the end, so enough workgroups exist
-// without a second pass over the output.  Only a linear too narrow for that
-// splits K across workgroups, whose fp32 partials the split-K reduction sums
-// in split order.  Each wave's k range is walked in phases of PH steps with
-// everything double-buffered: while phase p is computed, phase p + 1's x
-// tiles land in LDS (buffer loads that write LDS directly, row-major with an
-// XOR swizzle so the MFMA operand reads are conflict-free), its codes land in
-// registers and its scales and zero points are fetched.  One barrier per
-// phase.  Every result is summed in a fixed order: the kernel is
-// deterministic.
+// without a second pass over the output.  A workgroup first requests its
+// whole x range as buffer loads that write LDS directly (row-major,
+// XOR-swizzled so the MFMA operand reads are conflict-free; lanes past M, K
+// or the range read zeros) and its scales and zero points as 16-byte runs
+// into LDS; each wave keeps its code loads a fixed window ahead of the step
+// it computes, so codes return in step order and the multiplications
+// overlap the transfer.  One barrier per workgroup.  A layer whose k range does
+// not fit one workgroup splits K across workgroups; their fp32 partials are
+// summed in split order by the split-K reduction.  Every result is summed in
+// a fixed order: the kernel is deterministic.
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -51,7 +50,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int SK_WAVES = 4;
 constexpr int SK_STEP = 128;                    // k per step
-constexpr int SK_SLOTS = 8;                     // steps x k-ways x 16-row blocks per phase
+constexpr int SK_XCAP = 32;                     // x blocks (step x k-way x 16 rows) per workgroup
+constexpr int SK_SWMAX = 32;                    // steps per wave (code registers)
+constexpr int SK_CWIN = 12;                     // code loads in flight per lane
 constexpr int SK_XBLK = 256;                    // 16-byte LDS slots per 16-row x block of a step
 constexpr uint32_t SK_OOB = 0x80000000u;        // beyond every buffer resource
 
@@ -115,41 +116,39 @@ __device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
   swap16u(v[2], v[3]);
 }
 
-template <int MB, int KW, int BITS>
+template <int MB, int KW, int SWC, int BITS>
 struct SkGeo {
   static constexpr int CW = SK_WAVES / KW;            // channel groups
   static constexpr int NC = 16 * CW;                  // channels per workgroup
-  static constexpr int PH = SK_SLOTS / (KW * MB);     // steps per k-way per phase
+  static constexpr int NB = KW * SWC * MB;            // x blocks in LDS
   static constexpr int GPS = BITS == 4 ? 1 : 2;       // groups per step
-  static constexpr int G = PH * GPS;                  // groups per channel and k-way per phase
-  static constexpr int NCL = BITS == 4 ? PH : PH / 2; // 16-byte code loads per lane per phase
-  static constexpr int SPT = (64 * G + 255) / 256;    // scale entries per thread per phase
-  static_assert(PH >= 2 && NC * KW == 64, "geometry");
+  static constexpr int R = SWC * GPS;                 // groups per (channel, k-way)
+  static constexpr int PS = (2 * R + 14 + 15) / 16;   // 16-byte scale pieces per (channel, k-way)
+  static constexpr int PZ = (R + 15 + 15) / 16;       // 16-byte zero pieces
+  static constexpr int NCL = BITS == 4 ? SWC : SWC / 2;   // 16-byte code loads per lane
+  static_assert(NC * KW == 64 && NB <= SK_XCAP && SWC <= SK_SWMAX && SWC % 8 == 0, "geometry");
 };
 
 struct SkArgs {
   int M, K, N;
   int s0, s1;              // the workgroup's steps (its split of K)
   int sw;                  // steps per k-way
-  int np;                  // phases (even)
   int n0;                  // first output channel of the workgroup
   int rw0;                 // row of n0 inside its block
   int nvalid;              // channels of the workgroup below N
   int nsplit;
+  uint32_t g_blk;          // index of the block's first scale / zero
   uint16_t *y;
   float *part;             // [nsplit][M][N] fp32
 };
 
-template <int ACT, int MB, int KW, int BITS>
+template <int ACT, int MB, int KW, int SWC, int BITS>
 __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, Rsrc sr, Rsrc zr,
-                                            uint32_t RB, uint32_t GPR, uint4 *xb0, uint4 *xb1,
-                                            float2 *sb0, float2 *sb1, float *red) {
-  using Gm = SkGeo<MB, KW, BITS>;
-  constexpr int CW = Gm::CW, PH = Gm::PH, GPS = Gm::GPS, G = Gm::G, NCL = Gm::NCL;
-  constexpr int SPT = Gm::SPT;
+                                            uint32_t RB, uint32_t GPR, uint4 *xb, uint4 *ss,
+                                            uint4 *zz, float *red) {
+  using Gm = SkGeo<MB, KW, SWC, BITS>;
+  constexpr int CW = Gm::CW, GPS = Gm::GPS, NCL = Gm::NCL, PS = Gm::PS, PZ = Gm::PZ;
   constexpr uint32_t BIAS = ACT == 0 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
-  constexpr uint32_t ONES = ACT == 0 ? 0x3f803f80u : 0x3c003c00u;
-  constexpr float BIASF = ACT == 0 ? 128.f : 1024.f;
   constexpr uint32_t STEPB = SK_STEP * BITS / 8;     // code bytes per channel per step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,164 +161,172 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   auto kend = [&](int k) { return min(a.s0 + (k + 1) * a.sw, a.s1); };
   const int kb = kbeg(kw), ke = kend(kw);
 
-  // ---- x DMA: per phase 4 * SK_SLOTS loads of 1 KB (4 rows x 128 k);
-  // wave w issues loads 8w .. 8w + 7.  Load j fills rows 4(j&3) .. +3 of
-  // block b = j/4 = (k-way * PH + step) * MB + mb; lane l takes row
-  // rr = 4(j&3) + l/16 of the block and writes slot 16 rr + l%16, which holds
-  // chunk (l%16) ^ rr of that row.
-  constexpr int XL = 4 * SK_SLOTS / SK_WAVES;        // DMA loads per wave per phase
-  uint32_t xrow[XL];                                 // byte offset of the lane's row and chunk
-  int xkc[XL];                                       // k of the lane's chunk within a step
-#pragma unroll
-  for (int q = 0; q < XL; ++q) {
-    const int j = XL * wave + q;
-    const int b = j >> 2, mb = b % MB;
-    const int rr = 4 * (j & 3) + (lane >> 4);
-    const int row = 16 * mb + rr;
+  // ---- x: block b = (k-way * SWC + step) * MB + mb holds 16 rows x 128 k;
+  // wave w loads rows 4w .. 4w + 3 of every block (1 KB per load); lane l
+  // takes row rr = 4w + l/16 of the block and fills slot 16 rr + l%16 with
+  // chunk (l%16) ^ rr of that row.  Rows past M are not loaded (their MFMA
+  // output rows are discarded).
+  {
+    const int rr = 4 * wave + (lane >> 4);
     const int c = (lane & 15) ^ rr;
-    xkc[q] = 8 * c;
-    xrow[q] = row < a.M ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)(8 * c)) * 2u : SK_OOB;
-  }
-  auto issue_x = [&](int p, uint4 *dst) {
 #pragma unroll
-    for (int q = 0; q < XL; ++q) {
-      const int j = XL * wave + q;
-      const int b = j >> 2;
-      const int kwb = b / (PH * MB), st = (b / MB) % PH;
-      const int gs = kbeg(kwb) + p * PH + st;
-      const bool ok = xrow[q] != SK_OOB && gs < kend(kwb) && gs * SK_STEP + xkc[q] < a.K;
-      const uint32_t off = ok ? xrow[q] + (uint32_t)gs * (SK_STEP * 2) : SK_OOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(dst + b * SK_XBLK + 64 * (j & 3)), 16,
-                                               off, 0, 0, 0);
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 16 * mb + rr;
+      if (16 * mb + 4 * wave < a.M) {                 // uniform
+        const uint32_t rowoff = row < a.M ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)(8 * c)) * 2u
+                                          : SK_OOB;
+#pragma unroll
+        for (int t = 0; t < KW * SWC; ++t) {
+          const int kwb = t / SWC, st = t % SWC;
+          const int gs = kbeg(kwb) + st;
+          const bool ok = rowoff != SK_OOB && gs < kend(kwb) && gs * SK_STEP + 8 * c < a.K;
+          const uint32_t off = ok ? rowoff + (uint32_t)gs * (SK_STEP * 2) : SK_OOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xr, (lds_void *)(xb + (t * MB + mb) * SK_XBLK + 64 * wave), 16, off, 0, 0, 0);
+        }
+      }
     }
+  }
+
+  // ---- scales and zero points: for each (channel, k-way) pair the runs of
+  // its groups, read as 16-byte pieces from the 16-byte boundary at or below
+  // the run's start (the arrays start 16-byte aligned)
+  constexpr int SPS = (64 * PS + 255) / 256, SPZ = (64 * PZ + 255) / 256;
+  uint4 spv[SPS], zpv[SPZ];
+  auto run_start = [&](int pair) {
+    return a.g_blk + (uint32_t)(a.rw0 + pair / KW) * GPR + (uint32_t)(kbeg(pair % KW) * GPS);
   };
+#pragma unroll
+  for (int j = 0; j < SPS; ++j) {
+    const int u = tid + 256 * j, pair = u / PS, piece = u % PS;
+    const bool ok = u < 64 * PS && pair / KW < a.nvalid;
+    spv[j] = ld128(sr, ok ? ((2u * run_start(pair)) & ~15u) + 16u * piece : SK_OOB);
+  }
+#pragma unroll
+  for (int j = 0; j < SPZ; ++j) {
+    const int u = tid + 256 * j, pair = u / PZ, piece = u % PZ;
+    const bool ok = u < 64 * PZ && pair / KW < a.nvalid;
+    zpv[j] = ld128(zr, ok ? (run_start(pair) & ~15u) + 16u * piece : SK_OOB);
+  }
 
   // ---- codes of the lane's channel and k-way, straight to registers.
   // INT4: one 16-byte load per step (chunks 4g .. 4g + 3); INT2: one per
   // two steps (lane group g gets bytes 16g .. 16g + 15 of the pair's 64).
+  // Code loads are issued CWIN loads ahead of their use, so they return in
+  // step order and each step computes as soon as its codes are in.
+  constexpr int CWIN = NCL < SK_CWIN ? NCL : SK_CWIN;
+  uint32_t cw[NCL][4];
   const uint32_t crow = ch_ok ? (uint32_t)(a.rw0 + cl) * RB : SK_OOB;
-  auto issue_codes = [&](int p, uint32_t (*dst)[4]) {
-#pragma unroll
-    for (int s = 0; s < NCL; ++s) {
-      int gs, lstep;
-      if constexpr (BITS == 4) {
-        gs = kb + p * PH + s;
-        lstep = gs;
-      } else {
-        gs = kb + p * PH + 2 * s;
-        lstep = gs + (g >> 1);
-      }
-      const uint32_t off = (crow != SK_OOB && lstep < ke) ? crow + (uint32_t)gs * STEPB + 16u * g
-                                                          : SK_OOB;
-      const uint4 v = ld128(cr, off);
-      dst[s][0] = v.x; dst[s][1] = v.y; dst[s][2] = v.z; dst[s][3] = v.w;
-    }
+  auto load_codes = [&](int s) {
+    const int gs = BITS == 4 ? kb + s : kb + 2 * s;
+    const int lstep = BITS == 4 ? gs : gs + (g >> 1);
+    const uint32_t off = (crow != SK_OOB && lstep < ke) ? crow + (uint32_t)gs * STEPB + 16u * g
+                                                        : SK_OOB;
+    const uint4 v = ld128(cr, off);
+    cw[s][0] = v.x; cw[s][1] = v.y; cw[s][2] = v.z; cw[s][3] = v.w;
   };
+#pragma unroll
+  for (int s = 0; s < CWIN; ++s) load_codes(s);
 
-  // ---- scales and zero points: entry u = (channel, k-way) pair u / G, group
-  // u % G of the phase; staged in LDS as (S, -(B + z)) at [group][pair].
-  // Groups past the k-way's range or past K get S = 0.
-  uint32_t sv[SPT], zv[SPT];
-  bool sok[SPT];
-  auto issue_scales = [&](int p) {
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      const int u = tid + 256 * j;
-      const int pi = u / G, gi = u % G;
-      const int c = pi / KW, k = pi % KW;
-      const int gs = kbeg(k) + p * PH + gi / GPS, h = gi % GPS;
-      const bool ok = u < 64 * G && c < a.nvalid && gs < kend(k) && gs * SK_STEP + h * 64 < a.K;
-      const uint32_t gidx = ok ? (uint32_t)(a.rw0 + c) * GPR + (uint32_t)(gs * GPS + h) : SK_OOB / 4u;
-      sok[j] = ok;
-      sv[j] = ld16(sr, 2u * gidx);
-      zv[j] = ld8(zr, gidx);
-    }
-  };
-  auto store_scales = [&](float2 *dst) {
+  for (int j = 0; j < SPS; ++j)
+    if (tid + 256 * j < 64 * PS) ss[tid + 256 * j] = spv[j];
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      const int u = tid + 256 * j;
-      if (u < 64 * G) {
-        const int pi = u / G, gi = u % G;
-        dst[gi * 64 + pi] = make_float2(sok[j] ? f16_bits_to_f32((uint16_t)sv[j]) : 0.f,
-                                        -(BIASF + (float)zv[j]));
-      }
-    }
-  };
+  for (int j = 0; j < SPZ; ++j)
+    if (tid + 256 * j < 64 * PZ) zz[tid + 256 * j] = zpv[j];
+  lds_barrier();
 
   floatx4 yacc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) yacc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  const uint4 ones = make_uint4(ONES, ONES, ONES, ONES);
-  const int pidx = cl * KW + kw;                     // the lane's (channel, k-way) pair
+  // the lane's scale and zero runs in LDS
+  const int pidx = cl * KW + kw;
+  const uint32_t g0 = a.g_blk + (uint32_t)(a.rw0 + cl) * GPR + (uint32_t)(kb * GPS);
+  const uint16_t *srun = reinterpret_cast<const uint16_t *>(
+      reinterpret_cast<const uint8_t *>(ss + pidx * PS) + ((2u * g0) & 15u));
+  const uint8_t *zrun = reinterpret_cast<const uint8_t *>(zz + pidx * PZ) + (g0 & 15u);
 
-  auto compute = [&](const uint4 *xb, const float2 *sb, uint32_t (*cw)[4]) {
-    if constexpr (BITS == 2) {
+  // Per group the MFMAs accumulate sum x (B + q) and, against a constant
+  // operand -(B + z) (exact in bf16 / fp16 for z <= 15), sum x * -(B + z)
+  // into the same registers: the result is sum x (q - z), scaled by s in
+  // fp32 afterwards.  Software-pipelined over steps: while step st is
+  // multiplied, the A fragments, scales and zero points of step st + 1 are
+  // read from LDS, the codes of a later step are requested, and the scaling
+  // of step st - 1 is applied (its MFMA results are complete by then).
+  // Steps past the k-way's range add zeros.
+  constexpr uint32_t NEGB = ACT == 0 ? 0xc300c300u : 0xe400e400u;   // -(B + 0) pairs
+  uint4 av[2][4][MB];
+  float sc[3][GPS];
+  uint32_t zp[2][GPS];
+  floatx4 gacc[2][GPS][MB];
+  auto read_step = [&](int st, uint4 (&A)[4][MB], float (&S)[GPS], uint32_t (&Z)[GPS]) {
 #pragma unroll
-      for (int s = 0; s < NCL; ++s) transpose4(cw[s]);
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 16 * r + (sk_chunk<BITS>(g, i) ^ r);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) A[i][mb] = xb[((kw * SWC + st) * MB + mb) * SK_XBLK + slot];
     }
 #pragma unroll
-    for (int st = 0; st < PH; ++st) {
-      floatx4 gacc[MB], gsum[MB];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t w;
-        if constexpr (BITS == 4) {
-          w = cw[st][i];
-        } else {
-          const uint32_t t = cw[st >> 1][2 * (st & 1) + (i >> 1)];
-          w = (i & 1) ? (t >> 16) : (t & 0xffffu);
-        }
-        const uint4 b = unpack_chunk<BITS>(w, BIAS);
-        const bool first = BITS == 4 ? i == 0 : (i & 1) == 0;   // first MFMA of a group
-        const int slot = 16 * r + (sk_chunk<BITS>(g, i) ^ r);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const uint4 av = xb[((kw * PH + st) * MB + mb) * SK_XBLK + slot];
-          gacc[mb] = mfma16<ACT>(av, b, first ? zero4 : gacc[mb]);
-          gsum[mb] = mfma16<ACT>(av, ones, first ? zero4 : gsum[mb]);
-        }
-        const bool last = BITS == 4 ? i == 3 : (i & 1) == 1;
-        if (last) {
-          const int h = BITS == 4 ? 0 : (i >> 1);
-          const float2 sc = sb[(st * GPS + h) * 64 + pidx];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              yacc[mb][e] = fmaf(sc.x, fmaf(sc.y, gsum[mb][e], gacc[mb][e]), yacc[mb][e]);
-          // apply the group here: deferring the corrections would keep every
-          // group's MFMA results of the phase live
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(yacc[mb]));
-        }
-      }
+    for (int h = 0; h < GPS; ++h) {
+      const int gs = kb + st;
+      // groups past the k-way's range or past K, and channels past N, get
+      // scale 0 (their x or codes read as zeros)
+      const bool ok = ch_ok && gs < ke && gs * SK_STEP + h * 64 < a.K;
+      const float sraw = f16_bits_to_f32(srun[st * GPS + h]);
+      S[h] = ok ? sraw : 0.f;
+      const uint32_t z = zrun[st * GPS + h];
+      Z[h] = NEGB | z | (z << 16);
     }
   };
-
-  // ---- phases: compute p while p + 1 is in flight (loads of phases past
-  // the k-way's range are out of range: no traffic, zeros)
-  uint32_t c0[NCL][4], c1[NCL][4];
-  issue_scales(0);
-  issue_x(0, xb0);
-  issue_codes(0, c0);
-  store_scales(sb0);
-  lds_barrier();
-  for (int p = 0; p < a.np; p += 2) {
-    issue_scales(p + 1);
-    issue_x(p + 1, xb1);
-    issue_codes(p + 1, c1);
-    compute(xb0, sb0, c0);
-    store_scales(sb1);
-    lds_barrier();
-    issue_scales(p + 2);
-    issue_x(p + 2, xb0);
-    issue_codes(p + 2, c0);
-    compute(xb1, sb1, c1);
-    store_scales(sb0);
-    lds_barrier();
+  auto scale_step = [&](const floatx4 (&ga)[GPS][MB], const float (&S)[GPS]) {
+#pragma unroll
+    for (int h = 0; h < GPS; ++h)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[mb][e] = fmaf(S[h], ga[h][mb][e], yacc[mb][e]);
+    // keep the scaling here: otherwise it is all moved after the last step
+    // and every step's MFMA results stay live
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(yacc[mb]));
+  };
+  read_step(0, av[0], sc[0], zp[0]);
+#pragma unroll
+  for (int st = 0; st < SWC; ++st) {
+    const int cur = st & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < SWC) read_step(st + 1, av[cur ^ 1], sc[(st + 1) % 3], zp[cur ^ 1]);
+    // the load CWIN ahead of this step's
+    if constexpr (BITS == 4) {
+      if (st + CWIN < NCL) load_codes(st + CWIN);
+    } else {
+      if ((st & 1) == 0 && (st >> 1) + CWIN < NCL) load_codes((st >> 1) + CWIN);
+      if ((st & 1) == 0) transpose4(cw[st >> 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w;
+      if constexpr (BITS == 4) {
+        w = cw[st][i];
+      } else {
+        const uint32_t t = cw[st >> 1][2 * (st & 1) + (i >> 1)];
+        w = (i & 1) ? (t >> 16) : (t & 0xffffu);
+      }
+      const uint4 b = unpack_chunk<BITS>(w, BIAS);
+      const int h = BITS == 4 ? 0 : (i >> 1);
+      const bool first = BITS == 4 ? i == 0 : (i & 1) == 0;   // first MFMA of a group
+      const uint4 zb = make_uint4(zp[cur][h], zp[cur][h], zp[cur][h], zp[cur][h]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        gacc[cur][h][mb] = mfma16<ACT>(av[cur][i][mb], b, first ? zero4 : gacc[cur][h][mb]);
+        gacc[cur][h][mb] = mfma16<ACT>(av[cur][i][mb], zb, gacc[cur][h][mb]);
+      }
+    }
+    if (st > 0) scale_step(gacc[cur ^ 1], sc[(st - 1) % 3]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  scale_step(gacc[(SWC - 1) & 1], sc[(SWC - 1) % 3]);
 
   // ---- k-ways meet in LDS, summed in k-way order
   if constexpr (KW > 1) {
@@ -369,32 +376,23 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
 
 // BITSEL: 4 or 2 for a uniform (Layer-mix) linear, 0 for Channel-mix blocks
 // of either width (the channels of a workgroup lie in one block).
-template <int ACT, int MB, int KW, int BITSEL>
+template <int ACT, int MB, int KW, int SWC, int BITSEL>
 __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(
     LayoutDev L, int M, const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    uint16_t *__restrict__ y, float *__restrict__ part, int sps, int sw, int np) {
-  // double-buffered x tiles and (scale, zero) tables; separate arrays so the
-  // wait before reading one buffer does not cover the loads into the other
-  constexpr int GMAX = SK_SLOTS / (KW * MB) * (BITSEL == 4 ? 1 : 2);
-  __shared__ __attribute__((aligned(16))) uint4 xb0[SK_SLOTS * SK_XBLK];
-  __shared__ __attribute__((aligned(16))) uint4 xb1[SK_SLOTS * SK_XBLK];
-  __shared__ __attribute__((aligned(16))) float2 sb0[64 * GMAX];
-  __shared__ __attribute__((aligned(16))) float2 sb1[64 * GMAX];
+    uint16_t *__restrict__ y, float *__restrict__ part, int sps, int sw) {
+  using G2 = SkGeo<MB, KW, SWC, BITSEL == 4 ? 4 : 2>;   // the larger scale runs
+  __shared__ __attribute__((aligned(16))) uint4 xb[G2::NB * SK_XBLK];
+  __shared__ __attribute__((aligned(16))) uint4 ss[64 * G2::PS];
+  __shared__ __attribute__((aligned(16))) uint4 zz[64 * G2::PZ];
   __shared__ __attribute__((aligned(16))) float red[KW > 1 ? 3 * 64 * 4 * MB : 1];
-  // the x tiles start zeroed: every slot a load does not fill stays finite
-  for (int i = (int)threadIdx.x; i < SK_SLOTS * SK_XBLK; i += 64 * SK_WAVES) {
-    xb0[i] = make_uint4(0u, 0u, 0u, 0u);
-    xb1[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  lds_barrier();
   constexpr int NC = 16 * (SK_WAVES / KW);
   const int nsteps = (L.K + SK_STEP - 1) / SK_STEP;
   SkArgs a;
   a.M = M; a.K = L.K; a.N = L.N;
   a.s0 = (int)blockIdx.y * sps;
   a.s1 = min(a.s0 + sps, nsteps);
-  a.sw = sw; a.np = np;
+  a.sw = sw;
   a.nsplit = (int)gridDim.y;
   const int n0 = (int)blockIdx.x * NC;
   a.n0 = n0;
@@ -411,59 +409,76 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(
   const int bits = BITSEL ? BITSEL : __builtin_amdgcn_readfirstlane(bi.bits);
   const uint32_t RB = (uint32_t)(L.K * bits / 8);
   const uint32_t GPR = (uint32_t)(bits == 4 ? L.K / 128 : L.K / 64);
+  a.g_blk = (uint32_t)bi.grp_off;
+  const uint32_t gend = a.g_blk + (uint32_t)L.block_n * GPR;   // past the block's groups
   const Rsrc xr = make_rsrc(x, (uint32_t)M * (uint32_t)L.K * 2u);
   const Rsrc cr = make_rsrc(codes + bi.code_off, (uint32_t)L.block_n * RB);
-  const Rsrc sr = make_rsrc(scales + bi.grp_off, (uint32_t)L.block_n * GPR * 2u);
-  const Rsrc zr = make_rsrc(zeros + bi.grp_off, (uint32_t)L.block_n * GPR);
+  const Rsrc sr = make_rsrc(scales, 2u * gend);
+  const Rsrc zr = make_rsrc(zeros, gend);
   if (BITSEL != 2 && bits == 4)
-    skinny_tile<ACT, MB, KW, 4>(a, xr, cr, sr, zr, RB, GPR, xb0, xb1, sb0, sb1, red);
+    skinny_tile<ACT, MB, KW, SWC, 4>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz, red);
   else if constexpr (BITSEL != 4)
-    skinny_tile<ACT, MB, KW, 2>(a, xr, cr, sr, zr, RB, GPR, xb0, xb1, sb0, sb1, red);
+    skinny_tile<ACT, MB, KW, SWC, 2>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz, red);
 }
 
 struct SkPlan {
-  int mb, kw, tiles, nsplit, sps, sw, np;
+  int mb, kw, swc, tiles, nsplit, sps, sw;
   size_t part_bytes;
 };
 
-// Launch shape.  16-row blocks: 1 for M <= 16, else 2.  k-ways: the fewest
-// that give at least kSkFill workgroups (more k-ways stage more x per code
-// byte), at most 4 / blocks (a phase holds at least two steps).  K is split
-// across workgroups only while fewer than kSkMinTiles would exist.  Workspace:
-// fp32 partials [nsplit][M][N] when K is split.
-constexpr int kSkFill = 224;
-constexpr int kSkMinTiles = 48;
+// Launch shape, from a rough time model in units of one step of one wave:
+// the busiest CU works through ceil(workgroups / CUs) k ranges of sw steps,
+// each round of resident workgroups adds a latency of about 8, and
+// splitting K adds about 16 for the second pass.  16-row blocks: 1 for
+// M <= 16, else 2.  Capacity: x for KW * steps * blocks <= 32 block-steps
+// in LDS, at most 32 steps per wave.  Workspace: fp32 partials
+// [nsplit][M][N] when K is split.
+constexpr int kCUs = 256;
 
-inline SkPlan skinny_plan(const LayoutDev &L, int M) {
-  SkPlan p;
-  p.mb = M <= 16 ? 1 : 2;
-  const int kwmax = 4 / p.mb;
-  p.kw = kwmax;
-  for (int kw = 1; kw <= kwmax; kw *= 2) {
-    if ((L.N + 64 / kw - 1) / (64 / kw) >= kSkFill) {
-      p.kw = kw;
-      break;
-    }
-  }
-  p.tiles = (L.N + 64 / p.kw - 1) / (64 / p.kw);
-  const int ph = SK_SLOTS / (p.kw * p.mb);
-  const int nsteps = (L.K + SK_STEP - 1) / SK_STEP;
-  p.nsplit = 1;
-  while (p.tiles * p.nsplit < kSkMinTiles && nsteps >= 2 * p.nsplit * p.kw * ph) p.nsplit *= 2;
-  p.sps = (nsteps + p.nsplit - 1) / p.nsplit;
-  p.nsplit = (nsteps + p.sps - 1) / p.sps;
-  p.sw = (p.sps + p.kw - 1) / p.kw;
-  p.np = (p.sw + ph - 1) / ph;
-  p.np += p.np & 1;
-  p.part_bytes = p.nsplit > 1 ? ((size_t)p.nsplit * (size_t)M * (size_t)L.N * 4u + 255u) & ~(size_t)255u
-                              : 0u;
-  return p;
+inline size_t skinny_lds_bytes(int mb, int kw, int swc) {
+  const int r = swc * 2;                              // sized for INT2 runs
+  return (size_t)kw * swc * mb * SK_XBLK * 16 + 64 * 16 * ((2 * r + 29) / 16 + (r + 30) / 16) +
+         (kw > 1 ? 3 * 64 * 4 * mb * 4 : 0);
 }
 
-template <int ACT, int MB, int KW>
-hipError_t launch_kw(const LayoutDev &L, int M, const SkPlan &p, const void *x,
-                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *y,
-                     void *workspace, hipStream_t s) {
+inline SkPlan skinny_plan(const LayoutDev &L, int M) {
+  SkPlan best{};
+  int best_cost = 0x7fffffff;
+  const int mb = M <= 16 ? 1 : 2;
+  const int nsteps = (L.K + SK_STEP - 1) / SK_STEP;
+  for (int kw = 1; kw <= 4 / mb; kw *= 2) {
+    const int tiles = (L.N + 64 / kw - 1) / (64 / kw);
+    const int cap = min(SK_SWMAX, SK_XCAP / (kw * mb));
+    if (cap < 8) continue;
+    for (int ns = 1; ns <= nsteps; ++ns) {
+      const int sps = (nsteps + ns - 1) / ns;
+      const int nsplit = (nsteps + sps - 1) / sps;
+      if (nsplit != ns) continue;
+      const int sw = (sps + kw - 1) / kw;
+      if (sw > cap) continue;
+      const int swc = sw <= 8 ? 8 : sw <= 16 ? 16 : 32;
+      const int per_cu = max(1, min(2, (int)((160u * 1024u) / skinny_lds_bytes(mb, kw, swc))));
+      const int wgs = tiles * nsplit;
+      const int rounds = (wgs + kCUs * per_cu - 1) / (kCUs * per_cu);
+      const int cost = 10 * ((wgs + kCUs - 1) / kCUs * sw + 8 * rounds + (nsplit > 1 ? 16 : 0)) + kw;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best.mb = mb; best.kw = kw; best.swc = swc; best.tiles = tiles;
+        best.nsplit = nsplit; best.sps = sps; best.sw = sw;
+      }
+      if (wgs >= kCUs) break;                         // more splits only add cost
+    }
+  }
+  best.part_bytes = best.nsplit > 1
+                        ? ((size_t)best.nsplit * (size_t)M * (size_t)L.N * 4u + 255u) & ~(size_t)255u
+                        : 0u;
+  return best;
+}
+
+template <int ACT, int MB, int KW, int SWC>
+hipError_t launch_cfg(const LayoutDev &L, int M, const SkPlan &p, const void *x,
+                      const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *y,
+                      void *workspace, hipStream_t s) {
   float *part = reinterpret_cast<float *>(workspace);
   uint16_t *yp = reinterpret_cast<uint16_t *>(y);
   uint32_t any4 = 0, all4 = ~0u;
@@ -476,17 +491,33 @@ hipError_t launch_kw(const LayoutDev &L, int M, const SkPlan &p, const void *x,
   const uint16_t *xp = reinterpret_cast<const uint16_t *>(x);
   const uint8_t *cp = reinterpret_cast<const uint8_t *>(codes);
   if (all4)
-    hipLaunchKernelGGL((skinny_kernel<ACT, MB, KW, 4>), grid, block, 0, s, L, M, xp, cp, scales, zeros,
-                       yp, part, p.sps, p.sw, p.np);
+    hipLaunchKernelGGL((skinny_kernel<ACT, MB, KW, SWC, 4>), grid, block, 0, s, L, M, xp, cp, scales,
+                       zeros, yp, part, p.sps, p.sw);
   else if (!any4)
-    hipLaunchKernelGGL((skinny_kernel<ACT, MB, KW, 2>), grid, block, 0, s, L, M, xp, cp, scales, zeros,
-                       yp, part, p.sps, p.sw, p.np);
+    hipLaunchKernelGGL((skinny_kernel<ACT, MB, KW, SWC, 2>), grid, block, 0, s, L, M, xp, cp, scales,
+                       zeros, yp, part, p.sps, p.sw);
   else
-    hipLaunchKernelGGL((skinny_kernel<ACT, MB, KW, 0>), grid, block, 0, s, L, M, xp, cp, scales, zeros,
-                       yp, part, p.sps, p.sw, p.np);
+    hipLaunchKernelGGL((skinny_kernel<ACT, MB, KW, SWC, 0>), grid, block, 0, s, L, M, xp, cp, scales,
+                       zeros, yp, part, p.sps, p.sw);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   return launch_splitk_reduce(part, p.nsplit, M, L.N, nullptr, yp, ACT, s);
+}
+
+template <int ACT, int MB, int KW>
+hipError_t launch_kw(const LayoutDev &L, int M, const SkPlan &p, const void *x,
+                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *y,
+                     void *workspace, hipStream_t s) {
+  constexpr int CAP = SK_XCAP / (KW * MB) < SK_SWMAX ? SK_XCAP / (KW * MB) : SK_SWMAX;
+  if (p.swc == 8 || CAP < 16)
+    return launch_cfg<ACT, MB, KW, 8>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  if constexpr (CAP >= 16) {
+    if (p.swc == 16 || CAP < 32)
+      return launch_cfg<ACT, MB, KW, 16>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  }
+  if constexpr (CAP >= 32)
+    return launch_cfg<ACT, MB, KW, 32>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  return hipErrorInvalidValue;
 }
 
 template <int ACT>
@@ -506,8 +537,14 @@ hipError_t launch_act(const LayoutDev &L, int M, const void *x, const uint32_t *
 }  // namespace
 
 bool skinny_supported(const LayoutDev &L, int M) {
-  return M > kGemvMaxM && M <= kSkinnyMaxM && (uint64_t)M * (uint64_t)L.K * 2u < (1ull << 31) &&
-         (uint64_t)L.block_n * (uint64_t)L.K / 2u < (1ull << 31);
+  if (M <= kGemvMaxM || M > kSkinnyMaxM) return false;
+  if ((uint64_t)M * (uint64_t)L.K * 2u >= (1ull << 31)) return false;
+  if ((uint64_t)L.block_n * (uint64_t)L.K / 2u >= (1ull << 31)) return false;
+  // scale byte offsets of the whole layer stay below 2^31
+  uint64_t groups = 0;
+  for (int i = 0; i < L.nblocks; ++i)
+    groups += (uint64_t)L.block_n * (uint64_t)(((L.int4_mask[i >> 5] >> (i & 31)) & 1u) ? L.K / 128 : L.K / 64);
+  return 2u * groups < (1ull << 31);
 }
 
 size_t skinny_workspace_bytes(const LayoutDev &L, int M) { return skinny_plan(L, M).part_bytes; }

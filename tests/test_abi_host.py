@@ -105,15 +105,17 @@ def test_argument_errors_before_launch(lib):
 
 def test_workspace_sizes():
     lay = gq.make_layout(4096, 14336, 14336, [4])
-    # dot-product path, and the small-batch path on a wide layer: no scratch
-    for M in (0, 1, 4, 5, 32):
+    # dot-product path, and the small-batch path on a wide layer up to 16
+    # rows (its whole k range fits one workgroup): no scratch
+    for M in (0, 1, 4, 5, 16):
         assert gq.gq_linear_workspace_bytes(lay, M) == 0
     # GEMM path: fp16 activations padded to whole tiles, row exponents
     for M in (64, 2048):
         ws = gq.gq_linear_workspace_bytes(lay, M)
         assert ws >= M * 4096 * 2 + M * 4 and ws % 256 == 0
-    # a narrow layer with long K splits K across workgroups: fp32 partials
-    narrow = gq.make_layout(4096, 256, 256, [4])
+    # a narrow layer with a K range too long for one workgroup splits K
+    # across workgroups: fp32 partials
+    narrow = gq.make_layout(28672, 256, 256, [4])
     ws = gq.gq_linear_workspace_bytes(narrow, 8)
     assert ws >= 2 * 8 * 256 * 4 and ws % 256 == 0
 
