@@ -82,17 +82,20 @@ __device__ __forceinline__ float dpp(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
-// Exchange halves between two registers (gfx950 lane swaps):
-//   swap32: lanes 32..63 of a  <->  lanes 0..31 of b
-//   swap16: odd rows of 16 lanes of a  <->  even rows of b
-// Afterwards a + b holds, in lanes whose bit 5 (bit 4) is clear, the sum of
-// a over the two halves, and in the others the sum of b.  The leading s_nop
-// covers the wait states the swap needs after a VALU write of its operands.
+// Exchange halves between two registers (the lane swaps of gq_device.h on
+// float bits).  Afterwards a + b holds, in lanes whose bit 5 (bit 4) is
+// clear, the sum of a over the two halves, and in the others the sum of b.
 __device__ __forceinline__ void swap32(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+  gq::swap32(ua, ub);
+  a = __builtin_bit_cast(float, ua);
+  b = __builtin_bit_cast(float, ub);
 }
 __device__ __forceinline__ void swap16(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+  gq::swap16(ua, ub);
+  a = __builtin_bit_cast(float, ua);
+  b = __builtin_bit_cast(float, ub);
 }
 
 // Sum V per-lane values over the 64 lanes of a wave.  Halving exchanges first

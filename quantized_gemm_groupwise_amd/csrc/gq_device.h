@@ -28,12 +28,27 @@ __device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off, uint32_t soff = 0)
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
 }
 
-// (a & m) | o in one VALU op (the three operands in VGPRs; gfx9 VOP3 takes
-// no literal constants).
+// (a & m) | o in one VALU op: gfx950's three-input bitwise op with truth
+// table 0xEA (bit i of the table is the result for input bits
+// (a, m, o) = (i >> 2 & 1, i >> 1 & 1, i & 1)).  A builtin rather than
+// inline assembly, so the compiler sees the instruction and keeps its wait
+// states against in-flight matrix instructions.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
+  return __builtin_amdgcn_bitop3_b32(a, m, o, 0xEA);
+}
+
+// Lane exchange between two registers (gfx950 lane swaps):
+//   swap32: lanes 32..63 of a  <->  lanes 0..31 of b
+//   swap16: odd rows of 16 lanes of a  <->  even rows of b
+__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
 }
 
 // LDS barrier for data written to LDS only: waits for this wave's LDS

@@ -48,10 +48,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int SK_WAVES = 4;
+constexpr int SK_WAVES = 8;                     // two per SIMD
+constexpr int SK_THREADS = 64 * SK_WAVES;
+constexpr int SK_PAIRS = 16 * SK_WAVES;         // (channel, k-way) pairs per workgroup
 constexpr int SK_STEP = 128;                    // k per step
 constexpr int SK_XCAP = 32;                     // x blocks (step x k-way x 16 rows) per workgroup
-constexpr int SK_SWMAX = 32;                    // steps per wave (code registers)
+constexpr int SK_SWMAX = 16;                    // steps per wave (code registers)
 constexpr int SK_CWIN = 12;                     // code loads in flight per lane
 constexpr int SK_XBLK = 256;                    // 16-byte LDS slots per 16-row x block of a step
 constexpr uint32_t SK_OOB = 0x80000000u;        // beyond every buffer resource
@@ -97,23 +99,15 @@ __device__ __forceinline__ uint4 unpack_chunk(uint32_t w, uint32_t bias) {
   return b;
 }
 
-// Lane-group exchange on gfx950 (the leading s_nop covers the wait states
-// the swaps need after a VALU write of their operands):
-//   swap32: lanes 32..63 of a  <->  lanes 0..31 of b
-//   swap16: odd rows of 16 lanes of a  <->  even rows of b
-__device__ __forceinline__ void swap32u(uint32_t &a, uint32_t &b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap16u(uint32_t &a, uint32_t &b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
 // Lane group g holds words 4g .. 4g + 3 of a 16-word block in (v[0..3]);
 // afterwards it holds words g, 4 + g, 8 + g, 12 + g.
+// (gfx950 lane swaps: swap32 exchanges lane groups 0, 1 of one register
+// with 2, 3 of the other, swap16 groups 1, 3 with 0, 2.)
 __device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
-  swap32u(v[0], v[2]);
-  swap32u(v[1], v[3]);
-  swap16u(v[0], v[1]);
-  swap16u(v[2], v[3]);
+  swap32(v[0], v[2]);
+  swap32(v[1], v[3]);
+  swap16(v[0], v[1]);
+  swap16(v[2], v[3]);
 }
 
 template <int MB, int KW, int SWC, int BITS>
@@ -126,7 +120,7 @@ struct SkGeo {
   static constexpr int PS = (2 * R + 14 + 15) / 16;   // 16-byte scale pieces per (channel, k-way)
   static constexpr int PZ = (R + 15 + 15) / 16;       // 16-byte zero pieces
   static constexpr int NCL = BITS == 4 ? SWC : SWC / 2;   // 16-byte code loads per lane
-  static_assert(NC * KW == 64 && NB <= SK_XCAP && SWC <= SK_SWMAX && SWC % 8 == 0, "geometry");
+  static_assert(NC * KW == SK_PAIRS && NB <= SK_XCAP && SWC <= SK_SWMAX && SWC % 4 == 0, "geometry");
 };
 
 struct SkArgs {
@@ -145,7 +139,7 @@ struct SkArgs {
 template <int ACT, int MB, int KW, int SWC, int BITS>
 __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, Rsrc sr, Rsrc zr,
                                             uint32_t RB, uint32_t GPR, uint4 *xb, uint4 *ss,
-                                            uint4 *zz, float *red) {
+                                            uint4 *zz) {
   using Gm = SkGeo<MB, KW, SWC, BITS>;
   constexpr int CW = Gm::CW, GPS = Gm::GPS, NCL = Gm::NCL, PS = Gm::PS, PZ = Gm::PZ;
   constexpr uint32_t BIAS = ACT == 0 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
@@ -162,27 +156,30 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   const int kb = kbeg(kw), ke = kend(kw);
 
   // ---- x: block b = (k-way * SWC + step) * MB + mb holds 16 rows x 128 k;
-  // wave w loads rows 4w .. 4w + 3 of every block (1 KB per load); lane l
-  // takes row rr = 4w + l/16 of the block and fills slot 16 rr + l%16 with
-  // chunk (l%16) ^ rr of that row.  Rows past M are not loaded (their MFMA
-  // output rows are discarded).
+  // wave w loads rows 4q .. 4q + 3 (q = w % 4) of every other block (1 KB
+  // per load); lane l takes row rr = 4q + l/16 of the block and fills slot
+  // 16 rr + l%16 with chunk (l%16) ^ rr of that row.  Rows past M are not
+  // loaded (their MFMA output rows are discarded).
   {
-    const int rr = 4 * wave + (lane >> 4);
+    constexpr int BS = SK_WAVES / 4;                  // waves per row quarter
+    const int qq = wave & 3, bset = wave >> 2;
+    const int rr = 4 * qq + (lane >> 4);
     const int c = (lane & 15) ^ rr;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int row = 16 * mb + rr;
-      if (16 * mb + 4 * wave < a.M) {                 // uniform
+      if (16 * mb + 4 * qq < a.M) {                   // uniform
         const uint32_t rowoff = row < a.M ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)(8 * c)) * 2u
                                           : SK_OOB;
 #pragma unroll
-        for (int t = 0; t < KW * SWC; ++t) {
+        for (int tt = 0; tt < KW * SWC / BS; ++tt) {
+          const int t = tt * BS + bset;
           const int kwb = t / SWC, st = t % SWC;
           const int gs = kbeg(kwb) + st;
           const bool ok = rowoff != SK_OOB && gs < kend(kwb) && gs * SK_STEP + 8 * c < a.K;
           const uint32_t off = ok ? rowoff + (uint32_t)gs * (SK_STEP * 2) : SK_OOB;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              xr, (lds_void *)(xb + (t * MB + mb) * SK_XBLK + 64 * wave), 16, off, 0, 0, 0);
+              xr, (lds_void *)(xb + (t * MB + mb) * SK_XBLK + 64 * qq), 16, off, 0, 0, 0);
         }
       }
     }
@@ -191,21 +188,22 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   // ---- scales and zero points: for each (channel, k-way) pair the runs of
   // its groups, read as 16-byte pieces from the 16-byte boundary at or below
   // the run's start (the arrays start 16-byte aligned)
-  constexpr int SPS = (64 * PS + 255) / 256, SPZ = (64 * PZ + 255) / 256;
+  constexpr int SPS = (SK_PAIRS * PS + SK_THREADS - 1) / SK_THREADS;
+  constexpr int SPZ = (SK_PAIRS * PZ + SK_THREADS - 1) / SK_THREADS;
   uint4 spv[SPS], zpv[SPZ];
   auto run_start = [&](int pair) {
     return a.g_blk + (uint32_t)(a.rw0 + pair / KW) * GPR + (uint32_t)(kbeg(pair % KW) * GPS);
   };
 #pragma unroll
   for (int j = 0; j < SPS; ++j) {
-    const int u = tid + 256 * j, pair = u / PS, piece = u % PS;
-    const bool ok = u < 64 * PS && pair / KW < a.nvalid;
+    const int u = tid + SK_THREADS * j, pair = u / PS, piece = u % PS;
+    const bool ok = u < SK_PAIRS * PS && pair / KW < a.nvalid;
     spv[j] = ld128(sr, ok ? ((2u * run_start(pair)) & ~15u) + 16u * piece : SK_OOB);
   }
 #pragma unroll
   for (int j = 0; j < SPZ; ++j) {
-    const int u = tid + 256 * j, pair = u / PZ, piece = u % PZ;
-    const bool ok = u < 64 * PZ && pair / KW < a.nvalid;
+    const int u = tid + SK_THREADS * j, pair = u / PZ, piece = u % PZ;
+    const bool ok = u < SK_PAIRS * PZ && pair / KW < a.nvalid;
     zpv[j] = ld128(zr, ok ? (run_start(pair) & ~15u) + 16u * piece : SK_OOB);
   }
 
@@ -230,10 +228,10 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
 
 #pragma unroll
   for (int j = 0; j < SPS; ++j)
-    if (tid + 256 * j < 64 * PS) ss[tid + 256 * j] = spv[j];
+    if (tid + SK_THREADS * j < SK_PAIRS * PS) ss[tid + SK_THREADS * j] = spv[j];
 #pragma unroll
   for (int j = 0; j < SPZ; ++j)
-    if (tid + 256 * j < 64 * PZ) zz[tid + 256 * j] = zpv[j];
+    if (tid + SK_THREADS * j < SK_PAIRS * PZ) zz[tid + SK_THREADS * j] = zpv[j];
   lds_barrier();
 
   floatx4 yacc[MB];
@@ -328,8 +326,11 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   __builtin_amdgcn_sched_barrier(0);
   scale_step(gacc[(SWC - 1) & 1], sc[(SWC - 1) % 3]);
 
-  // ---- k-ways meet in LDS, summed in k-way order
+  // ---- k-ways meet in LDS (the x tiles' space, free once every wave is
+  // done with it), summed in k-way order
   if constexpr (KW > 1) {
+    float *red = reinterpret_cast<float *>(xb);
+    lds_barrier();
     if (kw > 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -377,15 +378,15 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
 // BITSEL: 4 or 2 for a uniform (Layer-mix) linear, 0 for Channel-mix blocks
 // of either width (the channels of a workgroup lie in one block).
 template <int ACT, int MB, int KW, int SWC, int BITSEL>
-__global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(
+__global__ __launch_bounds__(SK_THREADS) void skinny_kernel(
     LayoutDev L, int M, const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     uint16_t *__restrict__ y, float *__restrict__ part, int sps, int sw) {
   using G2 = SkGeo<MB, KW, SWC, BITSEL == 4 ? 4 : 2>;   // the larger scale runs
   __shared__ __attribute__((aligned(16))) uint4 xb[G2::NB * SK_XBLK];
-  __shared__ __attribute__((aligned(16))) uint4 ss[64 * G2::PS];
-  __shared__ __attribute__((aligned(16))) uint4 zz[64 * G2::PZ];
-  __shared__ __attribute__((aligned(16))) float red[KW > 1 ? 3 * 64 * 4 * MB : 1];
+  __shared__ __attribute__((aligned(16))) uint4 ss[SK_PAIRS * G2::PS];
+  __shared__ __attribute__((aligned(16))) uint4 zz[SK_PAIRS * G2::PZ];
+  static_assert((KW - 1) * (SK_WAVES / KW) * MB * 4 * 64 <= G2::NB * SK_XBLK * 4, "reduction space");
   constexpr int NC = 16 * (SK_WAVES / KW);
   const int nsteps = (L.K + SK_STEP - 1) / SK_STEP;
   SkArgs a;
@@ -416,9 +417,9 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_kernel(
   const Rsrc sr = make_rsrc(scales, 2u * gend);
   const Rsrc zr = make_rsrc(zeros, gend);
   if (BITSEL != 2 && bits == 4)
-    skinny_tile<ACT, MB, KW, SWC, 4>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz, red);
+    skinny_tile<ACT, MB, KW, SWC, 4>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz);
   else if constexpr (BITSEL != 4)
-    skinny_tile<ACT, MB, KW, SWC, 2>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz, red);
+    skinny_tile<ACT, MB, KW, SWC, 2>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz);
 }
 
 struct SkPlan {
@@ -437,8 +438,8 @@ constexpr int kCUs = 256;
 
 inline size_t skinny_lds_bytes(int mb, int kw, int swc) {
   const int r = swc * 2;                              // sized for INT2 runs
-  return (size_t)kw * swc * mb * SK_XBLK * 16 + 64 * 16 * ((2 * r + 29) / 16 + (r + 30) / 16) +
-         (kw > 1 ? 3 * 64 * 4 * mb * 4 : 0);
+  return (size_t)kw * swc * mb * SK_XBLK * 16 +
+         (size_t)SK_PAIRS * 16 * ((2 * r + 29) / 16 + (r + 30) / 16);
 }
 
 inline SkPlan skinny_plan(const LayoutDev &L, int M) {
@@ -446,17 +447,18 @@ inline SkPlan skinny_plan(const LayoutDev &L, int M) {
   int best_cost = 0x7fffffff;
   const int mb = M <= 16 ? 1 : 2;
   const int nsteps = (L.K + SK_STEP - 1) / SK_STEP;
-  for (int kw = 1; kw <= 4 / mb; kw *= 2) {
-    const int tiles = (L.N + 64 / kw - 1) / (64 / kw);
+  for (int kw = 2; kw <= 8 / mb; kw *= 2) {
+    const int nc = 16 * (SK_WAVES / kw);
+    const int tiles = (L.N + nc - 1) / nc;
     const int cap = min(SK_SWMAX, SK_XCAP / (kw * mb));
-    if (cap < 8) continue;
+    if (cap < 4) continue;
     for (int ns = 1; ns <= nsteps; ++ns) {
       const int sps = (nsteps + ns - 1) / ns;
       const int nsplit = (nsteps + sps - 1) / sps;
       if (nsplit != ns) continue;
       const int sw = (sps + kw - 1) / kw;
       if (sw > cap) continue;
-      const int swc = sw <= 8 ? 8 : sw <= 16 ? 16 : 32;
+      const int swc = sw <= 4 ? 4 : sw <= 8 ? 8 : 16;
       const int per_cu = max(1, min(2, (int)((160u * 1024u) / skinny_lds_bytes(mb, kw, swc))));
       const int wgs = tiles * nsplit;
       const int rounds = (wgs + kCUs * per_cu - 1) / (kCUs * per_cu);
@@ -487,7 +489,7 @@ hipError_t launch_cfg(const LayoutDev &L, int M, const SkPlan &p, const void *x,
     any4 |= b;
     all4 &= b;
   }
-  const dim3 grid(p.tiles, p.nsplit), block(64 * SK_WAVES);
+  const dim3 grid(p.tiles, p.nsplit), block(SK_THREADS);
   const uint16_t *xp = reinterpret_cast<const uint16_t *>(x);
   const uint8_t *cp = reinterpret_cast<const uint8_t *>(codes);
   if (all4)
@@ -508,15 +510,15 @@ template <int ACT, int MB, int KW>
 hipError_t launch_kw(const LayoutDev &L, int M, const SkPlan &p, const void *x,
                      const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *y,
                      void *workspace, hipStream_t s) {
-  constexpr int CAP = SK_XCAP / (KW * MB) < SK_SWMAX ? SK_XCAP / (KW * MB) : SK_SWMAX;
-  if (p.swc == 8 || CAP < 16)
-    return launch_cfg<ACT, MB, KW, 8>(L, M, p, x, codes, scales, zeros, y, workspace, s);
-  if constexpr (CAP >= 16) {
-    if (p.swc == 16 || CAP < 32)
-      return launch_cfg<ACT, MB, KW, 16>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  constexpr int CAP = SK_XCAP / (KW * MB);
+  if (p.swc == 4 || CAP < 8)
+    return launch_cfg<ACT, MB, KW, 4>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  if constexpr (CAP >= 8) {
+    if (p.swc == 8 || CAP < 16)
+      return launch_cfg<ACT, MB, KW, 8>(L, M, p, x, codes, scales, zeros, y, workspace, s);
   }
-  if constexpr (CAP >= 32)
-    return launch_cfg<ACT, MB, KW, 32>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  if constexpr (CAP >= 16)
+    return launch_cfg<ACT, MB, KW, 16>(L, M, p, x, codes, scales, zeros, y, workspace, s);
   return hipErrorInvalidValue;
 }
 
@@ -526,12 +528,12 @@ hipError_t launch_act(const LayoutDev &L, int M, const void *x, const uint32_t *
                       hipStream_t s) {
   const SkPlan p = skinny_plan(L, M);
   if (p.mb == 1) {
-    if (p.kw == 1) return launch_kw<ACT, 1, 1>(L, M, p, x, codes, scales, zeros, y, workspace, s);
     if (p.kw == 2) return launch_kw<ACT, 1, 2>(L, M, p, x, codes, scales, zeros, y, workspace, s);
-    return launch_kw<ACT, 1, 4>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+    if (p.kw == 4) return launch_kw<ACT, 1, 4>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+    return launch_kw<ACT, 1, 8>(L, M, p, x, codes, scales, zeros, y, workspace, s);
   }
-  if (p.kw == 1) return launch_kw<ACT, 2, 1>(L, M, p, x, codes, scales, zeros, y, workspace, s);
-  return launch_kw<ACT, 2, 2>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  if (p.kw == 2) return launch_kw<ACT, 2, 2>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  return launch_kw<ACT, 2, 4>(L, M, p, x, codes, scales, zeros, y, workspace, s);
 }
 
 }  // namespace
