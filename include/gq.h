@@ -136,15 +136,20 @@ gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype
  * Kernels by M:
  *   M <= 4       bandwidth-bound dot-product kernel; (code - z) and S are
  *                applied exactly in fp32.
- *   4 < M <= 32  MFMA on the activations as given (bf16 or fp16) and the
- *                codes as exact B + q values; each group's scale and zero
- *                point are applied in fp32 after its MFMAs.  Long K is split
- *                across workgroups (fp32 partials in the workspace, summed
- *                in split order).
+ *   4 < M <= 32  MFMA on the activations as given (bf16 or fp16), the
+ *                codes as exact B + q values and the zero point as the exact
+ *                constant -(B + z), accumulated per group in fp32; each
+ *                group's scale is applied in fp32 after its MFMAs.  K ranges
+ *                longer than one workgroup holds are split across
+ *                workgroups (fp32 partials in the workspace, summed in split
+ *                order).
  *   M > 32       MFMA GEMM that rounds each dequantized weight once to fp16
  *                (the FP16 matmul of the survey review); activations are
  *                rescaled per row by a power of two so that their fp16 form
- *                is exact; small M splits K across workgroups.
+ *                is exact; small M splits K across workgroups, and with
+ *                256 x 256 tiles the tiles of an incomplete last round are
+ *                split along K (fp32 parts in the workspace, summed in part
+ *                order).
  * Every path is deterministic.  Results agree with the fp64 product of the
  * dequantized weights to about the bf16 output rounding (normwise relative
  * error <= 2e-3). */

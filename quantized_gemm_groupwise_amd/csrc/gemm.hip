@@ -389,7 +389,9 @@ constexpr uint32_t kOob = 0x80000000u;           // beyond every resource
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct BigArgs {
-  int K, Kp, N, M, m0, nkt;
+  int K, Kp, N, M, m0;
+  int kt0, kt1;                                  // k steps [kt0, kt1) of this workgroup (even count)
+  float *tail;                                   // fp32 partial tile of a split tail tile, or null
   const int *rexp;
   uint16_t *y;
   int out_fp16;
@@ -458,7 +460,7 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
   auto step = [&](int kt, const uint4 *cur, uint4 *nxt, const uint32_t (*bc)[BW],
                   const uint32_t *sc, const uint32_t *zc, uint32_t (*bn)[BW], uint32_t *sn,
                   uint32_t *zn) {
-    const int kn = kt + 1 < g.nkt ? kt + 1 : kt;
+    const int kn = kt + 1 < g.kt1 ? kt + 1 : kt;
     __builtin_amdgcn_sched_barrier(0);
     dma_a(kn, nxt);
     load_b(kn, bn, sn, zn);
@@ -526,16 +528,29 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
   };
 
   uint32_t b0[2][BW], b1[2][BW], s0[2], s1[2], z0[2], z1[2];
-  dma_a(0, As0);
-  load_b(0, b0, s0, z0);
+  dma_a(g.kt0, As0);
+  load_b(g.kt0, b0, s0, z0);
   lds_barrier();
-  // g.nkt is even: x is zero-padded to a multiple of 256 in k, and steps
+  // kt1 - kt0 is even: x is zero-padded to a multiple of 256 in k, and steps
   // past K get scale 0
-  for (int kt = 0; kt < g.nkt; kt += 2) {
+  for (int kt = g.kt0; kt < g.kt1; kt += 2) {
     step(kt, As0, As1, b0, s0, z0, b1, s1, z1);
     step(kt + 1, As1, As0, b1, s1, z1, b0, s0, z0);
   }
 
+  if (g.tail) {
+    // part of a split tail tile: the fp32 accumulators in register order
+    // (wave, mb, nb, e, lane), 256 contiguous bytes per store; the tail
+    // reduction sums the parts and writes y
+#pragma unroll
+    for (int mb = 0; mb < BIG_MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          g.tail[(((wave * BIG_MB + mb) * 2 + nb) * 16 + e) * 64 + (threadIdx.x & 63)] = acc[mb][nb][e];
+    return;
+  }
   if (!wave_active) return;
   // epilogue: lane (j, h) holds column ncol0 + 32nb + j and rows
   // 8(e/4) + 4h + e%4 of each 32-row block
@@ -557,11 +572,83 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
   }
 }
 
+// Tail split.  With one 256 x 256 tile per CU at a time, a tile count that
+// is not a multiple of the CU count leaves the last round partly idle.  The
+// last `rem` tiles (rem = tiles mod CUs) are therefore cut along K into
+// `parts` pieces of whole step pairs, run as rem * parts workgroups of the
+// last round, and summed in part order by gemm_tail_reduce_kernel.
+constexpr int kBigCUs = 256;
+constexpr int BIG_TILE_ELEMS = BIG_TM * BIG_TN;
+
+struct TailPlan {
+  int tiles, full, rem, parts, per;   // per: k steps per part (even)
+  size_t bytes;                       // fp32 partial tiles
+};
+
+inline TailPlan tail_plan(int tiles, int nkt) {
+  TailPlan t;
+  t.tiles = tiles;
+  t.rem = tiles % kBigCUs;
+  t.parts = t.rem ? kBigCUs / t.rem : 1;
+  if (t.parts > 4) t.parts = 4;
+  // a part keeps at least 8 step pairs; a tail that fills most of a round
+  // is left whole
+  while (t.parts > 1 && nkt / t.parts < 16) --t.parts;
+  if (t.rem == 0 || t.parts < 2) {
+    t.rem = 0;
+    t.parts = 1;
+  }
+  t.full = tiles - t.rem;
+  t.per = ((nkt + t.parts - 1) / t.parts + 1) & ~1;
+  t.bytes = (size_t)t.rem * t.parts * BIG_TILE_ELEMS * 4u;
+  return t;
+}
+
+// One thread per 4 consecutive lanes of a register-order row: 16-byte
+// loads of each part, 4 consecutive output columns of one output row.
+__global__ __launch_bounds__(256) void gemm_tail_reduce_kernel(const float *__restrict__ tail, int parts,
+                                                               int full, int m_tiles, int M, int N,
+                                                               const int *__restrict__ rexp,
+                                                               uint16_t *__restrict__ y, int out_fp16) {
+  const int t = (int)blockIdx.y;                                // tail tile index
+  const int q = 4 * ((int)blockIdx.x * 256 + (int)threadIdx.x);  // first element, register order
+  if (q >= BIG_TILE_ELEMS) return;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < parts; ++p) {
+    const float4 u = *reinterpret_cast<const float4 *>(tail + ((size_t)t * parts + p) * BIG_TILE_ELEMS + q);
+    v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+  }
+  const int lane = q & 63, e = (q >> 6) & 15, nb = (q >> 10) & 1, mb = (q >> 11) & (BIG_MB - 1);
+  const int wave = q >> 14;
+  const int tile = full + t;
+  const int m = (tile % m_tiles) * BIG_TM + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  const int n = (tile / m_tiles) * BIG_TN + wave * 64 + 32 * nb + (lane & 31);
+  if (m >= M) return;
+  const int ex = rexp[m];
+  const float r[4] = {v.x, v.y, v.z, v.w};
+  uint16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float w = ldexpf(r[i], ex);
+    o[i] = out_fp16 ? f32_to_f16_bits(w) : f32_to_bf16_rne(w);
+  }
+  uint16_t *dst = y + (int64_t)m * N + n;
+  if (n + 3 < N && ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0)) {
+    *reinterpret_cast<uint2 *>(dst) = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                  (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (n + i < N) dst[i] = o[i];
+  }
+}
+
 __global__ __launch_bounds__(64 * BIG_NW, 1) void gemm_big_kernel(
     LayoutDev L, int M, int Kp, uint32_t xa_bytes, int m_tiles, const uint16_t *__restrict__ xa,
     const int *__restrict__ rexp, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    uint16_t *__restrict__ y, int out_fp16) {
+    uint16_t *__restrict__ y, int out_fp16, int tail_full, int tail_parts, int tail_per,
+    float *__restrict__ tail) {
   __shared__ __attribute__((aligned(16))) uint4 As0[BIG_TILE_BYTES / 16];
   __shared__ __attribute__((aligned(16))) uint4 As1[BIG_TILE_BYTES / 16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -570,13 +657,20 @@ __global__ __launch_bounds__(64 * BIG_NW, 1) void gemm_big_kernel(
   const int h = lane >> 5;
   // tile order: m fastest, so the workgroups on one XCD (every 8th id)
   // share one m tile of x in that XCD's L2
-  const int tile = (int)blockIdx.x;
+  // workgroups past tail_full are parts of the split tail tiles
+  const int id = (int)blockIdx.x;
+  const int nkt = Kp / KT;
+  const bool part = id >= tail_full;
+  const int tile = part ? tail_full + (id - tail_full) / tail_parts : id;
+  const int pidx = part ? (id - tail_full) % tail_parts : 0;
   const int m_tile = tile % m_tiles;
   const int n_tile = tile / m_tiles;
   BigArgs g;
   g.K = L.K; g.Kp = Kp; g.N = L.N; g.M = M;
   g.m0 = m_tile * BIG_TM;
-  g.nkt = Kp / KT;
+  g.kt0 = part ? pidx * tail_per : 0;
+  g.kt1 = part ? min(g.kt0 + tail_per, nkt) : nkt;
+  g.tail = part ? tail + (size_t)(id - tail_full) * BIG_TILE_ELEMS : nullptr;
   g.rexp = rexp; g.y = y; g.out_fp16 = out_fp16;
   const int ncol0 = n_tile * BIG_TN + wave * 64;
   const bool wave_active = ncol0 < L.N;
@@ -673,7 +767,8 @@ namespace {
 
 // Workspace layout: fp16 activations [Mp][Kp] (zero padded to whole
 // 256-row tiles and pairs of 128-k steps), row exponents [M], split-K
-// partials [S][M][N].
+// partials [S][M][N] (tiled kernel) or the fp32 parts of the split tail
+// tiles (256 x 256 kernel).
 struct Workspace {
   int Mp, Kp;
   size_t a_bytes, e_bytes, p_bytes;
@@ -702,6 +797,9 @@ inline Workspace workspace_of(const LayoutDev &L, int M) {
   if (!use_big(L, M, w)) {
     const int sp = choose_splits(L, M, gemm_mb(M));
     if (sp > 1) w.p_bytes = (size_t)sp * (size_t)M * (size_t)L.N * 4u;
+  } else {
+    const int tiles = (w.Mp / BIG_TM) * ((L.N + BIG_TN - 1) / BIG_TN);
+    w.p_bytes = tail_plan(tiles, w.Kp / KT).bytes;
   }
   return w;
 }
@@ -734,9 +832,16 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
   if (use_big(L, M, w)) {
     const int m_tiles = w.Mp / BIG_TM;
     const int n_tiles = (L.N + BIG_TN - 1) / BIG_TN;
-    hipLaunchKernelGGL(gemm_big_kernel, dim3(m_tiles * n_tiles), dim3(64 * BIG_NW), 0, s, L, M, w.Kp,
-                       (uint32_t)w.a_bytes, m_tiles, xa, rexp, reinterpret_cast<const uint8_t *>(codes),
-                       scales, zeros, reinterpret_cast<uint16_t *>(y), out_fp16);
+    const TailPlan t = tail_plan(m_tiles * n_tiles, w.Kp / KT);
+    uint16_t *yp = reinterpret_cast<uint16_t *>(y);
+    hipLaunchKernelGGL(gemm_big_kernel, dim3(t.full + t.rem * t.parts), dim3(64 * BIG_NW), 0, s, L, M,
+                       w.Kp, (uint32_t)w.a_bytes, m_tiles, xa, rexp,
+                       reinterpret_cast<const uint8_t *>(codes), scales, zeros, yp, out_fp16, t.full,
+                       t.parts, t.per, part);
+    err = hipGetLastError();
+    if (err != hipSuccess || t.rem == 0) return err;
+    hipLaunchKernelGGL(gemm_tail_reduce_kernel, dim3(BIG_TILE_ELEMS / 1024, t.rem), dim3(256), 0, s, part,
+                       t.parts, t.full, m_tiles, M, L.N, rexp, yp, out_fp16);
     return hipGetLastError();
   }
   const int mb = gemm_mb(M);

@@ -165,3 +165,24 @@ def test_channel_mix_prefill(j):
     torch.cuda.synchronize()
     ms = sorted(set(rng.choice(2048, 24, replace=False).tolist()) | {0, 2047})
     check_linear_sample(y, x, W, 128, bits, rows, ms)
+
+
+@pytest.mark.parametrize("K,bits", [(4096, [4]), (8192, [4, 2] * 33)])
+def test_gemm_tail_split(K, bits):
+    """M = 2048, N = 8448: 264 tiles of 256 x 256, so the last 8 tiles (the
+    columns 8192..8447) are cut along K (2 parts at K = 4096, 4 at 8192)
+    and summed by the tail reduction."""
+    M, N = 2048, 8448
+    block_n = N if len(bits) == 1 else 128
+    W = S.decode_weight(7, N=N, K=K)
+    _say("gemm tail split", M, N, K, len(bits), "blocks")
+    p = gq.quantize_pack(torch.from_numpy(W).cuda(), bits, block_n)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(70 + K)
+    rows = sorted(set(rng.choice(8192, 12, replace=False).tolist())
+                  | set((8192 + rng.choice(256, 20, replace=False)).tolist()) | {0, N - 1})
+    x = S.activations(M, K, 71)
+    y = gq.linear(bf16_dev(x), p)
+    torch.cuda.synchronize()
+    ms = sorted(set(rng.choice(M, 24, replace=False).tolist()) | {0, M - 1})
+    check_linear_sample(y, x, W, block_n, bits, rows, ms)
