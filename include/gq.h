@@ -139,10 +139,10 @@ gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype
  *   4 < M <= 32  MFMA on the activations as given (bf16 or fp16), the
  *                codes as exact B + q values and the zero point as the exact
  *                constant -(B + z), accumulated per group in fp32; each
- *                group's scale is applied in fp32 after its MFMAs.  K ranges
- *                longer than one workgroup holds are split across
- *                workgroups (fp32 partials in the workspace, summed in split
- *                order).
+ *                group's scale is applied in fp32 after its MFMAs.  Long K ranges,
+ *                and small layers that would leave CUs idle, are split
+ *                across workgroups (fp32 partials in the workspace, summed in
+ *                split order).
  *   M > 32       MFMA GEMM that rounds each dequantized weight once to fp16
  *                (the FP16 matmul of the survey review); activations are
  *                rescaled per row by a power of two so that their fp16 form

@@ -23,20 +23,23 @@
 //        lane groups (gfx950 lane swaps) hands every lane its chunks.
 // B fragments hold code pairs in k order, so x is used exactly as stored.
 //
-// Work split.  A workgroup of 4 waves is CW channel groups (16 channels each,
-// one wave) times KW k-ways (CW * KW = 4).  Wide layers use KW = 1 (64
-// channels share every staged x tile); narrow ones use KW = 2 or 4, the
-// k-ways' partial sums meeting in LDS at the end, so enough workgroups exist
-// without a second pass over the output.  A workgroup first requests its
-// whole x range as buffer loads that write LDS directly (row-major,
-// XOR-swizzled so the MFMA operand reads are conflict-free; lanes past M, K
-// or the range read zeros) and its scales and zero points as 16-byte runs
-// into LDS; each wave keeps its code loads a fixed window ahead of the step
-// it computes, so codes return in step order and the multiplications
-// overlap the transfer.  One barrier per workgroup.  A layer whose k range does
-// not fit one workgroup splits K across workgroups; their fp32 partials are
-// summed in split order by the split-K reduction.  Every result is summed in
-// a fixed order: the kernel is deterministic.
+// Work split.  A workgroup of 8 waves (two per SIMD) is CW channel groups
+// (16 channels each, one wave) times KW k-ways (CW * KW = 8); the k-ways'
+// partial sums meet in LDS at the end.  The launch shape (k-ways, steps per
+// k-way, K splits) comes from a time model of the layer.  x reaches LDS by
+// buffer loads that write LDS directly (row-major, XOR-swizzled so the MFMA
+// operand reads are conflict-free; lanes past M, K or the range read zeros),
+// in chunks of 4 steps held in a ring of two buffers, one barrier per chunk:
+// the first steps compute while later chunks are still on their way.  The
+// scales and zero points come as 16-byte runs into LDS before the first
+// barrier.  Each wave streams its codes straight to registers in step order,
+// starting with a short window (a long burst from every wave of the chip
+// queues the x and scale loads the first barrier waits for behind it) that
+// grows by two loads a step, so codes return in step order and the
+// multiplications overlap the transfer.  A layer whose k range does not fit
+// one workgroup splits K across workgroups; their fp32 partials are summed
+// in split order by the split-K reduction.  Every result is summed in a
+// fixed order: the kernel is deterministic.
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -52,9 +55,13 @@ constexpr int SK_WAVES = 8;                     // two per SIMD
 constexpr int SK_THREADS = 64 * SK_WAVES;
 constexpr int SK_PAIRS = 16 * SK_WAVES;         // (channel, k-way) pairs per workgroup
 constexpr int SK_STEP = 128;                    // k per step
-constexpr int SK_XCAP = 32;                     // x blocks (step x k-way x 16 rows) per workgroup
+constexpr int SK_XCAP = 32;                     // x blocks (step x k-way x 16 rows) in LDS
 constexpr int SK_SWMAX = 16;                    // steps per wave (code registers)
+constexpr int SK_XSC = 4;                       // steps per x chunk
 constexpr int SK_CWIN = 12;                     // code loads in flight per lane
+constexpr int SK_CW0 = 2;                       // code loads issued before the first barrier
+constexpr int SK_CW1 = 4;                       // ... and right after it
+constexpr int SK_CRAMP = 2;                     // code loads per step until the window is full
 constexpr int SK_XBLK = 256;                    // 16-byte LDS slots per 16-row x block of a step
 constexpr uint32_t SK_OOB = 0x80000000u;        // beyond every buffer resource
 
@@ -114,13 +121,18 @@ template <int MB, int KW, int SWC, int BITS>
 struct SkGeo {
   static constexpr int CW = SK_WAVES / KW;            // channel groups
   static constexpr int NC = 16 * CW;                  // channels per workgroup
-  static constexpr int NB = KW * SWC * MB;            // x blocks in LDS
+  static constexpr int SC = SWC < SK_XSC ? SWC : SK_XSC;   // steps per x chunk
+  static constexpr int XCH = SWC / SC;                // x chunks
+  static constexpr int NXB = XCH > 1 ? 2 : 1;         // chunk buffers in LDS (a ring)
+  static constexpr int XS = KW * SC * MB * SK_XBLK;   // 16-byte slots per chunk buffer
   static constexpr int GPS = BITS == 4 ? 1 : 2;       // groups per step
   static constexpr int R = SWC * GPS;                 // groups per (channel, k-way)
   static constexpr int PS = (2 * R + 14 + 15) / 16;   // 16-byte scale pieces per (channel, k-way)
   static constexpr int PZ = (R + 15 + 15) / 16;       // 16-byte zero pieces
   static constexpr int NCL = BITS == 4 ? SWC : SWC / 2;   // 16-byte code loads per lane
-  static_assert(NC * KW == SK_PAIRS && NB <= SK_XCAP && SWC <= SK_SWMAX && SWC % 4 == 0, "geometry");
+  static_assert(NC * KW == SK_PAIRS && NXB * KW * SC * MB <= SK_XCAP && SWC <= SK_SWMAX &&
+                    SWC % 4 == 0 && SWC % SC == 0 && (KW * SC) % 2 == 0,
+                "geometry");
 };
 
 struct SkArgs {
@@ -138,10 +150,11 @@ struct SkArgs {
 
 template <int ACT, int MB, int KW, int SWC, int BITS>
 __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, Rsrc sr, Rsrc zr,
-                                            uint32_t RB, uint32_t GPR, uint4 *xb, uint4 *ss,
+                                            uint32_t RB, uint32_t GPR, uint4 *xb0, uint4 *xb1, uint4 *ss,
                                             uint4 *zz) {
   using Gm = SkGeo<MB, KW, SWC, BITS>;
   constexpr int CW = Gm::CW, GPS = Gm::GPS, NCL = Gm::NCL, PS = Gm::PS, PZ = Gm::PZ;
+  constexpr int SC = Gm::SC, XCH = Gm::XCH;
   constexpr uint32_t BIAS = ACT == 0 ? 0x43004300u : 0x64006400u;   // 128.0 / 1024.0 pairs
   constexpr uint32_t STEPB = SK_STEP * BITS / 8;     // code bytes per channel per step
   const int tid = threadIdx.x;
@@ -155,35 +168,41 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   auto kend = [&](int k) { return min(a.s0 + (k + 1) * a.sw, a.s1); };
   const int kb = kbeg(kw), ke = kend(kw);
 
-  // ---- x: block b = (k-way * SWC + step) * MB + mb holds 16 rows x 128 k;
-  // wave w loads rows 4q .. 4q + 3 (q = w % 4) of every other block (1 KB
-  // per load); lane l takes row rr = 4q + l/16 of the block and fills slot
-  // 16 rr + l%16 with chunk (l%16) ^ rr of that row.  Rows past M are not
-  // loaded (their MFMA output rows are discarded).
-  {
+  // ---- x, in chunks of SC steps held in a ring of two LDS buffers: chunk c
+  // sits in buffer c % 2, its block (k-way * SC + sl) * MB + mb holding 16
+  // rows x 128 k of step c * SC + sl.  Wave w loads rows 4q .. 4q + 3
+  // (q = w % 4) of every other block (1 KB per load); lane l takes row
+  // rr = 4q + l/16 and fills slot 16 rr + l%16 with chunk (l%16) ^ rr of that
+  // row.  Rows past M are not loaded (their MFMA output rows are discarded).
+  // Chunk c + 1 is requested once every wave has passed the barrier that
+  // ends chunk c - 1, the last reader of its buffer.
+  auto xbuf = [&](int c) { return (c & 1) ? xb1 : xb0; };
+  auto x_dma = [&](int c) {
     constexpr int BS = SK_WAVES / 4;                  // waves per row quarter
     const int qq = wave & 3, bset = wave >> 2;
     const int rr = 4 * qq + (lane >> 4);
-    const int c = (lane & 15) ^ rr;
+    const int cc = (lane & 15) ^ rr;
+    uint4 *dst = xbuf(c);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int row = 16 * mb + rr;
       if (16 * mb + 4 * qq < a.M) {                   // uniform
-        const uint32_t rowoff = row < a.M ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)(8 * c)) * 2u
+        const uint32_t rowoff = row < a.M ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)(8 * cc)) * 2u
                                           : SK_OOB;
 #pragma unroll
-        for (int tt = 0; tt < KW * SWC / BS; ++tt) {
+        for (int tt = 0; tt < KW * SC / BS; ++tt) {
           const int t = tt * BS + bset;
-          const int kwb = t / SWC, st = t % SWC;
-          const int gs = kbeg(kwb) + st;
-          const bool ok = rowoff != SK_OOB && gs < kend(kwb) && gs * SK_STEP + 8 * c < a.K;
+          const int kwb = t / SC, sl = t % SC;
+          const int gs = kbeg(kwb) + c * SC + sl;
+          const bool ok = rowoff != SK_OOB && gs < kend(kwb) && gs * SK_STEP + 8 * cc < a.K;
           const uint32_t off = ok ? rowoff + (uint32_t)gs * (SK_STEP * 2) : SK_OOB;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              xr, (lds_void *)(xb + (t * MB + mb) * SK_XBLK + 64 * qq), 16, off, 0, 0, 0);
+              xr, (lds_void *)(dst + (t * MB + mb) * SK_XBLK + 64 * qq), 16, off, 0, 0, 0);
         }
       }
     }
-  }
+  };
+  x_dma(0);
 
   // ---- scales and zero points: for each (channel, k-way) pair the runs of
   // its groups, read as 16-byte pieces from the 16-byte boundary at or below
@@ -210,9 +229,21 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   // ---- codes of the lane's channel and k-way, straight to registers.
   // INT4: one 16-byte load per step (chunks 4g .. 4g + 3); INT2: one per
   // two steps (lane group g gets bytes 16g .. 16g + 15 of the pair's 64).
-  // Code loads are issued CWIN loads ahead of their use, so they return in
-  // step order and each step computes as soon as its codes are in.
+  // Code loads are issued in step order, so they return in step order and
+  // each step computes as soon as its codes are in.  Only CW0 are requested
+  // before the first barrier: a larger burst from every wave of the chip
+  // would queue the x and scale loads the barrier waits for behind it.
+  // From there the window grows by CRAMP loads per step up to CWIN.
   constexpr int CWIN = NCL < SK_CWIN ? NCL : SK_CWIN;
+  constexpr int CW0 = NCL < SK_CW0 ? NCL : SK_CW0;
+  constexpr int CW1 = NCL < SK_CW1 ? NCL : SK_CW1;
+  // code loads issued before step st computes
+  auto ctarget = [&](int st) {
+    int t = CW1 + SK_CRAMP * st;
+    const int u = (BITS == 4 ? st : st / 2) + CWIN;
+    t = t < u ? t : u;
+    return t < NCL ? t : NCL;
+  };
   uint32_t cw[NCL][4];
   const uint32_t crow = ch_ok ? (uint32_t)(a.rw0 + cl) * RB : SK_OOB;
   auto load_codes = [&](int s) {
@@ -223,8 +254,10 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
     const uint4 v = ld128(cr, off);
     cw[s][0] = v.x; cw[s][1] = v.y; cw[s][2] = v.z; cw[s][3] = v.w;
   };
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int s = 0; s < CWIN; ++s) load_codes(s);
+  for (int s = 0; s < CW0; ++s) load_codes(s);
+  __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
   for (int j = 0; j < SPS; ++j)
@@ -233,6 +266,9 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   for (int j = 0; j < SPZ; ++j)
     if (tid + SK_THREADS * j < SK_PAIRS * PZ) zz[tid + SK_THREADS * j] = zpv[j];
   lds_barrier();
+  if constexpr (XCH > 1) x_dma(1);
+#pragma unroll
+  for (int s = CW0; s < CW1; ++s) load_codes(s);
 
   floatx4 yacc[MB];
 #pragma unroll
@@ -263,7 +299,8 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
     for (int i = 0; i < 4; ++i) {
       const int slot = 16 * r + (sk_chunk<BITS>(g, i) ^ r);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) A[i][mb] = xb[((kw * SWC + st) * MB + mb) * SK_XBLK + slot];
+      for (int mb = 0; mb < MB; ++mb)
+        A[i][mb] = xbuf(st / SC)[((kw * SC + st % SC) * MB + mb) * SK_XBLK + slot];
     }
 #pragma unroll
     for (int h = 0; h < GPS; ++h) {
@@ -294,12 +331,16 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   for (int st = 0; st < SWC; ++st) {
     const int cur = st & 1;
     __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < SWC && (st + 1) % SC == 0) {
+      // the next x chunk is in (every wave's DMA of it is complete), and the
+      // buffer of the one just finished is free for the chunk after
+      lds_barrier();
+      if ((st + 1) / SC + 1 < XCH) x_dma((st + 1) / SC + 1);
+    }
     if (st + 1 < SWC) read_step(st + 1, av[cur ^ 1], sc[(st + 1) % 3], zp[cur ^ 1]);
-    // the load CWIN ahead of this step's
-    if constexpr (BITS == 4) {
-      if (st + CWIN < NCL) load_codes(st + CWIN);
-    } else {
-      if ((st & 1) == 0 && (st >> 1) + CWIN < NCL) load_codes((st >> 1) + CWIN);
+#pragma unroll
+    for (int s = ctarget(st); s < ctarget(st + 1); ++s) load_codes(s);
+    if constexpr (BITS == 2) {
       if ((st & 1) == 0) transpose4(cw[st >> 1]);
     }
 #pragma unroll
@@ -329,7 +370,7 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   // ---- k-ways meet in LDS (the x tiles' space, free once every wave is
   // done with it), summed in k-way order
   if constexpr (KW > 1) {
-    float *red = reinterpret_cast<float *>(xb);
+    float *red = reinterpret_cast<float *>(xb0);
     lds_barrier();
     if (kw > 0) {
 #pragma unroll
@@ -383,10 +424,11 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     uint16_t *__restrict__ y, float *__restrict__ part, int sps, int sw) {
   using G2 = SkGeo<MB, KW, SWC, BITSEL == 4 ? 4 : 2>;   // the larger scale runs
-  __shared__ __attribute__((aligned(16))) uint4 xb[G2::NB * SK_XBLK];
+  __shared__ __attribute__((aligned(16))) uint4 xb0[G2::XS];
+  __shared__ __attribute__((aligned(16))) uint4 xb1[G2::NXB > 1 ? G2::XS : 1];
   __shared__ __attribute__((aligned(16))) uint4 ss[SK_PAIRS * G2::PS];
   __shared__ __attribute__((aligned(16))) uint4 zz[SK_PAIRS * G2::PZ];
-  static_assert((KW - 1) * (SK_WAVES / KW) * MB * 4 * 64 <= G2::NB * SK_XBLK * 4, "reduction space");
+  static_assert((KW - 1) * (SK_WAVES / KW) * MB * 4 * 64 <= G2::XS * 4, "reduction space");
   constexpr int NC = 16 * (SK_WAVES / KW);
   const int nsteps = (L.K + SK_STEP - 1) / SK_STEP;
   SkArgs a;
@@ -417,9 +459,9 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(
   const Rsrc sr = make_rsrc(scales, 2u * gend);
   const Rsrc zr = make_rsrc(zeros, gend);
   if (BITSEL != 2 && bits == 4)
-    skinny_tile<ACT, MB, KW, SWC, 4>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz);
+    skinny_tile<ACT, MB, KW, SWC, 4>(a, xr, cr, sr, zr, RB, GPR, xb0, xb1, ss, zz);
   else if constexpr (BITSEL != 4)
-    skinny_tile<ACT, MB, KW, SWC, 2>(a, xr, cr, sr, zr, RB, GPR, xb, ss, zz);
+    skinny_tile<ACT, MB, KW, SWC, 2>(a, xr, cr, sr, zr, RB, GPR, xb0, xb1, ss, zz);
 }
 
 struct SkPlan {
@@ -436,21 +478,40 @@ struct SkPlan {
 // [nsplit][M][N] when K is split.
 constexpr int kCUs = 256;
 
+// x blocks resident in LDS: one chunk buffer, or a ring of two
+__host__ __device__ constexpr int skinny_x_blocks(int mb, int kw, int swc) {
+  return (swc > SK_XSC ? 2 : 1) * kw * (swc < SK_XSC ? swc : SK_XSC) * mb;
+}
+
 inline size_t skinny_lds_bytes(int mb, int kw, int swc) {
   const int r = swc * 2;                              // sized for INT2 runs
-  return (size_t)kw * swc * mb * SK_XBLK * 16 +
+  return (size_t)skinny_x_blocks(mb, kw, swc) * SK_XBLK * 16 +
          (size_t)SK_PAIRS * 16 * ((2 * r + 29) / 16 + (r + 30) / 16);
 }
 
+// Launch shape from a time model (us), fitted on MI355X to per-wave
+// timestamps of this kernel and to forced launch shapes on the Llama-3-8B
+// layers: a workgroup step takes ~0.27 us with one 16-row block and ~0.65 us
+// with two; the weights, and at half weight the x tiles every workgroup
+// reads from L2 (M x its K range), stream at ~5 TB/s over the CUs that have
+// work; a round of workgroups past the first costs ~3 us, a K split the
+// reduction launch (~2 us) and ~0.5 us per split.
 inline SkPlan skinny_plan(const LayoutDev &L, int M) {
   SkPlan best{};
-  int best_cost = 0x7fffffff;
+  double best_cost = 1e30;
   const int mb = M <= 16 ? 1 : 2;
   const int nsteps = (L.K + SK_STEP - 1) / SK_STEP;
+  double wbytes = 0.0;                                // packed codes, scales and zeros
+  for (int i = 0; i < L.nblocks; ++i) {
+    const bool b4 = (L.int4_mask[i >> 5] >> (i & 31)) & 1u;
+    wbytes += (double)L.block_n * L.K * (b4 ? 0.5 + 3.0 / 128 : 0.25 + 3.0 / 64);
+  }
   for (int kw = 2; kw <= 8 / mb; kw *= 2) {
     const int nc = 16 * (SK_WAVES / kw);
     const int tiles = (L.N + nc - 1) / nc;
-    const int cap = min(SK_SWMAX, SK_XCAP / (kw * mb));
+    int cap = 0;                                       // most steps per k-way
+    for (int c = 4; c <= SK_SWMAX; c *= 2)
+      if (skinny_x_blocks(mb, kw, c) <= SK_XCAP) cap = c;
     if (cap < 4) continue;
     for (int ns = 1; ns <= nsteps; ++ns) {
       const int sps = (nsteps + ns - 1) / ns;
@@ -462,7 +523,11 @@ inline SkPlan skinny_plan(const LayoutDev &L, int M) {
       const int per_cu = max(1, min(2, (int)((160u * 1024u) / skinny_lds_bytes(mb, kw, swc))));
       const int wgs = tiles * nsplit;
       const int rounds = (wgs + kCUs * per_cu - 1) / (kCUs * per_cu);
-      const int cost = 10 * ((wgs + kCUs - 1) / kCUs * sw + 8 * rounds + (nsplit > 1 ? 16 : 0)) + kw;
+      const double xbytes = (double)tiles * M * L.K * 2.0;
+      const double t_bw = (wbytes + 0.5 * xbytes) / (5.0e6 * (wgs < kCUs ? wgs : kCUs) / kCUs);
+      const double t_comp = (double)((wgs + kCUs - 1) / kCUs) * sw * (mb == 1 ? 0.27 : 0.65);
+      const double t_split = nsplit > 1 ? 2.0 + 0.5 * nsplit : 0.0;
+      const double cost = (t_bw > t_comp ? t_bw : t_comp) + 3.0 * (rounds - 1) + t_split;
       if (cost < best_cost) {
         best_cost = cost;
         best.mb = mb; best.kw = kw; best.swc = swc; best.tiles = tiles;
@@ -510,15 +575,18 @@ template <int ACT, int MB, int KW>
 hipError_t launch_kw(const LayoutDev &L, int M, const SkPlan &p, const void *x,
                      const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *y,
                      void *workspace, hipStream_t s) {
-  constexpr int CAP = SK_XCAP / (KW * MB);
-  if (p.swc == 4 || CAP < 8)
+  constexpr bool ok8 = skinny_x_blocks(MB, KW, 8) <= SK_XCAP;
+  constexpr bool ok16 = skinny_x_blocks(MB, KW, 16) <= SK_XCAP;
+  if (p.swc == 4)
     return launch_cfg<ACT, MB, KW, 4>(L, M, p, x, codes, scales, zeros, y, workspace, s);
-  if constexpr (CAP >= 8) {
-    if (p.swc == 8 || CAP < 16)
+  if constexpr (ok8) {
+    if (p.swc == 8)
       return launch_cfg<ACT, MB, KW, 8>(L, M, p, x, codes, scales, zeros, y, workspace, s);
   }
-  if constexpr (CAP >= 16)
-    return launch_cfg<ACT, MB, KW, 16>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  if constexpr (ok16) {
+    if (p.swc == 16)
+      return launch_cfg<ACT, MB, KW, 16>(L, M, p, x, codes, scales, zeros, y, workspace, s);
+  }
   return hipErrorInvalidValue;
 }
 
