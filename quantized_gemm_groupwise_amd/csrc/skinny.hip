@@ -293,7 +293,10 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   uint4 av[2][4][MB];
   float sc[3][GPS];
   uint32_t zp[2][GPS];
-  floatx4 gacc[2][GPS][MB];
+  // partial accumulators per (group, row block): with one row block the
+  // chunks alternate between two, so no MFMA waits for the one just issued
+  constexpr int NP = MB == 1 ? 2 : 1;
+  floatx4 gacc[2][GPS][MB][NP];
   auto read_step = [&](int st, uint4 (&A)[4][MB], float (&S)[GPS], uint32_t (&Z)[GPS]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -314,13 +317,15 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
       Z[h] = NEGB | z | (z << 16);
     }
   };
-  auto scale_step = [&](const floatx4 (&ga)[GPS][MB], const float (&S)[GPS]) {
+  auto scale_step = [&](const floatx4 (&ga)[GPS][MB][NP], const float (&S)[GPS]) {
 #pragma unroll
     for (int h = 0; h < GPS; ++h)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) yacc[mb][e] = fmaf(S[h], ga[h][mb][e], yacc[mb][e]);
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yacc[mb][e] = fmaf(S[h], ga[h][mb][p][e], yacc[mb][e]);
     // keep the scaling here: otherwise it is all moved after the last step
     // and every step's MFMA results stay live
 #pragma unroll
@@ -343,6 +348,7 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
     if constexpr (BITS == 2) {
       if ((st & 1) == 0) transpose4(cw[st >> 1]);
     }
+    uint4 bq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t w;
@@ -352,14 +358,29 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
         const uint32_t t = cw[st >> 1][2 * (st & 1) + (i >> 1)];
         w = (i & 1) ? (t >> 16) : (t & 0xffffu);
       }
-      const uint4 b = unpack_chunk<BITS>(w, BIAS);
-      const int h = BITS == 4 ? 0 : (i >> 1);
-      const bool first = BITS == 4 ? i == 0 : (i & 1) == 0;   // first MFMA of a group
-      const uint4 zb = make_uint4(zp[cur][h], zp[cur][h], zp[cur][h], zp[cur][h]);
+      bq[i] = unpack_chunk<BITS>(w, BIAS);
+    }
+    // chunks in pairs: the data MFMAs of both, then their zero-point MFMAs,
+    // so every MFMA's accumulator was last written two MFMAs earlier
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        gacc[cur][h][mb] = mfma16<ACT>(av[cur][i][mb], b, first ? zero4 : gacc[cur][h][mb]);
-        gacc[cur][h][mb] = mfma16<ACT>(av[cur][i][mb], zb, gacc[cur][h][mb]);
+    for (int ip = 0; ip < 4; ip += 2) {
+#pragma unroll
+      for (int i = ip; i < ip + 2; ++i) {
+        const int h = BITS == 4 ? 0 : (i >> 1);
+        const int p = NP == 2 ? (i & 1) : 0;
+        const bool first = (BITS == 4 ? i : (i & 1)) < NP;   // first MFMA of its accumulator
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          gacc[cur][h][mb][p] = mfma16<ACT>(av[cur][i][mb], bq[i], first ? zero4 : gacc[cur][h][mb][p]);
+      }
+#pragma unroll
+      for (int i = ip; i < ip + 2; ++i) {
+        const int h = BITS == 4 ? 0 : (i >> 1);
+        const int p = NP == 2 ? (i & 1) : 0;
+        const uint4 zb = make_uint4(zp[cur][h], zp[cur][h], zp[cur][h], zp[cur][h]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          gacc[cur][h][mb][p] = mfma16<ACT>(av[cur][i][mb], zb, gacc[cur][h][mb][p]);
       }
     }
     if (st > 0) scale_step(gacc[cur ^ 1], sc[(st - 1) % 3]);
