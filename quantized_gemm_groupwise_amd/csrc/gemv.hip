@@ -44,7 +44,7 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kLanes = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kLanes * kWaves;
-constexpr int kStageSub = 4;               // x sub-units staged per thread per chunk
+constexpr int kStageSubMax = 4;            // x sub-units staged per thread per chunk, at most
 constexpr int kLdsBytes = 65536;
 
 template <int ACT>
@@ -185,22 +185,24 @@ struct Geo {
 // sub-units of 16 activations (one INT2 code word, two INT4 code words).
 // Thread t stages sub-units t, t + 256, ...; the SPU sub-units of a unit sit
 // in consecutive lanes, which combine their partial sums with DPP.  The
-// loads of all kStageSub sub-units are issued unconditionally (sub-units
-// past the end read out of range and get zeros), so the wait before the
-// stores counts exactly; stage_x_store skips the arithmetic of sub-units no
-// thread of the workgroup owns.
-template <int BITS>
+// loads of all SS sub-units are issued unconditionally (sub-units past the
+// end read out of range and get zeros), so the wait before the stores counts
+// exactly; stage_x_store skips the arithmetic of sub-units no thread of the
+// workgroup owns.  SS is chosen at launch as the fewest sub-units (1, 2 or
+// 4) that stage a whole row: every register held for staging is one less
+// wave per SIMD.
+template <int SS>
 struct StageRegs {
-  uint32_t raw[kStageSub][8];
+  uint32_t raw[SS][8];
 };
 
-template <int BITS, int M>
-__device__ __forceinline__ void stage_x_load(StageRegs<BITS> &st, Rsrc xr, uint32_t xbytes, int K,
+template <int BITS, int M, int SS>
+__device__ __forceinline__ void stage_x_load(StageRegs<SS> &st, Rsrc xr, uint32_t xbytes, int K,
                                              int k0, int nslice) {
   using Gm = Geo<BITS>;
   const int subs = M * nslice * kLanes * Gm::SPU;
 #pragma unroll
-  for (int j = 0; j < kStageSub; ++j) {
+  for (int j = 0; j < SS; ++j) {
     const int su = (int)threadIdx.x + j * kThreads;
     const int unit = su / Gm::SPU, part = su % Gm::SPU;
     const int lane = unit & (kLanes - 1);
@@ -215,15 +217,15 @@ __device__ __forceinline__ void stage_x_load(StageRegs<BITS> &st, Rsrc xr, uint3
   }
 }
 
-template <int BITS, int ACT, int M>
-__device__ __forceinline__ void stage_x_store(const StageRegs<BITS> &st, int nslice, uint4 *pairs,
+template <int BITS, int ACT, int M, int SS>
+__device__ __forceinline__ void stage_x_store(const StageRegs<SS> &st, int nslice, uint4 *pairs,
                                               float *sums) {
   using Gm = Geo<BITS>;
   constexpr uint32_t ONES = ACT == 0 ? 0x3f803f80u : 0x3c003c00u;
   constexpr float BIASF = ACT == 0 ? 128.f : 1024.f;
   const int subs = M * nslice * kLanes * Gm::SPU;
 #pragma unroll
-  for (int j = 0; j < kStageSub; ++j) {
+  for (int j = 0; j < SS; ++j) {
     if (j * kThreads >= subs) break;            // uniform: nothing left to stage
     const int su = (int)threadIdx.x + j * kThreads;
     const int unit = su / Gm::SPU, part = su % Gm::SPU;
@@ -421,23 +423,23 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
 }
 
 // Slices per staged chunk for a bit-width and M: each thread stages at most
-// kStageSub sub-units and the chunk fits kLdsBytes.
-__host__ __device__ constexpr int chunk_slices(int bits, int M) {
+// ss sub-units and the chunk fits kLdsBytes.
+__host__ __device__ constexpr int chunk_slices(int bits, int M, int ss) {
   const int pw = bits == 4 ? 16 : 32, nsum = bits == 4 ? 1 : 2;
-  const int by_units = kStageSub * kThreads / (M * kLanes * (bits == 4 ? 2 : 4));
+  const int by_units = ss * kThreads / (M * kLanes * (bits == 4 ? 2 : 4));
   const int by_lds = kLdsBytes / (M * kLanes * 4 * (pw + nsum));
   return by_units < by_lds ? by_units : by_lds;
 }
 
-__host__ __device__ constexpr int stage_bytes(int bits, int M, int nslice_row) {
+__host__ __device__ constexpr int stage_bytes(int bits, int M, int nslice_row, int ss) {
   const int pw = bits == 4 ? 16 : 32, nsum = bits == 4 ? 1 : 2;
-  const int ch = chunk_slices(bits, M);
+  const int ch = chunk_slices(bits, M, ss);
   const int c = nslice_row < ch ? nslice_row : ch;
   return M * c * kLanes * 4 * (pw + nsum);
 }
 
 // One workgroup: stage x chunk by chunk, stream the wave's R rows.
-template <int BITS, int ACT, int M, int R, int NL>
+template <int BITS, int ACT, int M, int R, int NL, int SS>
 __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &bi, int blk,
                                            int n0, bool active, const uint16_t *__restrict__ x,
                                            const uint8_t *__restrict__ codes,
@@ -450,9 +452,9 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
   const int RB = K * BITS / 8;               // bytes per packed row
   const int GPR = K / Gm::G;                 // groups per row
   const int nslice_row = (RB + 1023) >> 10;
-  // slices per staged chunk: every thread stages at most kStageSub sub-units
-  // and the chunk fits the LDS budget
-  constexpr int CHUNK = chunk_slices(BITS, M);
+  // slices per staged chunk: every thread stages at most SS sub-units and
+  // the chunk fits the LDS budget
+  constexpr int CHUNK = chunk_slices(BITS, M, SS);
   static_assert(CHUNK >= 1, "chunk");
   static_assert(CHUNK * M * kLanes * 4 * (Gm::PW + Gm::NSUM) <= kLdsBytes, "lds");
   const int r0 = n0 - blk * L.block_n;
@@ -483,12 +485,12 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
     // whole row in one load group and one staged chunk: straight-line code,
     // so slice i waits only for the loads issued before it
     LoadGroup<BITS, R, NL> g;
-    StageRegs<BITS> st;
-    stage_x_load<BITS, M>(st, xr, xbytes, K, 0, nslice_row);
+    StageRegs<SS> st;
+    stage_x_load<BITS, M, SS>(st, xr, xbytes, K, 0, nslice_row);
     __builtin_amdgcn_sched_barrier(0);
     issue_group<BITS, R, NL, false>(g, 0, nslice_row, lane, rr);
     __builtin_amdgcn_sched_barrier(0);
-    stage_x_store<BITS, ACT, M>(st, nslice_row, pairs, sums);
+    stage_x_store<BITS, ACT, M, SS>(st, nslice_row, pairs, sums);
     lds_barrier();
     compute_group<BITS, ACT, M, R, NL>(g, 0, nslice_row, 0, lane, pairs, sums, nslice_row, acc);
   } else {
@@ -497,12 +499,12 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
       const int cend = c0 + cn;
       if (c0 > 0) lds_barrier();               // previous chunk fully read
       LoadGroup<BITS, R, NL> g;
-      StageRegs<BITS> st;
-      stage_x_load<BITS, M>(st, xr, xbytes, K, c0 * Gm::SK, cn);
+      StageRegs<SS> st;
+      stage_x_load<BITS, M, SS>(st, xr, xbytes, K, c0 * Gm::SK, cn);
       __builtin_amdgcn_sched_barrier(0);
       issue_group<BITS, R, NL, true>(g, c0, cend, lane, rr);
       __builtin_amdgcn_sched_barrier(0);
-      stage_x_store<BITS, ACT, M>(st, cn, pairs, sums);
+      stage_x_store<BITS, ACT, M, SS>(st, cn, pairs, sums);
       lds_barrier();
       for (int s = c0;;) {
         compute_group<BITS, ACT, M, R, NL>(g, s, cend, c0, lane, pairs, sums, cn, acc);
@@ -531,7 +533,7 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
 // BITSEL: 4 or 2 for a uniform (Layer-mix) linear, 0 for a Channel-mix
 // layout where the workgroup reads its block's width from the bit mask (the
 // 4R rows of a workgroup never straddle two blocks).
-template <int ACT, int M, int R, int NL, int BITSEL>
+template <int ACT, int M, int R, int NL, int BITSEL, int SS>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint16_t *__restrict__ x,
                                                         const uint8_t *__restrict__ codes,
                                                         const uint16_t *__restrict__ scales,
@@ -542,23 +544,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint1
   const int nb = (int)blockIdx.x * kWaves * R;
   const int n0 = nb + wave * R;
   const bool active = n0 < L.N;                // inactive waves still stage x
+  // the launch picks SS so that a chunk holds at least one slice of every
+  // bit-width in the layout; other combinations are never launched
+  constexpr bool ok4 = chunk_slices(4, M, SS) >= 1, ok2 = chunk_slices(2, M, SS) >= 1;
   if constexpr (BITSEL == 4) {
     BlockInfo bi = {4, 0, 0};
-    gemv_block<4, ACT, M, R, NL>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
+    if constexpr (ok4)
+      gemv_block<4, ACT, M, R, NL, SS>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
   } else if constexpr (BITSEL == 2) {
     BlockInfo bi = {2, 0, 0};
-    gemv_block<2, ACT, M, R, NL>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
-  } else {
+    if constexpr (ok2)
+      gemv_block<2, ACT, M, R, NL, SS>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
+  } else if constexpr (ok4 && ok2) {
     const int blk = nb / L.block_n;
     const BlockInfo bi = block_info(L, blk);
     if (__builtin_amdgcn_readfirstlane(bi.bits) == 4)
-      gemv_block<4, ACT, M, R, NL>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
+      gemv_block<4, ACT, M, R, NL, SS>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
     else
-      gemv_block<2, ACT, M, R, NL>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
+      gemv_block<2, ACT, M, R, NL, SS>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
   }
 }
 
-template <int ACT, int M, int R, int NL>
+template <int ACT, int M, int R, int NL, int SS>
 hipError_t launch_rows(const LayoutDev &L, int bitsel, const void *x, const uint32_t *codes,
                        const uint16_t *scales, const uint8_t *zeros, void *y, hipStream_t s) {
   const int blocks = (L.N + kWaves * R - 1) / (kWaves * R);
@@ -566,16 +573,27 @@ hipError_t launch_rows(const LayoutDev &L, int bitsel, const void *x, const uint
   const uint8_t *cp = reinterpret_cast<const uint8_t *>(codes);
   uint16_t *yp = reinterpret_cast<uint16_t *>(y);
   const dim3 g(blocks), b(kThreads);
-  const int s4 = stage_bytes(4, M, (L.K * 4 / 8 + 1023) / 1024);
-  const int s2 = stage_bytes(2, M, (L.K * 2 / 8 + 1023) / 1024);
+  const int s4 = stage_bytes(4, M, (L.K * 4 / 8 + 1023) / 1024, SS);
+  const int s2 = stage_bytes(2, M, (L.K * 2 / 8 + 1023) / 1024, SS);
   if (bitsel == 4)
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 4>), g, b, s4, s, L, xp, cp, scales, zeros, yp);
+    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 4, SS>), g, b, s4, s, L, xp, cp, scales, zeros, yp);
   else if (bitsel == 2)
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
+    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2, SS>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
   else
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0>), g, b, s4 > s2 ? s4 : s2, s, L, xp, cp, scales,
-                       zeros, yp);
+    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0, SS>), g, b, s4 > s2 ? s4 : s2, s, L, xp, cp,
+                       scales, zeros, yp);
   return hipGetLastError();
+}
+
+template <int ACT, int M, int SS>
+hipError_t launch_r(const LayoutDev &L, int bitsel, bool two, int ns, const void *x,
+                    const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *y,
+                    hipStream_t s) {
+  if (ns <= 1)
+    return two ? launch_rows<ACT, M, 2, 1, SS>(L, bitsel, x, codes, scales, zeros, y, s)
+               : launch_rows<ACT, M, 1, 1, SS>(L, bitsel, x, codes, scales, zeros, y, s);
+  return two ? launch_rows<ACT, M, 2, 2, SS>(L, bitsel, x, codes, scales, zeros, y, s)
+             : launch_rows<ACT, M, 1, 2, SS>(L, bitsel, x, codes, scales, zeros, y, s);
 }
 
 template <int ACT, int M>
@@ -594,11 +612,14 @@ hipError_t launch_m(const LayoutDev &L, const void *x, const uint32_t *codes,
   // once, or more rows per wave, leaves fewer waves to cover HBM latency.
   const int ns = (L.K * (any4 ? 4 : 2) / 8 + 1023) / 1024;
   const bool two = L.N >= 4096;
-  if (ns <= 1)
-    return two ? launch_rows<ACT, M, 2, 1>(L, bitsel, x, codes, scales, zeros, y, s)
-               : launch_rows<ACT, M, 1, 1>(L, bitsel, x, codes, scales, zeros, y, s);
-  return two ? launch_rows<ACT, M, 2, 2>(L, bitsel, x, codes, scales, zeros, y, s)
-             : launch_rows<ACT, M, 1, 2>(L, bitsel, x, codes, scales, zeros, y, s);
+  // staging sub-units per thread that hold a whole row of x (INT2 slices
+  // carry twice the activations of INT4 ones)
+  const int ns4 = (L.K * 4 / 8 + 1023) / 1024, ns2 = (L.K * 2 / 8 + 1023) / 1024;
+  const int u4 = any4 ? M * kLanes * 2 * ns4 : 0, u2 = all4 ? 0 : M * kLanes * 4 * ns2;
+  const int need = ((u4 > u2 ? u4 : u2) + kThreads - 1) / kThreads;
+  if (need <= 1) return launch_r<ACT, M, 1>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
+  if (need <= 2) return launch_r<ACT, M, 2>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
+  return launch_r<ACT, M, kStageSubMax>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
 }
 
 template <int ACT>
