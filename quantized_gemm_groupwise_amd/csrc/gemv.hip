@@ -10,8 +10,12 @@
 // each wave R of them.  A packed row is cut into 1 KB slices; lane l reads
 // bytes [1024 i + 16 l, +16) of slice i of each of its R rows, i.e. the
 // codes of KPL = 128/b consecutive k.  Code, scale and zero loads for NL
-// slices are issued as one group, and the next group is issued before the
-// current one is computed, so each slice waits only for its own bytes.
+// slices are issued as one group, so each slice waits only for its own
+// bytes.  A row longer than one group is streamed group by group (keeping a
+// second group in flight measured slower on the 14336-long rows: the extra
+// registers cost more than the latency they hide).  Each kernel is compiled
+// for one of the two cases, so the short-row kernels hold only the registers
+// they use: fewer registers, more resident waves.
 //
 // Loads go through buffer resources, one per row for codes, scales and
 // zeros, whose size is the row's own length (0 for rows past N).  A lane
@@ -439,7 +443,9 @@ __host__ __device__ constexpr int stage_bytes(int bits, int M, int nslice_row, i
 }
 
 // One workgroup: stage x chunk by chunk, stream the wave's R rows.
-template <int BITS, int ACT, int M, int R, int NL, int SS>
+// ONE: every row of the layout fits one load group and one staged chunk
+// (chosen at launch, so each kernel holds the registers of one path only).
+template <int BITS, int ACT, int M, int R, int NL, int SS, bool ONE>
 __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &bi, int blk,
                                            int n0, bool active, const uint16_t *__restrict__ x,
                                            const uint8_t *__restrict__ codes,
@@ -481,7 +487,7 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
-  if (nslice_row <= NL && nslice_row <= CHUNK) {
+  if constexpr (ONE) {
     // whole row in one load group and one staged chunk: straight-line code,
     // so slice i waits only for the loads issued before it
     LoadGroup<BITS, R, NL> g;
@@ -533,7 +539,7 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
 // BITSEL: 4 or 2 for a uniform (Layer-mix) linear, 0 for a Channel-mix
 // layout where the workgroup reads its block's width from the bit mask (the
 // 4R rows of a workgroup never straddle two blocks).
-template <int ACT, int M, int R, int NL, int BITSEL, int SS>
+template <int ACT, int M, int R, int NL, int BITSEL, int SS, bool ONE>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint16_t *__restrict__ x,
                                                         const uint8_t *__restrict__ codes,
                                                         const uint16_t *__restrict__ scales,
@@ -550,18 +556,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint1
   if constexpr (BITSEL == 4) {
     BlockInfo bi = {4, 0, 0};
     if constexpr (ok4)
-      gemv_block<4, ACT, M, R, NL, SS>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
+      gemv_block<4, ACT, M, R, NL, SS, ONE>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
   } else if constexpr (BITSEL == 2) {
     BlockInfo bi = {2, 0, 0};
     if constexpr (ok2)
-      gemv_block<2, ACT, M, R, NL, SS>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
+      gemv_block<2, ACT, M, R, NL, SS, ONE>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
   } else if constexpr (ok4 && ok2) {
     const int blk = nb / L.block_n;
     const BlockInfo bi = block_info(L, blk);
     if (__builtin_amdgcn_readfirstlane(bi.bits) == 4)
-      gemv_block<4, ACT, M, R, NL, SS>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
+      gemv_block<4, ACT, M, R, NL, SS, ONE>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
     else
-      gemv_block<2, ACT, M, R, NL, SS>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
+      gemv_block<2, ACT, M, R, NL, SS, ONE>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
   }
 }
 
@@ -573,15 +579,27 @@ hipError_t launch_rows(const LayoutDev &L, int bitsel, const void *x, const uint
   const uint8_t *cp = reinterpret_cast<const uint8_t *>(codes);
   uint16_t *yp = reinterpret_cast<uint16_t *>(y);
   const dim3 g(blocks), b(kThreads);
-  const int s4 = stage_bytes(4, M, (L.K * 4 / 8 + 1023) / 1024, SS);
-  const int s2 = stage_bytes(2, M, (L.K * 2 / 8 + 1023) / 1024, SS);
-  if (bitsel == 4)
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 4, SS>), g, b, s4, s, L, xp, cp, scales, zeros, yp);
-  else if (bitsel == 2)
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2, SS>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
-  else
-    hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0, SS>), g, b, s4 > s2 ? s4 : s2, s, L, xp, cp,
-                       scales, zeros, yp);
+  const int ns4 = (L.K * 4 / 8 + 1023) / 1024, ns2 = (L.K * 2 / 8 + 1023) / 1024;
+  const int s4 = stage_bytes(4, M, ns4, SS), s2 = stage_bytes(2, M, ns2, SS);
+  const bool one4 = ns4 <= NL && ns4 <= chunk_slices(4, M, SS);
+  const bool one2 = ns2 <= NL && ns2 <= chunk_slices(2, M, SS);
+  if (bitsel == 4) {
+    if (one4)
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 4, SS, true>), g, b, s4, s, L, xp, cp, scales, zeros, yp);
+    else
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 4, SS, false>), g, b, s4, s, L, xp, cp, scales, zeros, yp);
+  } else if (bitsel == 2) {
+    if (one2)
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2, SS, true>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
+    else
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2, SS, false>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
+  } else {
+    const int sm = s4 > s2 ? s4 : s2;
+    if (one4 && one2)
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0, SS, true>), g, b, sm, s, L, xp, cp, scales, zeros, yp);
+    else
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0, SS, false>), g, b, sm, s, L, xp, cp, scales, zeros, yp);
+  }
   return hipGetLastError();
 }
 
