@@ -413,15 +413,19 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     dv[q] = (uint32_t)(((lane >> 4) * g.Kp + (((lane & 15) ^ (4 * q + (lane >> 4))) * 8)) * 2);
-  auto dma_a = [&](int kt, uint4 *dst) {
+  // loads p0 .. p0 + np - 1 of the wave's BIG_DMA
+  auto dma_a = [&](int kt, uint4 *dst, int p0, int np) {
 #pragma unroll
-    for (int p = 0; p < BIG_DMA; ++p) {
+    for (int p = p0; p < p0 + np; ++p) {
       const int i = BIG_DMA * wave + p;
       const uint32_t soff = (uint32_t)(((g.m0 + 4 * i) * g.Kp + kt * KT) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(dst + 64 * i), 16, dv[p & 3], soff,
                                                0, 0);
     }
   };
+  // x loads per sub-step, over the first four: the last ones then have
+  // half a step to land before the barrier that waits for them
+  constexpr int DMA_PER_SUB = BIG_DMA / 4;
   // MFMA operand reads: lane (j, h) of 32-row block mb, sub-step t reads row
   // 32 mb + j, chunk 8h + t, i.e. slot chunk ((8h) ^ (j & 8)) | (t ^ (j & 7))
   const uint32_t rb = (uint32_t)(j * 16 + ((8 * h) ^ (j & 8)));   // in 16-byte slots
@@ -462,7 +466,6 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
                   uint32_t *zn) {
     const int kn = kt + 1 < g.kt1 ? kt + 1 : kt;
     __builtin_amdgcn_sched_barrier(0);
-    dma_a(kn, nxt);
     load_b(kn, bn, sn, zn);
     __builtin_amdgcn_sched_barrier(0);
     // the half step past K (INT2 rows with K % 128 == 64) gets scale 0;
@@ -500,6 +503,10 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int c = t & 1, n = c ^ 1;
+      // the next tile's x arrives a few loads per sub-step: issued in one
+      // burst after the barrier, the four waves' loads queued in the
+      // address unit for ~1 us while no MFMA ran
+      if (t < 4) dma_a(kn, nxt, DMA_PER_SUB * t, DMA_PER_SUB);
       if (t + 1 < 8) {
         read_a(t + 1, af[n]);
         make_b(t + 1, bf[n]);
@@ -515,6 +522,7 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
 #pragma unroll
       for (int i = 0; i < 2 * BIG_MB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        if (t < 4 && i < DMA_PER_SUB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // x load
         if (t + 1 < 8) {
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);          // VALU
           if (i < BIG_MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
@@ -528,7 +536,7 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
   };
 
   uint32_t b0[2][BW], b1[2][BW], s0[2], s1[2], z0[2], z1[2];
-  dma_a(g.kt0, As0);
+  dma_a(g.kt0, As0, 0, BIG_DMA);
   load_b(g.kt0, b0, s0, z0);
   lds_barrier();
   // kt1 - kt0 is even: x is zero-padded to a multiple of 256 in k, and steps
