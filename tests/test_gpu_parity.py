@@ -140,6 +140,8 @@ def test_dequant_bit_exact(block_n, bits):
 @pytest.mark.parametrize("N,K,block_n,bits", [
     (512, 512, 512, [4]), (300, 1024, 300, [2]), (1000, 2048, 1000, [4]),
     (512, 1024, 128, [4, 2, 2, 4]), (129, 192, 129, [2]),
+    (640, 8192, 640, [4]),          # rows longer than one load group, 2 staging sub-units at M = 1
+    (256, 6144, 128, [4, 2]),       # the same for a Channel-mix layout, 3-slice INT4 rows
 ])
 def test_linear_gemv(M, N, K, block_n, bits):
     W = S.decode_weight(0, N=N, K=K)
