@@ -295,7 +295,18 @@ def channel_mix(torch, gq, S):
         out[f"quantize_pack_mlp{j}"] = {"N": N, "K": K, "us": round(t / 10 * 1e6, 1),
                                         "GBps": round(qb * 10 / t / 1e9, 1),
                                         "frac_hbm": round(qb * 10 / t / 1e9 / HBM_PEAK_GBS, 3)}
-        del W
+        # fake quantization (quantize -> dequantize, bf16 out): the forward of
+        # a FakeQuantize module; fp32 in, bf16 out
+        wfq = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+        ft = GraphTimer(torch, lambda: gq.gq_fake_quant(p.layout, W.data_ptr(), gq.GQ_BF16,
+                                                        wfq.data_ptr(), p.flags.data_ptr()))
+        ft.run(2)
+        t, _ = ft.run(10)
+        fb = N * K * (4 + 2)
+        out[f"fake_quant_bf16_mlp{j}"] = {"N": N, "K": K, "us": round(t / 10 * 1e6, 1),
+                                          "GBps": round(fb * 10 / t / 1e9, 1),
+                                          "frac_hbm": round(fb * 10 / t / 1e9 / HBM_PEAK_GBS, 3)}
+        del W, wfq
         torch.cuda.empty_cache()
         M = 2048
         x = torch.from_numpy(S.channel_mix_x(j).view(np.int16)).cuda().view(torch.bfloat16)

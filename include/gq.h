@@ -117,6 +117,21 @@ gq_status gq_quantize_pack(const gq_layout *layout, const float *w, uint32_t *co
 gq_status gq_dequant(const gq_layout *layout, const uint32_t *codes, const uint16_t *scales,
                      const uint8_t *zeros, gq_dtype out_dtype, void *w_out, void *stream);
 
+/* Fake quantization: w_out = (code - z) * S with S, z and the codes of
+ * gq_quantize_pack, without packing -- the forward of a FakeQuantize module
+ * in quantization-aware training ("大模型量化实战：从原理到4-bit部署的完整指南",
+ * section 5.2: quantize and dequantize in the forward, FP32 gradient in the
+ * backward).  Equal to gq_quantize_pack followed by gq_dequant, bit for bit,
+ * in one pass over w.  The straight-through backward is the identity
+ * (dL/dw = dL/dw_out: a MinMax range clips no weight), so it has no entry
+ * point.
+ *   w      DEVICE fp32 [N][K], 16-byte aligned, read only.
+ *   w_out  DEVICE [N][K] of out_dtype (GQ_FP32 exact; GQ_BF16 / GQ_FP16
+ *          rounded to nearest even), 16-byte aligned, written; may not alias w.
+ *   flags  DEVICE uint32 or NULL; GQ_FLAG_* bits as for gq_quantize_pack. */
+gq_status gq_fake_quant(const gq_layout *layout, const float *w, gq_dtype out_dtype, void *w_out,
+                        uint32_t *flags, void *stream);
+
 /* Workspace gq_linear needs for this layout, M and activation dtype (HOST
  * output *bytes; may be 0).  Pure host computation. */
 gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,

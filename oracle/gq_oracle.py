@@ -262,6 +262,17 @@ def dequant_as(p: Packed, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def fake_quant(W, layout: Layout, dtype: str = "fp32") -> np.ndarray:
+    """Quantize, then dequantize, without packing ([QP] section 5.2: a
+    FakeQuantize module simulates round(x/s) + z in the forward pass; the
+    backward lets the gradient through the FP32 path, i.e. the identity).
+
+    The quantizer is the group-wise MinMax one of quantize_pack and the
+    dequantizer the one of dequant, applied in that order; dtype as for
+    dequant_as ('fp32' exact, 'fp16', 'bf16' bits)."""
+    return dequant_as(quantize_pack(W, layout), dtype)
+
+
 # ------------------------------------------------------------ matmul
 
 def bf16_bits_to_f64(bits) -> np.ndarray:

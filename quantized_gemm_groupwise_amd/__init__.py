@@ -30,8 +30,8 @@ GQ_MAX_BLOCKS = 1024
 GROUP = {4: 128, 2: 64}
 
 # Every symbol include/gq.h declares.
-EXPORTS = ("gq_packed_bytes", "gq_quantize_pack", "gq_dequant", "gq_linear_workspace_bytes",
-           "gq_linear", "gq_status_string")
+EXPORTS = ("gq_packed_bytes", "gq_quantize_pack", "gq_fake_quant", "gq_dequant",
+           "gq_linear_workspace_bytes", "gq_linear", "gq_status_string")
 
 
 class GqError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "gq_packed_bytes": ([L, P(S), P(S), P(S)], ctypes.c_int),
         "gq_quantize_pack": ([L, VP, VP, VP, VP, VP, VP], ctypes.c_int),
+        "gq_fake_quant": ([L, VP, ctypes.c_int, VP, VP, VP], ctypes.c_int),
         "gq_dequant": ([L, VP, VP, VP, ctypes.c_int, VP, VP], ctypes.c_int),
         "gq_linear_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
         "gq_linear": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
@@ -107,6 +108,11 @@ def gq_quantize_pack(layout, w_ptr, codes_ptr, scales_ptr, zeros_ptr, flags_ptr=
                      stream=None) -> int:
     return load_library().gq_quantize_pack(ctypes.byref(layout), w_ptr, codes_ptr, scales_ptr,
                                            zeros_ptr, flags_ptr, _stream(stream))
+
+
+def gq_fake_quant(layout, w_ptr, out_dtype, out_ptr, flags_ptr=None, stream=None) -> int:
+    return load_library().gq_fake_quant(ctypes.byref(layout), w_ptr, int(out_dtype), out_ptr,
+                                        flags_ptr, _stream(stream))
 
 
 def gq_dequant(layout, codes_ptr, scales_ptr, zeros_ptr, out_dtype, out_ptr, stream=None) -> int:
@@ -208,6 +214,24 @@ def dequant(p: Packed, dtype=torch.float32, stream=None) -> torch.Tensor:
     out = torch.empty((p.N, p.K), dtype=dtype, device=p.codes.device)
     _check(gq_dequant(p.layout, p.codes.data_ptr(), p.scales.data_ptr(), p.zeros.data_ptr(),
                       _DT[dtype], out.data_ptr(), stream), "gq_dequant")
+    return out
+
+
+def fake_quant(w: torch.Tensor, bits, block_n: int | None = None, dtype=torch.float32,
+               flags: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Quantize-dequantize fp32 weights w [N][K] (the forward of a FakeQuantize
+    module); the straight-through backward is the identity."""
+    _cuda(w, "w")
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor [N][K]")
+    N, K = w.shape
+    bl = [int(bits)] if isinstance(bits, int) else [int(b) for b in bits]
+    if block_n is None:
+        block_n = N // len(bl) if bl else N
+    lay = make_layout(K, N, max(1, int(block_n)), bl)
+    out = torch.empty((N, K), dtype=dtype, device=w.device)
+    fp = flags.data_ptr() if flags is not None else None
+    _check(gq_fake_quant(lay, w.data_ptr(), _DT[dtype], out.data_ptr(), fp, stream), "gq_fake_quant")
     return out
 
 

@@ -60,6 +60,20 @@ gq_status gq_quantize_pack(const gq_layout *layout, const float *w, uint32_t *co
   return launched(launch_quantize_pack(L, w, codes, scales, zeros, flags, s), s);
 }
 
+gq_status gq_fake_quant(const gq_layout *layout, const float *w, gq_dtype out_dtype, void *w_out,
+                        uint32_t *flags, void *stream) {
+  LayoutDev L;
+  gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  if (out_dtype != GQ_BF16 && out_dtype != GQ_FP16 && out_dtype != GQ_FP32) return GQ_ERR_DTYPE;
+  if (L.N == 0) return GQ_OK;
+  if ((st = check_ptr16(w)) != GQ_OK) return st;
+  if ((st = check_ptr16(w_out)) != GQ_OK) return st;
+  if (flags && ((uintptr_t)flags & 3u)) return GQ_ERR_ALIGNMENT;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launched(launch_fake_quant(L, w, out_dtype, w_out, flags, s), s);
+}
+
 gq_status gq_dequant(const gq_layout *layout, const uint32_t *codes, const uint16_t *scales,
                      const uint8_t *zeros, gq_dtype out_dtype, void *w_out, void *stream) {
   LayoutDev L;

@@ -51,6 +51,8 @@ size_t linear_workspace_bytes(const LayoutDev &L, int M, gq_dtype act);
 hipError_t launch_quantize_pack(const LayoutDev &L, const float *w, uint32_t *codes,
                                 uint16_t *scales, uint8_t *zeros, uint32_t *flags,
                                 hipStream_t s);
+hipError_t launch_fake_quant(const LayoutDev &L, const float *w, gq_dtype out, void *w_out,
+                             uint32_t *flags, hipStream_t s);
 hipError_t launch_dequant(const LayoutDev &L, const uint32_t *codes, const uint16_t *scales,
                           const uint8_t *zeros, gq_dtype out, void *w_out, hipStream_t s);
 hipError_t launch_gemv(const LayoutDev &L, int M, gq_dtype act, const void *x,

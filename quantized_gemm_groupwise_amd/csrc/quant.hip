@@ -10,6 +10,13 @@
 //
 // Dequantizer: (q - z) * s, the "Zero Point" formula of "Low-bit
 // Quantization: Slimming Large Models to the Extreme".
+//
+// Fake quantization (quantize, then dequantize, in one pass): the forward of
+// quantization-aware training with FakeQuantize modules ("大模型量化实战",
+// section 5.2: the forward quantizes and dequantizes, the gradient flows
+// through in FP32).  Same groups, scale, zero point and codes as the packing
+// quantizer; the output is (c - z) * s, exact in fp32, rounded to nearest
+// even for bf16 / fp16.
 #include "gq_internal.h"
 
 namespace gq {
@@ -22,11 +29,15 @@ constexpr int kLanes = 64;
 // One wave quantizes the 512-weight segment [k0, k0 + 512) of row n.  Lane l
 // holds weights k0 + 8l .. k0 + 8l + 7; a group of g weights spans g/8
 // consecutive lanes, so the min/max reduction is a butterfly over g/8 lanes.
-template <int BITS>
+// MODE kPack writes codes, scale and zero point; the other modes write the
+// fake-quantized weights of the lane to orow (0 bf16, 1 fp16, 2 fp32).
+constexpr int kPack = -1;
+template <int BITS, int MODE>
 __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, int K, int kl,
                                               uint8_t *__restrict__ crow,
                                               uint16_t *__restrict__ srow,
-                                              uint8_t *__restrict__ zrow, uint32_t *flags) {
+                                              uint8_t *__restrict__ zrow, void *__restrict__ orow,
+                                              uint32_t *flags) {
   constexpr int G = BITS == 4 ? 128 : 64;
   constexpr int LPG = G / 8;  // lanes per group
   const bool active = kl < K;
@@ -63,10 +74,36 @@ __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, in
   const float S = (float)s16;
   const float z = fminf(fmaxf(rintf(-lo / S), 0.f), qm);
   uint32_t packed = 0;
+  float fq[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float c = fminf(fmaxf(rintf(v[i] / S) + z, 0.f), qm);
     packed |= ((uint32_t)c) << (BITS * i);
+    fq[i] = (c - z) * S;                     // exact: |c - z| <= 15, S has 11 bits
+  }
+  if (MODE != kPack) {
+    if (active) {
+      if (MODE == 2) {
+        float *o = reinterpret_cast<float *>(orow) + kl;
+        *reinterpret_cast<float4 *>(o) = make_float4(fq[0], fq[1], fq[2], fq[3]);
+        *reinterpret_cast<float4 *>(o + 4) = make_float4(fq[4], fq[5], fq[6], fq[7]);
+      } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint16_t a = MODE == 0 ? f32_to_bf16_rne(fq[2 * p]) : f32_to_f16_bits(fq[2 * p]);
+          const uint16_t b = MODE == 0 ? f32_to_bf16_rne(fq[2 * p + 1]) : f32_to_f16_bits(fq[2 * p + 1]);
+          h[p] = (uint32_t)a | ((uint32_t)b << 16);
+        }
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(orow) + kl) = make_uint4(h[0], h[1], h[2], h[3]);
+      }
+    }
+    if (flags) {
+      uint32_t f = finite ? 0u : GQ_FLAG_NONFINITE;
+      if (finite && __builtin_isinf(S)) f |= GQ_FLAG_SCALE_OVERFLOW;
+      if (f && active) atomicOr(flags, f);
+    }
+    return;
   }
   if (!active) return;
   if (BITS == 4) {
@@ -87,10 +124,11 @@ __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, in
   }
 }
 
+template <int MODE>
 __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
     LayoutDev L, const float *__restrict__ w, uint8_t *__restrict__ codes,
-    uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros, uint32_t *flags,
-    int segs_per_row) {
+    uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros, void *__restrict__ wout,
+    uint32_t *flags, int segs_per_row) {
   const int wave = threadIdx.x / kLanes;
   const int lane = threadIdx.x & (kLanes - 1);
   const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
@@ -103,14 +141,19 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
   const BlockInfo bi = block_info(L, blk);
   const float *wrow = w + (int64_t)n * L.K;
   const int kl = seg * kSeg + lane * 8;
+  void *orow = nullptr;
+  if (MODE != kPack)
+    orow = reinterpret_cast<uint8_t *>(wout) + (int64_t)n * L.K * (MODE == 2 ? 4 : 2);
   if (bi.bits == 4) {
-    uint8_t *crow = codes + bi.code_off + (uint64_t)r * (uint64_t)(L.K / 2);
+    uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)(L.K / 2) : nullptr;
     const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(L.K / 128);
-    quant_segment<4>(wrow, L.K, kl, crow, scales + g0, zeros + g0, flags);
+    quant_segment<4, MODE>(wrow, L.K, kl, crow, MODE == kPack ? scales + g0 : nullptr,
+                           MODE == kPack ? zeros + g0 : nullptr, orow, flags);
   } else {
-    uint8_t *crow = codes + bi.code_off + (uint64_t)r * (uint64_t)(L.K / 4);
+    uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)(L.K / 4) : nullptr;
     const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(L.K / 64);
-    quant_segment<2>(wrow, L.K, kl, crow, scales + g0, zeros + g0, flags);
+    quant_segment<2, MODE>(wrow, L.K, kl, crow, MODE == kPack ? scales + g0 : nullptr,
+                           MODE == kPack ? zeros + g0 : nullptr, orow, flags);
   }
 }
 
@@ -181,8 +224,28 @@ hipError_t launch_quantize_pack(const LayoutDev &L, const float *w, uint32_t *co
   const int segs = (L.K + kSeg - 1) / kSeg;
   const int64_t waves = (int64_t)L.N * segs;
   const int64_t blocks = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(quantize_pack_kernel, dim3((unsigned)blocks), dim3(kWaves * kLanes), 0, s, L, w,
-                     reinterpret_cast<uint8_t *>(codes), scales, zeros, flags, segs);
+  hipLaunchKernelGGL(quantize_pack_kernel<kPack>, dim3((unsigned)blocks), dim3(kWaves * kLanes), 0, s,
+                     L, w, reinterpret_cast<uint8_t *>(codes), scales, zeros, nullptr, flags, segs);
+  return hipGetLastError();
+}
+
+hipError_t launch_fake_quant(const LayoutDev &L, const float *w, gq_dtype out, void *w_out,
+                             uint32_t *flags, hipStream_t s) {
+  if (L.N == 0) return hipSuccess;
+  const int segs = (L.K + kSeg - 1) / kSeg;
+  const int64_t waves = (int64_t)L.N * segs;
+  const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves)), block(kWaves * kLanes);
+  switch (out) {
+    case GQ_BF16:
+      hipLaunchKernelGGL(quantize_pack_kernel<0>, grid, block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
+      break;
+    case GQ_FP16:
+      hipLaunchKernelGGL(quantize_pack_kernel<1>, grid, block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
+      break;
+    default:
+      hipLaunchKernelGGL(quantize_pack_kernel<2>, grid, block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
+      break;
+  }
   return hipGetLastError();
 }
 

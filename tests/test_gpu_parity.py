@@ -134,6 +134,55 @@ def test_dequant_bit_exact(block_n, bits):
         assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(exp).view(np.uint8)), name
 
 
+# ------------------------------------------------------- fake quantization
+
+def _fq_bytes(t: torch.Tensor, name: str) -> np.ndarray:
+    got = t.cpu()
+    got = got.view(torch.int16).numpy().view(np.uint16) if name == "bf16" else got.numpy()
+    return np.ascontiguousarray(got).view(np.uint8)
+
+
+@pytest.mark.parametrize("N,K,block_n,bits", [
+    (1, 64, 1, [2]), (3, 640, 3, [4]), (129, 576, 129, [2]), (256, 1024, 256, [4]),
+    (512, 1024, 128, [4, 2, 2, 4]), (384, 768, 128, [2, 4, 2]),
+])
+def test_fake_quant_bit_exact(N, K, block_n, bits):
+    """gq_fake_quant equals the oracle's quantize-then-dequantize, bit for bit,
+    for fp32, fp16 and bf16 outputs, and the GPU's own quantize_pack + dequant."""
+    W = S.decode_weight(4, N=N, K=K)
+    L = O.Layout(K, N, block_n, bits)
+    w = to_dev(W)
+    p = gq.quantize_pack(w, bits, block_n)
+    _say("fake quant", N, K, block_n, bits)
+    for dt, name in [(torch.float32, "fp32"), (torch.float16, "fp16"), (torch.bfloat16, "bf16")]:
+        flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out = gq.fake_quant(w, bits, block_n, dt, flags=flags)
+        two_pass = gq.dequant(p, dt)
+        torch.cuda.synchronize()
+        exp = np.ascontiguousarray(O.fake_quant(W, L, name)).view(np.uint8)
+        assert np.array_equal(_fq_bytes(out, name), exp), name
+        assert np.array_equal(_fq_bytes(two_pass, name), exp), name
+        assert int(flags.item()) == 0
+
+
+def test_fake_quant_flags_and_edge_groups():
+    """The flags of quantize_pack, and exact output for degenerate, clamped-zero
+    and tie groups next to a non-finite one (whose output is unspecified)."""
+    g = 128
+    rows = [np.full(g, 0.37, np.float32), np.linspace(3.0, 4.0, g, dtype=np.float32),
+            np.linspace(-4.0, -3.0, g, dtype=np.float32),
+            (np.arange(g, dtype=np.float32) - 40.5) * np.float32(2 ** -7), np.zeros(g, np.float32)]
+    W = np.stack(rows)
+    W[4, 5] = np.nan
+    L = O.Layout(g, W.shape[0], W.shape[0], [4])
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = gq.fake_quant(to_dev(W), 4, W.shape[0], torch.float32, flags=flags)
+    torch.cuda.synchronize()
+    exp = O.fake_quant(W, L)
+    assert np.array_equal(out.cpu().numpy()[:4], exp[:4])
+    assert int(flags.item()) == O.FLAG_NONFINITE
+
+
 # ------------------------------------------------------------- linear
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])

@@ -128,6 +128,53 @@ def test_endpoint_and_error_bounds_random(bits):
     assert np.mean(err <= Sv[:, None] / 2) > 0.999
 
 
+# ----------------------------------------------------- fake quantization
+
+def test_fake_quant_hand_example():
+    """One INT2 group of the 64 weights k/16 (k = 0..63) through FakeQuantize
+    ("大模型量化实战", section 5.2: round(x/s) + z in the forward, then back).
+    x_min = 0 and x_max = 63/16 give s = (63/16)/3 = 21/16, exact in fp16, and
+    z = round(0) = 0, so the code is round(k/21): 0 up to k = 10, 1 from 11
+    to 31, 2 from 32 to 52 and 3 from 53 on; the output is code * 21/16."""
+    w = (np.arange(64, dtype=np.float32) / 16).reshape(1, 64)
+    out = O.fake_quant(w, O.Layout(64, 1, 1, [2]))
+    code = np.array([0] * 11 + [1] * 21 + [2] * 21 + [3] * 11)
+    assert np.array_equal(out[0].astype(np.float64), code * 21 / 16)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_fake_quant_keeps_values_on_the_grid(bits):
+    """A group whose values already sit on a 2^b-level grid spanning it
+    (v = j/2^b - 1/2, j = 0..2^b-1, each level present) comes back unchanged:
+    s = (2^b - 1)/2^b / (2^b - 1) = 2^-b, z = 2^(b-1), code = j."""
+    g = O.GROUP_SIZE[bits]
+    lv = 2 ** bits
+    j = np.arange(g) % lv
+    w = (j / lv - 0.5).astype(np.float32).reshape(1, g)
+    out = O.fake_quant(w, O.Layout(g, 1, 1, [bits]))
+    assert np.array_equal(out, w)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_fake_quant_levels_and_error(bits):
+    """Each output group takes at most 2^b values (16 for INT4, 4 for INT2:
+    datatype table of "Low-bit Quantization"), evenly spaced, and stays within
+    half a step of the input wherever the zero point was not clamped, plus the
+    part of the range past (2^b - 1) steps when the fp16 scale rounded down."""
+    g = O.GROUP_SIZE[bits]
+    W = S.decode_weight(1, N=64, K=1024)
+    fq = O.fake_quant(W, O.Layout(1024, 64, 64, [bits])).astype(np.float64).reshape(-1, g)
+    G = W.astype(np.float64).reshape(-1, g)
+    for out, w in zip(fq, G):
+        vals = np.unique(out)
+        assert len(vals) <= 2 ** bits
+        step = np.min(np.diff(vals))
+        assert np.allclose((vals - vals[0]) / step, np.rint((vals - vals[0]) / step), atol=1e-9)
+        if w.min() < 0 < w.max():
+            over = max(0.0, (w.max() - w.min()) - O.qmax(bits) * step)
+            assert np.max(np.abs(out - w)) <= (step / 2 + over) * (1 + 2 ** -10)
+
+
 # -------------------------------------------------------- P4 idempotence
 
 @pytest.mark.parametrize("bits", [4, 2])
