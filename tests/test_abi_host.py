@@ -82,6 +82,13 @@ def test_argument_errors_before_launch(lib):
     assert Q(A, A, A + 1, A, None, None) == gq.GQ_ERR_ALIGNMENT
     assert Q(A, A, None, A, None, None) == gq.GQ_ERR_NULL_ARG
     assert Q(A, A, A, A, A + 2, None) == gq.GQ_ERR_ALIGNMENT
+    F = lambda *a: lib.gq_fake_quant(ctypes.byref(lay), *a)
+    assert F(A, 7, A, None, None) == gq.GQ_ERR_DTYPE
+    assert F(None, gq.GQ_BF16, A, None, None) == gq.GQ_ERR_NULL_ARG
+    assert F(bad, gq.GQ_BF16, A, None, None) == gq.GQ_ERR_ALIGNMENT
+    assert F(A, gq.GQ_FP32, None, None, None) == gq.GQ_ERR_NULL_ARG
+    assert F(A, gq.GQ_FP32, bad, None, None) == gq.GQ_ERR_ALIGNMENT
+    assert F(A, gq.GQ_FP32, A, A + 2, None) == gq.GQ_ERR_ALIGNMENT
     D = lambda *a: lib.gq_dequant(ctypes.byref(lay), *a)
     assert D(A, A, A, 7, A, None) == gq.GQ_ERR_DTYPE
     assert D(A, A, A, gq.GQ_FP32, bad, None) == gq.GQ_ERR_ALIGNMENT
@@ -101,6 +108,7 @@ def test_argument_errors_before_launch(lib):
     assert Lf(0, gq.GQ_BF16, None, None, None, 0) == gq.GQ_OK
     lay0 = gq.make_layout(512, 0, 1, [])
     assert lib.gq_quantize_pack(ctypes.byref(lay0), None, None, None, None, None, None) == gq.GQ_OK
+    assert lib.gq_fake_quant(ctypes.byref(lay0), None, gq.GQ_BF16, None, None, None) == gq.GQ_OK
 
 
 def test_workspace_sizes():
