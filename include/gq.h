@@ -172,6 +172,33 @@ gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void
                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                     void *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace gq_linear_dx needs for this layout, M and dtype (HOST output
+ * *bytes; may be 0).  Returns GQ_ERR_SHAPE where gq_linear_dx would (N not a
+ * multiple of 8, or buffers past 2 GiB).  Pure host computation. */
+gq_status gq_linear_dx_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
+                                       size_t *bytes);
+
+/* Data gradient of gq_linear: dx = dy . W_hat, dx[m][k] = sum_n dy[m][n] *
+ * W_hat[n][k], the product back-propagation needs to train through the
+ * packed weights (GreenBitAI, the Q-SFT and Bitorch Engine paragraphs:
+ * full-parameter fine-tuning in the quantized weight space).  Same
+ * arithmetic as the M > 32 path of gq_linear: each dequantized weight rounded
+ * once to fp16, dy rescaled per row by a power of two so that its fp16 form is
+ * exact, MFMA with fp32 accumulation, x 2^e and round to nearest even.
+ *   act    GQ_BF16 or GQ_FP16: dtype of dy and dx.
+ *   dy     DEVICE [M][N] act, 16-byte aligned; N must be a multiple of 8.
+ *   dx     DEVICE [M][K] act, 2-byte aligned, written.
+ *   workspace  DEVICE, 256-byte aligned, at least
+ *          gq_linear_dx_workspace_bytes; overwritten; calls sharing it must
+ *          be ordered on one stream.
+ * Work is tiled 256 (m) x 256 (k); the reduction over n is split across
+ * workgroups when the tiles alone would leave CUs idle (fp32 parts in the
+ * workspace, summed in part order).  Deterministic.  N == 0 writes zeros.
+ * Errors: GQ_ERR_SHAPE for N % 8 != 0 (and the layout rules of gq_linear). */
+gq_status gq_linear_dx(const gq_layout *layout, int32_t M, gq_dtype act, const void *dy,
+                       const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                       void *dx, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *gq_status_string(gq_status status);
 

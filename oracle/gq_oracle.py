@@ -17,6 +17,9 @@ Sources (page title, then the part of the page):
   [QP]  "大模型量化实战：从原理到4-bit部署的完整指南" (jsqmd.com) -- section 2.2:
         Q(x) = round(x/s) + z, s = (x_max - x_min)/(q_max - q_min),
         z = round(0 - x_min/s), z kept inside the integer range.
+  [GB]  also the Q-SFT and Bitorch Engine paragraphs: full-parameter
+        fine-tuning in the quantized weight space, which back-propagates
+        through the low-bit weights.
   [SV]  "A Survey of Low-bit Large Language Models: Basics, Systems, and
         Algorithms" (paper review) -- section 5.2 and section 6.2:
         weight-only quantization dequantizes and then runs an FP16 matmul.
@@ -289,6 +292,22 @@ def linear(x_bf16, p: Packed, rows=None) -> np.ndarray:
     x = bf16_bits_to_f64(x_bf16)
     w = dequant(p, rows).astype(np.float64)
     return x @ w.T
+
+
+def linear_dx(dy_bf16, p: Packed, cols=None) -> np.ndarray:
+    """dX = dY . W_hat accumulated in fp64: the data gradient of
+    y = x . W_hat^T, which back-propagation through the quantized linear
+    needs when the model is fine-tuned in its quantized space ([GB] Q-SFT
+    and Bitorch Engine paragraphs: gradients through low-bit weights).
+    W_hat is the dequantized weight of dequant ([LB] "Zero Point").
+
+    dy_bf16: uint16 bf16 bit patterns [M][N].  cols: optional subset of input
+    channels k; returns fp64 [M][len(cols)] (all K when cols is None)."""
+    dy = bf16_bits_to_f64(dy_bf16)
+    w = dequant(p).astype(np.float64)
+    if cols is not None:
+        w = w[:, np.asarray(list(cols), dtype=np.int64)]
+    return dy @ w
 
 
 def f64_to_bf16_bits(a) -> np.ndarray:

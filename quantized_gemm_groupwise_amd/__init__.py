@@ -8,6 +8,7 @@ kernels.  PyTorch provides device memory and the current stream.
 Convenience layer:
     packed = quantize_pack(w, bits, block_n=None)   # w: fp32 cuda [N][K]
     y = linear(x, packed)                           # x: bf16/fp16 cuda [M][K]
+    dx = linear_dx(dy, packed)                      # dy: bf16/fp16 cuda [M][N]
     w_hat = dequant(packed, torch.float32)
 """
 from __future__ import annotations
@@ -31,7 +32,8 @@ GROUP = {4: 128, 2: 64}
 
 # Every symbol include/gq.h declares.
 EXPORTS = ("gq_packed_bytes", "gq_quantize_pack", "gq_fake_quant", "gq_dequant",
-           "gq_linear_workspace_bytes", "gq_linear", "gq_status_string")
+           "gq_linear_workspace_bytes", "gq_linear", "gq_linear_dx_workspace_bytes",
+           "gq_linear_dx", "gq_status_string")
 
 
 class GqError(RuntimeError):
@@ -66,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gq_dequant": ([L, VP, VP, VP, ctypes.c_int, VP, VP], ctypes.c_int),
         "gq_linear_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
         "gq_linear": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
+        "gq_linear_dx_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
+        "gq_linear_dx": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
         "gq_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -134,6 +138,22 @@ def gq_linear(layout, M, act, x_ptr, codes_ptr, scales_ptr, zeros_ptr, y_ptr, ws
     return load_library().gq_linear(ctypes.byref(layout), int(M), int(act), x_ptr, codes_ptr,
                                     scales_ptr, zeros_ptr, y_ptr, ws_ptr, int(ws_bytes),
                                     _stream(stream))
+
+
+def gq_linear_dx_workspace_bytes(layout, M: int, act: int = GQ_BF16) -> int:
+    b = ctypes.c_size_t()
+    st = load_library().gq_linear_dx_workspace_bytes(ctypes.byref(layout), int(M), int(act),
+                                                     ctypes.byref(b))
+    if st != GQ_OK:
+        raise GqError(st, "gq_linear_dx_workspace_bytes")
+    return b.value
+
+
+def gq_linear_dx(layout, M, act, dy_ptr, codes_ptr, scales_ptr, zeros_ptr, dx_ptr, ws_ptr, ws_bytes,
+                 stream=None) -> int:
+    return load_library().gq_linear_dx(ctypes.byref(layout), int(M), int(act), dy_ptr, codes_ptr,
+                                       scales_ptr, zeros_ptr, dx_ptr, ws_ptr, int(ws_bytes),
+                                       _stream(stream))
 
 
 # ------------------------------------------------------ tensor-level API
@@ -269,3 +289,25 @@ def linear(x: torch.Tensor, p: Packed, out: torch.Tensor | None = None, ws: torc
     _check(gq_linear(p.layout, M, act, x.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
                      p.zeros.data_ptr(), y.data_ptr(), wptr, wbytes, stream), "gq_linear")
     return y
+
+
+def linear_dx(dy: torch.Tensor, p: Packed, out: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """dX = dY . W_hat for bf16 or fp16 dY [M][N] (the data gradient of
+    linear); dX is [M][K] in dY's dtype."""
+    _cuda(dy, "dy")
+    if dy.dim() != 2 or dy.shape[1] != p.N:
+        raise ValueError(f"dy must be [M][{p.N}]")
+    act = _DT.get(dy.dtype)
+    if act not in (GQ_BF16, GQ_FP16):
+        raise ValueError("dy must be bfloat16 or float16")
+    M = dy.shape[0]
+    dx = torch.empty((M, p.K), dtype=dy.dtype, device=dy.device) if out is None else out
+    need = gq_linear_dx_workspace_bytes(p.layout, M, act)
+    if ws is None:
+        ws = workspace(need, dy.device)
+    wptr = ws.data_ptr() if ws is not None else None
+    wbytes = ws.numel() if ws is not None else 0
+    _check(gq_linear_dx(p.layout, M, act, dy.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
+                        p.zeros.data_ptr(), dx.data_ptr(), wptr, wbytes, stream), "gq_linear_dx")
+    return dx

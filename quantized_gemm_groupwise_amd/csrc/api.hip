@@ -127,6 +127,44 @@ gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void
   return launched(launch_gemm(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
 }
 
+gq_status gq_linear_dx_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
+                                       size_t *bytes) {
+  if (!bytes) return GQ_ERR_NULL_ARG;
+  LayoutDev L;
+  const gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  if (M < 0) return GQ_ERR_SHAPE;
+  if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  if (M > 0 && L.N > 0 && !dx_supported(L, M)) return GQ_ERR_SHAPE;
+  *bytes = dx_workspace_bytes(L, M);
+  return GQ_OK;
+}
+
+gq_status gq_linear_dx(const gq_layout *layout, int32_t M, gq_dtype act, const void *dy,
+                       const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                       void *dx, void *workspace, size_t workspace_bytes, void *stream) {
+  LayoutDev L;
+  gq_status st = make_layout(layout, &L);
+  if (st != GQ_OK) return st;
+  if (M < 0) return GQ_ERR_SHAPE;
+  if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  if (M == 0) return GQ_OK;
+  if (L.N > 0 && !dx_supported(L, M)) return GQ_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!dx) return GQ_ERR_NULL_ARG;
+  if ((uintptr_t)dx & 1u) return GQ_ERR_ALIGNMENT;
+  if (L.N == 0)  // an empty sum: dX is zero
+    return launched(launch_dx(L, M, act, nullptr, nullptr, nullptr, nullptr, dx, nullptr, s), s);
+  if ((st = check_ptr16(dy)) != GQ_OK) return st;
+  if ((st = check_ptr16(codes)) != GQ_OK) return st;
+  if (!scales || !zeros) return GQ_ERR_NULL_ARG;
+  if ((uintptr_t)scales & 1u) return GQ_ERR_ALIGNMENT;
+  const size_t need = dx_workspace_bytes(L, M);
+  if (!workspace || workspace_bytes < need) return GQ_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 255u) return GQ_ERR_ALIGNMENT;
+  return launched(launch_dx(L, M, act, dy, codes, scales, zeros, dx, workspace, s), s);
+}
+
 const char *gq_status_string(gq_status status) {
   switch (status) {
     case GQ_OK: return "GQ_OK: success";

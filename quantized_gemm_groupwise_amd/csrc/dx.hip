@@ -1,0 +1,385 @@
+// Data gradient through the packed weights: dX = dY . W_hat, the product the
+// backward pass needs for y = x . W_hat^T, i.e.
+//     dX[m][k] = sum_n dY[m][n] * W_hat[n][k],   W_hat = (q - z) * s.
+// GreenBitAI's full-parameter fine-tuning of the low-bit model and Bitorch
+// Engine's quantization-aware training run this product in their backward
+// pass ("只需单卡 RTX 3090 低比特量化训练就能实现 LLaMA-3 8B 全参微调", Q-SFT
+// and Bitorch Engine paragraphs).  The arithmetic is the forward matmul's:
+// each weight is rounded once to fp16 ("A Survey of Low-bit Large Language
+// Models", sections 5.2 and 6.2: dequantize, then an FP16 matmul), dY is
+// rescaled per row by a power of two so that its fp16 form is exact, the
+// MFMAs accumulate in fp32, and x 2^e and round-to-nearest-even end it.
+//
+// Work split.  A workgroup of 4 waves computes a 256 (m) x 256 (k) tile of
+// dX, each wave 64 columns and all 256 rows (eight 32-row blocks times two
+// 32-column blocks of MFMA 32x32x16).  The reduction runs over n in steps of
+// 128; dY's 256 x 128 slice of a step reaches LDS by buffer loads that write
+// LDS directly, one step ahead, into the other of two buffers, in the layout
+// the forward matmul uses for x (sub-step t reduces over n-chunks t and
+// 8 + t of the step).
+//
+// The weight operand.  A packed word holds consecutive k of one row n, but a
+// lane of the MFMA weight operand needs 8 consecutive n of one k.  So each
+// wave unpacks the 16 x 64 weight block of a sub-step itself -- a lane takes
+// one row and 16 consecutive k, with that row's scale and zero point -- and
+// writes it transposed into a private LDS block ([k][n] fp16), from which it
+// reads its operand fragments back.  LDS operations of one wave complete in
+// issue order, so the exchange needs no barrier.  A 128-row step lies inside
+// one Channel-mix block (blocks are multiples of 128 rows), so the bit width
+// is uniform per step.
+#include "gq_device.h"
+#include "gq_internal.h"
+
+namespace gq {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int DX_NT = 128;                              // n per step
+constexpr int DX_MB = 8;                                // 32-row blocks per wave
+constexpr int DX_NW = 4;                                // waves, 64 columns each
+constexpr int DX_TM = 32 * DX_MB;                       // 256 rows of dX
+constexpr int DX_TK = 64 * DX_NW;                       // 256 columns of dX
+constexpr int DX_TILE_BYTES = DX_TM * DX_NT * 2;        // 64 KB of dY per step
+constexpr int DX_DMA = DX_TILE_BYTES / (1024 * DX_NW);  // 1 KB LDS loads per wave per step
+constexpr int DX_WBLK = 64 * 16;                        // halfs of a wave's weight block
+constexpr uint32_t kOobDx = 0x80000000u;                // beyond every resource
+
+struct DxArgs {
+  int M, N, K, Np;
+  int m0, k0w;             // tile row origin; the wave's first column
+  int st0, st1;            // n steps [st0, st1) of this workgroup (even count)
+  bool kact;               // the wave's columns lie below K
+  const int *rexp;
+  uint16_t *dx;            // bf16/fp16 output, or
+  float *part;             // the fp32 partial [M][K] of this split
+  int out_fp16;
+};
+
+__device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uint4 *As0, uint4 *As1,
+                                        _Float16 *Wb, Rsrc xr, Rsrc cr, Rsrc sr, Rsrc zr, int wave) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  // weight block lane roles: row ri of the sub-step, 16 columns at 16 cj
+  const int ri = lane & 15, cj = lane >> 4;
+
+  // dY tile DMA (the forward matmul's x tile): load i (= DX_DMA * wave + p)
+  // writes slots 64 i .. 64 i + 63, rows 4i .. 4i + 3; lane l -> row
+  // 4i + l/16, chunk (l%16) ^ (row & 15), row & 15 = 4 (i & 3) + l/16
+  uint32_t dv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    dv[q] = (uint32_t)(((lane >> 4) * g.Np + (((lane & 15) ^ (4 * q + (lane >> 4))) * 8)) * 2);
+  auto dma_a = [&](int st, uint4 *dst, int p0, int np) {
+#pragma unroll
+    for (int p = p0; p < p0 + np; ++p) {
+      const int i = DX_DMA * wave + p;
+      const uint32_t soff = (uint32_t)(((g.m0 + 4 * i) * g.Np + st * DX_NT) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(dst + 64 * i), 16, dv[p & 3], soff,
+                                               0, 0);
+    }
+  };
+  // operand reads: lane (j, h) of block mb, sub-step t reads row 32 mb + j,
+  // chunk 8h + t, i.e. slot chunk ((8h) ^ (j & 8)) | (t ^ (j & 7))
+  const uint32_t rb = (uint32_t)(j * 16 + ((8 * h) ^ (j & 8)));
+
+  // block of a step (clamped: padding steps past N load nothing anyway)
+  auto step_block = [&](int st) {
+    int blk = st * DX_NT / L.block_n;
+    return blk < L.nblocks ? blk : L.nblocks - 1;
+  };
+  // codes, scale and zero point of row n0 + 8t + (ri & 7) + 64 (ri >> 3),
+  // columns k0w + 16 cj .. + 15 (8 bytes of INT4 codes or 4 of INT2)
+  auto load_b = [&](int st, uint2 *cw, uint32_t *sv, uint32_t *zv) {
+    const int blk = step_block(st);
+    const BlockInfo bi = block_info(L, blk);
+    const int bits = __builtin_amdgcn_readfirstlane(bi.bits);
+    const uint32_t RB = (uint32_t)(L.K * bits / 8);
+    const uint32_t GPR = (uint32_t)(bits == 4 ? L.K / 128 : L.K / 64);
+    const uint32_t gcol = (uint32_t)(g.k0w / (bits == 4 ? 128 : 64));
+    const uint32_t ccol = (uint32_t)((g.k0w + 16 * cj) * bits / 8);
+    uint32_t co[8], gi[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int n = st * DX_NT + 8 * t + (ri & 7) + 64 * (ri >> 3);
+      const bool ok = g.kact && n < g.N;
+      const uint32_t r = (uint32_t)(n - blk * L.block_n);
+      co[t] = ok ? (uint32_t)bi.code_off + r * RB + ccol : kOobDx;
+      gi[t] = ok ? (uint32_t)bi.grp_off + r * GPR + gcol : kOobDx;
+    }
+    if (bits == 4) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) cw[t] = ld64(cr, co[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) cw[t] = make_uint2(ld32(cr, co[t]), 0u);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      sv[t] = ld16(sr, gi[t] < kOobDx ? 2u * gi[t] : kOobDx);
+      zv[t] = ld8(zr, gi[t]);
+    }
+  };
+
+  floatx16 acc[DX_MB][2];
+#pragma unroll
+  for (int mb = 0; mb < DX_MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
+
+  // one n step from LDS tile `cur` with weights (bc, sc, zc); starts the
+  // next step's dY DMA into `nxt` and its weight loads into (bn, sn, zn).
+  // On the last step both reload the same step, so every load stays
+  // unconditional.  The bit width enters as uniform shift, mask and byte
+  // selectors rather than a branch: two copies of the MFMA loop under a
+  // branch make the register allocator spill the accumulators.
+  auto step = [&](int st, const uint4 *cur, uint4 *nxt, const uint2 *bc, const uint32_t *sc,
+                  const uint32_t *zc, uint2 *bn, uint32_t *sn, uint32_t *zn) {
+    const int sn_ = st + 1 < g.st1 ? st + 1 : st;
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(sn_, bn, sn, zn);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool b4 = __builtin_amdgcn_readfirstlane(block_info(L, step_block(st)).bits) == 4;
+    // chunk c of a lane's 16 codes as unpack_f16_chunk wants it: INT4 takes
+    // word c as it is; INT2 spreads byte 2c to the low half and byte 2c + 1
+    // to the high half of the word
+    const uint32_t sel0 = b4 ? 0x03020100u : 0x01010000u;
+    const uint32_t sel1 = b4 ? 0x07060504u : 0x03030202u;
+    const uint32_t sh = b4 ? 4u : 2u;
+    const uint32_t mask = b4 ? 0x000f000fu : 0x00030003u;
+    // unpack this lane's 16 weights of sub-step t and write them to the
+    // wave's block at [column][row]
+    auto make_b = [&](int t) {
+      const uint16_t zb = f32_to_f16_bits(-(1024.f + (float)zc[t]));
+      const half2v s2 = __builtin_bit_cast(half2v, sc[t] | (sc[t] << 16));
+      const half2v cz = __builtin_bit_cast(half2v, (uint32_t)zb | ((uint32_t)zb << 16));
+      const uint32_t cwd[2] = {__builtin_amdgcn_perm(bc[t].y, bc[t].x, sel0),
+                               __builtin_amdgcn_perm(bc[t].y, bc[t].x, sel1)};
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // 1024 + q for elements e and e + 4 of chunk c, then (q - z) s
+          const uint32_t p = and_or(cwd[c] >> (sh * e), mask, 0x64006400u);
+          const half2v v = (__builtin_bit_cast(half2v, p) + cz) * s2;
+          Wb[(16 * cj + 8 * c + e) * 16 + ri] = v.x;
+          Wb[(16 * cj + 8 * c + e + 4) * 16 + ri] = v.y;
+        }
+      }
+    };
+    // B operand of lane (j, h): rows 8h .. 8h + 7 of column 32 nb + j
+    auto read_b = [&](half8 *bf) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bf[nb] = *reinterpret_cast<const half8 *>(&Wb[(32 * nb + j) * 16 + 8 * h]);
+    };
+    auto read_a = [&](int t, half8 *af) {
+      const uint32_t slot = rb + (uint32_t)(t ^ (j & 7));
+#pragma unroll
+      for (int mb = 0; mb < DX_MB; ++mb) af[mb] = __builtin_bit_cast(half8, cur[mb * 512 + slot]);
+    };
+    half8 af[2][DX_MB], bf[2][2];
+    make_b(0);
+    read_b(bf[0]);
+    read_a(0, af[0]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int c = t & 1, n = c ^ 1;
+      // the next tile's dY, a quarter of the loads per sub-step over the
+      // first four
+      if (t < 4) dma_a(sn_, nxt, (DX_DMA / 4) * t, DX_DMA / 4);
+      if (t + 1 < 8) {
+        make_b(t + 1);
+        read_b(bf[n]);
+        read_a(t + 1, af[n]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < DX_MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][mb], bf[c][nb], acc[mb][nb], 0, 0, 0);
+      // one wave per SIMD: the next sub-step's unpacking, its LDS exchange
+      // and operand reads issue between this sub-step's MFMAs
+#pragma unroll
+      for (int i = 0; i < 2 * DX_MB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        if (t < 4 && i < DX_DMA / 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // dY load
+        if (t + 1 < 8) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);          // VALU
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);          // LDS write
+          if (i < DX_MB + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the next tile's DMA has landed in every wave's part once all waves
+    // pass this barrier
+    lds_barrier();
+  };
+  uint2 b0[8], b1[8];
+  uint32_t s0[8], s1[8], z0[8], z1[8];
+  dma_a(g.st0, As0, 0, DX_DMA);
+  load_b(g.st0, b0, s0, z0);
+  lds_barrier();
+  for (int st = g.st0; st < g.st1; st += 2) {
+    step(st, As0, As1, b0, s0, z0, b1, s1, z1);
+    step(st + 1, As1, As0, b1, s1, z1, b0, s0, z0);
+  }
+
+  if (!g.kact) return;
+  // lane (j, h) holds column k0w + 32 nb + j and rows 8(e/4) + 4h + e%4 of
+  // each 32-row block
+  if (g.part) {
+#pragma unroll
+    for (int mb = 0; mb < DX_MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = g.m0 + mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int k = g.k0w + 32 * nb + j;
+          if (m < g.M && k < g.K) g.part[(int64_t)m * g.K + k] = acc[mb][nb][e];
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int mb = 0; mb < DX_MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = g.m0 + mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      const int ex = m < g.M ? g.rexp[m] : 0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int k = g.k0w + 32 * nb + j;
+        const float v = ldexpf(acc[mb][nb][e], ex);
+        if (m < g.M && k < g.K)
+          g.dx[(int64_t)m * g.K + k] = g.out_fp16 ? f32_to_f16_bits(v) : f32_to_bf16_rne(v);
+      }
+    }
+}
+
+__global__ __launch_bounds__(64 * DX_NW, 1) void dx_kernel(
+    LayoutDev L, int M, int Np, uint32_t ya_bytes, int m_tiles, const uint16_t *__restrict__ ya,
+    const int *__restrict__ rexp, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, uint32_t code_bytes,
+    uint32_t groups, uint16_t *__restrict__ dx, int out_fp16, int steps_per_split,
+    float *__restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint4 As0[DX_TILE_BYTES / 16];
+  __shared__ __attribute__((aligned(16))) uint4 As1[DX_TILE_BYTES / 16];
+  __shared__ __attribute__((aligned(16))) _Float16 Wb[DX_NW * DX_WBLK];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // tile order: m fastest, so the workgroups on one XCD (every 8th id)
+  // share one m tile of dY in that XCD's L2
+  const int tile = (int)blockIdx.x;
+  const int m_tile = tile % m_tiles, k_tile = tile / m_tiles;
+  const int nsteps = Np / DX_NT;
+  DxArgs g;
+  g.M = M; g.N = L.N; g.K = L.K; g.Np = Np;
+  g.m0 = m_tile * DX_TM;
+  g.k0w = k_tile * DX_TK + wave * 64;
+  g.kact = g.k0w < L.K;
+  g.st0 = (int)blockIdx.y * steps_per_split;
+  g.st1 = min(g.st0 + steps_per_split, nsteps);
+  g.rexp = rexp;
+  g.dx = dx;
+  g.part = gridDim.y > 1 ? part + (size_t)blockIdx.y * (size_t)M * (size_t)L.K : nullptr;
+  g.out_fp16 = out_fp16;
+  const Rsrc xr = make_rsrc(ya, ya_bytes);
+  const Rsrc cr = make_rsrc(codes, code_bytes);
+  const Rsrc sr = make_rsrc(scales, 2u * groups);
+  const Rsrc zr = make_rsrc(zeros, groups);
+  dx_wave(L, g, As0, As1, Wb + wave * DX_WBLK, xr, cr, sr, zr, wave);
+}
+
+// dX = 0 for an empty reduction (N == 0): a fill kernel rather than a
+// memset, so that the call can be captured in a graph.
+__global__ __launch_bounds__(256) void dx_zero_kernel(uint16_t *__restrict__ dx, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dx[i] = 0;
+}
+
+// dY rows padded to whole 256-row tiles, n to whole pairs of 128 steps.
+struct DxWs {
+  int Mp, Np, splits, per;
+  size_t a_bytes, e_bytes, p_bytes;
+};
+
+inline size_t round256(size_t v) { return (v + 255u) & ~(size_t)255u; }
+
+inline DxWs dx_workspace_of(const LayoutDev &L, int M) {
+  DxWs w;
+  w.Np = (L.N + 2 * DX_NT - 1) / (2 * DX_NT) * (2 * DX_NT);
+  w.Mp = (M + DX_TM - 1) / DX_TM * DX_TM;
+  w.a_bytes = round256((size_t)w.Mp * (size_t)w.Np * 2u);
+  w.e_bytes = round256((size_t)(M > 0 ? M : 1) * 4u);
+  // split n across workgroups until the tiles fill the CUs once, keeping
+  // at least 8 steps (4 pairs) per split
+  const int tiles = (w.Mp / DX_TM) * ((L.K + DX_TK - 1) / DX_TK);
+  const int nsteps = w.Np / DX_NT;
+  int sp = 1;
+  while (tiles * sp < 256 && nsteps / (2 * sp) >= 8 && sp < 16) sp *= 2;
+  w.per = ((nsteps + sp - 1) / sp + 1) & ~1;             // even
+  w.splits = (nsteps + w.per - 1) / w.per;
+  w.p_bytes = w.splits > 1 ? (size_t)w.splits * (size_t)M * (size_t)L.K * 4u : 0u;
+  return w;
+}
+
+}  // namespace
+
+bool dx_supported(const LayoutDev &L, int M) {
+  if (L.N % 8 != 0) return false;                        // dY rows in 16-byte pieces
+  const DxWs w = dx_workspace_of(L, M);
+  if (w.a_bytes >= ((size_t)1 << 31)) return false;
+  uint64_t code_bytes = 0, groups = 0;
+  for (int i = 0; i < L.nblocks; ++i) {
+    const bool b4 = (L.int4_mask[i >> 5] >> (i & 31)) & 1u;
+    code_bytes += (uint64_t)L.block_n * L.K / (b4 ? 2 : 4);
+    groups += (uint64_t)L.block_n * L.K / (b4 ? 128 : 64);
+  }
+  return code_bytes < ((uint64_t)1 << 31) && 2u * groups < ((uint64_t)1 << 31);
+}
+
+size_t dx_workspace_bytes(const LayoutDev &L, int M) {
+  if (M <= 0 || L.N == 0 || L.K == 0) return 0;
+  const DxWs w = dx_workspace_of(L, M);
+  return w.a_bytes + w.e_bytes + w.p_bytes;
+}
+
+hipError_t launch_dx(const LayoutDev &L, int M, gq_dtype act, const void *dy,
+                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *dx,
+                     void *workspace, hipStream_t s) {
+  if (L.N == 0) {
+    const size_t n = (size_t)M * (size_t)L.K;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(dx_zero_kernel, dim3(blocks < 4096 ? (unsigned)blocks : 4096u), dim3(256), 0, s,
+                       reinterpret_cast<uint16_t *>(dx), n);
+    return hipGetLastError();
+  }
+  const DxWs w = dx_workspace_of(L, M);
+  uint16_t *ya = reinterpret_cast<uint16_t *>(workspace);
+  int *rexp = reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) + w.a_bytes);
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + w.a_bytes + w.e_bytes);
+  hipError_t err = launch_prep_rows(dy, M, L.N, w.Mp, w.Np, act, ya, rexp, s);
+  if (err != hipSuccess) return err;
+  uint64_t code_bytes = 0, groups = 0;
+  for (int i = 0; i < L.nblocks; ++i) {
+    const bool b4 = (L.int4_mask[i >> 5] >> (i & 31)) & 1u;
+    code_bytes += (uint64_t)L.block_n * L.K / (b4 ? 2 : 4);
+    groups += (uint64_t)L.block_n * L.K / (b4 ? 128 : 64);
+  }
+  const int m_tiles = w.Mp / DX_TM, k_tiles = (L.K + DX_TK - 1) / DX_TK;
+  const int out_fp16 = act == GQ_FP16 ? 1 : 0;
+  uint16_t *dxp = reinterpret_cast<uint16_t *>(dx);
+  hipLaunchKernelGGL(dx_kernel, dim3(m_tiles * k_tiles, w.splits), dim3(64 * DX_NW), 0, s, L, M, w.Np,
+                     (uint32_t)w.a_bytes, m_tiles, ya, rexp, reinterpret_cast<const uint8_t *>(codes),
+                     scales, zeros, (uint32_t)code_bytes, (uint32_t)groups, dxp, out_fp16, w.per, part);
+  err = hipGetLastError();
+  if (err != hipSuccess || w.splits == 1) return err;
+  return launch_splitk_reduce(part, w.splits, M, L.K, rexp, dxp, out_fp16, s);
+}
+
+}  // namespace gq

@@ -25,18 +25,16 @@
 namespace gq {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 
 // ---------------------------------------------------------------- pre-pass
 
 // One workgroup per row of the padded activation matrix xa [Mp][Kp]: largest
-// magnitude, exponent, rescale, convert, permute.  Rows m >= M and columns
-// k >= K are written as zeros, so the GEMM reads whole tiles without masks.
-// act 0: bf16 input (rescaled), act 1: fp16 input (copied).
-template <int ACT>
+// magnitude, exponent, rescale, convert, permute (PERM).  Rows m >= M and
+// columns k >= K are written as zeros, so the GEMM reads whole tiles without
+// masks.  act 0: bf16 input (rescaled), act 1: fp16 input (copied).
+template <int ACT, bool PERM>
 __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict__ x, int M, int K,
                                                      int Kp, uint16_t *__restrict__ xa,
                                                      int *__restrict__ rexp) {
@@ -91,35 +89,24 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
         h[2 * i + 1] = (uint16_t)(w[i] >> 16);
       }
     }
-    // chunk order (0,4,1,5,2,6,3,7)
     uint4 o;
-    o.x = (uint32_t)h[0] | ((uint32_t)h[4] << 16);
-    o.y = (uint32_t)h[1] | ((uint32_t)h[5] << 16);
-    o.z = (uint32_t)h[2] | ((uint32_t)h[6] << 16);
-    o.w = (uint32_t)h[3] | ((uint32_t)h[7] << 16);
+    if (PERM) {
+      // chunk order (0,4,1,5,2,6,3,7)
+      o.x = (uint32_t)h[0] | ((uint32_t)h[4] << 16);
+      o.y = (uint32_t)h[1] | ((uint32_t)h[5] << 16);
+      o.z = (uint32_t)h[2] | ((uint32_t)h[6] << 16);
+      o.w = (uint32_t)h[3] | ((uint32_t)h[7] << 16);
+    } else {
+      o.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      o.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+      o.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
+      o.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
+    }
     *reinterpret_cast<uint4 *>(out + c) = o;
   }
 }
 
 // ------------------------------------------------------------------- GEMM
-
-// Unpack the 8 codes of one 8-k chunk into 4 packed fp16 pairs (q - z) * s,
-// pair i holding chunk elements (i, i + 4).  `t` carries the chunk's codes
-// with element i at bits [B*i, B*i + B) of its low half (elements 0..3) and
-// element 4 + i at the same bits of its high half.
-template <int B>
-__device__ __forceinline__ void unpack_chunk(uint32_t t, half2v cz, half2v s2, half8 &out) {
-  const uint32_t mask = B == 4 ? 0x000f000fu : 0x00030003u;
-  const uint32_t bias = 0x64006400u;                             // 1024.0 pairs
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t p = and_or(t >> (B * i), mask, bias);         // 1024 + q, exact
-    half2v v = __builtin_bit_cast(half2v, p);
-    v = (v + cz) * s2;                                           // (q - z) exact, then * s
-    out[2 * i] = v.x;
-    out[2 * i + 1] = v.y;
-  }
-}
 
 constexpr int KT = 128;                   // k per main-loop step
 constexpr int LDA = KT + 8;               // halfs per LDS row (conflict-free b128 reads)
@@ -240,12 +227,12 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs &g, uint16_t (*As)[32 *
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if constexpr (BITS == 4) {
-          unpack_chunk<4>(bcur[nb][t], cz[nb], s2[nb], bf[nb]);
+          unpack_f16_chunk<4>(bcur[nb][t], cz[nb], s2[nb], bf[nb]);
         } else {
           const uint32_t wv = bcur[nb][t >> 1];
           // bytes (b0, b0, b1, b1) for the low chunk, (b2, b2, b3, b3) for the high one
           const uint32_t tc = __builtin_amdgcn_perm(wv, wv, (t & 1) ? 0x03030202u : 0x01010000u);
-          unpack_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
+          unpack_f16_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
         }
       }
     };
@@ -489,11 +476,11 @@ __device__ __forceinline__ void big_wave(const BigArgs &g, uint4 *As0, uint4 *As
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if constexpr (BITS == 4) {
-          unpack_chunk<4>(bc[nb][t], cz[nb], s2[nb], bf[nb]);
+          unpack_f16_chunk<4>(bc[nb][t], cz[nb], s2[nb], bf[nb]);
         } else {
           const uint32_t wv = bc[nb][t >> 1];
           const uint32_t tc = __builtin_amdgcn_perm(wv, wv, (t & 1) ? 0x03030202u : 0x01010000u);
-          unpack_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
+          unpack_f16_chunk<2>(tc, cz[nb], s2[nb], bf[nb]);
         }
       }
     };
@@ -814,6 +801,16 @@ inline Workspace workspace_of(const LayoutDev &L, int M) {
 
 }  // namespace
 
+hipError_t launch_prep_rows(const void *x, int M, int K, int Mp, int Kp, gq_dtype act, uint16_t *xa,
+                            int *rexp, hipStream_t s) {
+  const uint16_t *xin = reinterpret_cast<const uint16_t *>(x);
+  if (act == GQ_BF16)
+    hipLaunchKernelGGL((prep_x_kernel<0, false>), dim3(Mp), dim3(256), 0, s, xin, M, K, Kp, xa, rexp);
+  else
+    hipLaunchKernelGGL((prep_x_kernel<1, false>), dim3(Mp), dim3(256), 0, s, xin, M, K, Kp, xa, rexp);
+  return hipGetLastError();
+}
+
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, const int *rexp,
                                 uint16_t *y, int out_fp16, hipStream_t s) {
   const int64_t total = (int64_t)M * N;
@@ -831,9 +828,9 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + w.a_bytes + w.e_bytes);
   const uint16_t *xin = reinterpret_cast<const uint16_t *>(x);
   if (act == GQ_BF16)
-    hipLaunchKernelGGL(prep_x_kernel<0>, dim3(w.Mp), dim3(256), 0, s, xin, M, L.K, w.Kp, xa, rexp);
+    hipLaunchKernelGGL((prep_x_kernel<0, true>), dim3(w.Mp), dim3(256), 0, s, xin, M, L.K, w.Kp, xa, rexp);
   else
-    hipLaunchKernelGGL(prep_x_kernel<1>, dim3(w.Mp), dim3(256), 0, s, xin, M, L.K, w.Kp, xa, rexp);
+    hipLaunchKernelGGL((prep_x_kernel<1, true>), dim3(w.Mp), dim3(256), 0, s, xin, M, L.K, w.Kp, xa, rexp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int out_fp16 = act == GQ_FP16 ? 1 : 0;

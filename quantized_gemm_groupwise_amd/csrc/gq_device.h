@@ -21,6 +21,13 @@ __device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off, uint32_t soff = 0) 
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ uint2 ld64(Rsrc r, uint32_t off, uint32_t soff = 0) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t ld32(Rsrc r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
 __device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
 }
@@ -49,6 +56,29 @@ __device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b) {
   const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
   a = r[0];
   b = r[1];
+}
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Unpack the 8 codes of one 8-element chunk into 4 packed fp16 pairs
+// (q - z) * s, pair i holding chunk elements (i, i + 4): the one fp16
+// rounding per weight of the MFMA matmuls.  `t` carries the chunk's codes
+// with element i at bits [B*i, B*i + B) of its low half (elements 0..3) and
+// element 4 + i at the same bits of its high half; cz = -(1024 + z) and
+// s2 = s, both as fp16 pairs.
+template <int B>
+__device__ __forceinline__ void unpack_f16_chunk(uint32_t t, half2v cz, half2v s2, half8 &out) {
+  const uint32_t mask = B == 4 ? 0x000f000fu : 0x00030003u;
+  const uint32_t bias = 0x64006400u;                             // 1024.0 pairs
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p = and_or(t >> (B * i), mask, bias);         // 1024 + q, exact
+    half2v v = __builtin_bit_cast(half2v, p);
+    v = (v + cz) * s2;                                           // (q - z) exact, then * s
+    out[2 * i] = v.x;
+    out[2 * i + 1] = v.y;
+  }
 }
 
 // LDS barrier for data written to LDS only: waits for this wave's LDS

@@ -72,10 +72,21 @@ size_t skinny_workspace_bytes(const LayoutDev &L, int M);
 hipError_t launch_skinny(const LayoutDev &L, int M, gq_dtype act, const void *x,
                          const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                          void *y, void *workspace, hipStream_t s);
+// Rows of x [M][K] (bf16 or fp16) as exact fp16 in natural order, [Mp][Kp]
+// zero padded, with the power-of-two row exponents rexp[M] of the rescale.
+hipError_t launch_prep_rows(const void *x, int M, int K, int Mp, int Kp, gq_dtype act, uint16_t *xa,
+                            int *rexp, hipStream_t s);
 // Sum split-K fp32 partials [splits][M][N] in split order, times 2^rexp[m]
 // when rexp is not null, rounded to bf16 (or fp16).
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, const int *rexp,
                                 uint16_t *y, int out_fp16, hipStream_t s);
+
+// Data gradient dX = dY . W_hat (dx.hip).  Needs N % 8 == 0.
+bool dx_supported(const LayoutDev &L, int M);
+size_t dx_workspace_bytes(const LayoutDev &L, int M);
+hipError_t launch_dx(const LayoutDev &L, int M, gq_dtype act, const void *dy,
+                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *dx,
+                     void *workspace, hipStream_t s);
 
 // MFMA tile rows per workgroup, in 32-row blocks, for a given M.
 inline int gemm_mb(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }

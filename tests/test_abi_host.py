@@ -111,6 +111,36 @@ def test_argument_errors_before_launch(lib):
     assert lib.gq_fake_quant(ctypes.byref(lay0), None, gq.GQ_BF16, None, None, None) == gq.GQ_OK
 
 
+def test_dx_argument_errors_before_launch(lib):
+    """gq_linear_dx: every refusal happens on the host, before a launch."""
+    lay = gq.make_layout(512, 256, 128, [4, 2])
+    A, bad = 0x10000, 0x10008
+    Dx = lambda M, act, dy, dx, ws, wsb: lib.gq_linear_dx(ctypes.byref(lay), M, act, dy, A, A, A, dx,
+                                                          ws, wsb, None)
+    assert Dx(-1, gq.GQ_BF16, A, A, None, 0) == gq.GQ_ERR_SHAPE
+    assert Dx(1, gq.GQ_FP32, A, A, None, 0) == gq.GQ_ERR_DTYPE
+    assert Dx(1, gq.GQ_BF16, bad, A, None, 0) == gq.GQ_ERR_ALIGNMENT
+    assert Dx(1, gq.GQ_BF16, None, A, None, 0) == gq.GQ_ERR_NULL_ARG
+    assert Dx(1, gq.GQ_BF16, A, A + 1, None, 0) == gq.GQ_ERR_ALIGNMENT
+    assert Dx(1, gq.GQ_BF16, A, None, None, 0) == gq.GQ_ERR_NULL_ARG
+    need = gq.gq_linear_dx_workspace_bytes(lay, 300)
+    # dY as fp16 padded to whole 256 x 256 tiles, plus the row exponents
+    assert need >= 512 * 256 * 2 + 300 * 4 and need % 256 == 0
+    assert Dx(300, gq.GQ_BF16, A, A, None, 0) == gq.GQ_ERR_WORKSPACE
+    assert Dx(300, gq.GQ_BF16, A, A, A, need - 1) == gq.GQ_ERR_WORKSPACE
+    assert Dx(300, gq.GQ_BF16, A, A, A + 16, need) == gq.GQ_ERR_ALIGNMENT
+    assert Dx(0, gq.GQ_BF16, None, None, None, 0) == gq.GQ_OK
+    # N % 8 != 0: refused by both calls
+    odd = gq.make_layout(512, 12, 12, [4])
+    with pytest.raises(gq.GqError):
+        gq.gq_linear_dx_workspace_bytes(odd, 4)
+    assert lib.gq_linear_dx(ctypes.byref(odd), 4, gq.GQ_BF16, A, A, A, A, A, A, 1 << 20, None) \
+        == gq.GQ_ERR_SHAPE
+    # a small tile grid splits the n range: fp32 parts in the workspace
+    wide = gq.make_layout(256, 16384, 16384, [4])
+    assert gq.gq_linear_dx_workspace_bytes(wide, 64) >= 2 * 64 * 256 * 4
+
+
 def test_workspace_sizes():
     lay = gq.make_layout(4096, 14336, 14336, [4])
     # dot-product path, and the small-batch path on a wide layer up to 16

@@ -302,6 +302,70 @@ def test_linear_exact_integer_case():
     assert np.array_equal(O.bf16_bits_to_f64(O.f64_to_bf16_bits(y)), exact)
 
 
+# ------------------------------------ data gradient dX = dY . W_hat
+
+@pytest.mark.parametrize("M,K,N,block_n,bits", [
+    (1, 128, 3, 3, [4]), (3, 128, 5, 5, [2]), (2, 256, 7, 7, [4]), (2, 256, 256, 128, [4, 2]),
+])
+def test_linear_dx_brute_force(M, K, N, block_n, bits):
+    """dX[m][k] = sum_n dY[m][n] (c - z) S in exact rational arithmetic,
+    straight from the packed fields, against the fp64 oracle; N != K keeps a
+    transposed weight from passing."""
+    rng = np.random.default_rng(M * 7 + K + N)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    p = O.quantize_pack(W, O.Layout(K, N, block_n, bits))
+    dy = S.bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    dy64 = O.bf16_bits_to_f64(dy)
+    cols = list(range(K)) if N < 8 else [0, 1, 63, 64, 127, 128, 255]
+    dx = O.linear_dx(dy, p)
+    assert dx.shape == (M, K)
+    assert np.array_equal(O.linear_dx(dy, p, cols), dx[:, cols])
+    fields = [O.block_fields(p, b) for b in range(N // block_n)]
+    for m in range(M):
+        for k in cols[:24]:
+            acc = Fraction(0)
+            for n in range(N):
+                c, sc, z, b, g = fields[n // block_n]
+                r = n % block_n
+                acc += (Fraction(float(dy64[m, n])) * (int(c[r, k]) - int(z[r, k // g]))
+                        * Fraction(float(sc[r, k // g])))
+            assert abs(Fraction(float(dx[m, k])) - acc) <= Fraction(1, 10 ** 12) * (1 + abs(acc))
+
+
+def test_linear_dx_is_the_adjoint_of_linear():
+    """<dY, x . W_hat^T> = <dY . W_hat, x> for any x: the data gradient is the
+    transpose of the forward product (Channel-mix, three blocks)."""
+    rng = np.random.default_rng(5)
+    M, K, N = 4, 256, 384
+    W = S.decode_weight(1, N=N, K=K)
+    p = O.quantize_pack(W, O.Layout(K, N, 128, [4, 2, 4]))
+    x = S.activations(M, K, 17)
+    dy = S.bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    lhs = float(np.sum(O.bf16_bits_to_f64(dy) * O.linear(x, p)))
+    rhs = float(np.sum(O.linear_dx(dy, p) * O.bf16_bits_to_f64(x)))
+    scale = float(np.sum(np.abs(O.bf16_bits_to_f64(dy)) @ np.abs(O.dequant(p).astype(np.float64))
+                         * np.abs(O.bf16_bits_to_f64(x))))
+    assert abs(lhs - rhs) <= 1e-12 * scale
+
+
+def test_linear_dx_exact_integer_case():
+    """dY in {-1, 0, 1} and weights on a 2^-6 grid: dX is an integer product
+    times 2^-6, exact in fp64 and in bf16."""
+    rng = np.random.default_rng(12)
+    M, K, N = 3, 128, 10
+    base = rng.integers(-7, 9, size=(N, K)).astype(np.float64)
+    base[:, 0] = -7
+    base[:, 1] = 8
+    W = (base * 2.0 ** -6).astype(np.float32)
+    p = O.quantize_pack(W, O.Layout(K, N, N, [4]))
+    assert np.all(p.scales.view(np.float16).astype(np.float64) == 2.0 ** -6)
+    di = rng.integers(-1, 2, size=(M, N))
+    dy = S.bf16_bits(di.astype(np.float32))
+    dx = O.linear_dx(dy, p)
+    exact = (di @ base.astype(np.int64)) * 2.0 ** -6
+    assert np.array_equal(dx, exact)
+
+
 # ------------------------------------------------------ P8 special cases
 
 def test_channel_mix_uniform_equivalence():
