@@ -43,7 +43,7 @@ constexpr int DX_TM = 32 * DX_MB;                       // 256 rows of dX
 constexpr int DX_TK = 64 * DX_NW;                       // 256 columns of dX
 constexpr int DX_TILE_BYTES = DX_TM * DX_NT * 2;        // 64 KB of dY per step
 constexpr int DX_DMA = DX_TILE_BYTES / (1024 * DX_NW);  // 1 KB LDS loads per wave per step
-constexpr int DX_WBLK = 64 * 16;                        // halfs of a wave's weight block
+constexpr int DX_WBLK = 24 * 8 * 4;                     // dwords of a wave's weight block
 constexpr uint32_t kOobDx = 0x80000000u;                // beyond every resource
 
 struct DxArgs {
@@ -58,12 +58,29 @@ struct DxArgs {
 };
 
 __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uint4 *As0, uint4 *As1,
-                                        _Float16 *Wb, Rsrc xr, Rsrc cr, Rsrc sr, Rsrc zr, int wave) {
+                                        uint32_t *Wb, Rsrc xr, Rsrc cr, Rsrc sr, Rsrc zr, int wave) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 31;
   const int h = lane >> 5;
-  // weight block lane roles: row ri of the sub-step, 16 columns at 16 cj
+  // weight block lane roles: lane (ri, cj) loads row ri of the sub-step,
+  // columns 16 cj .. 16 cj + 15.  Lanes ri and ri ^ 1 then swap halves, so
+  // that the even lane holds rows (ri, ri + 1) x columns 16 cj .. + 7 and the
+  // odd one rows (ri - 1, ri) x columns 16 cj + 8 .. + 15: column group
+  // g = 2 cj + odd of 8 columns, one dword (two rows) per column.
   const int ri = lane & 15, cj = lane >> 4;
+  const bool odd = ri & 1;
+  // Wb holds column 8g + c, rows 8hh .. 8hh + 7 (hh = half of the 16
+  // rows) in one 16-byte chunk.  The two groups 2p, 2p + 1 of a half sit
+  // side by side (16 chunks) at chunk 24 (4 hh + p) + 2 (p & 1) + 4 hh: the
+  // 16 lanes of an operand read then cover 16 consecutive chunks, and the 32
+  // lanes of a write (or paired write) cycle 32 (64) different banks.
+  const uint32_t wbase = (uint32_t)(4 * (24 * (4 * (ri >> 3) + cj) + 2 * (cj & 1) + 4 * (ri >> 3) +
+                                         8 * (odd ? 1 : 0)) + ((ri >> 1) & 3));
+  const uint32_t rbase = (uint32_t)(4 * (24 * (4 * h + (j >> 4)) + 2 * ((j >> 4) & 1) + 4 * h +
+                                         8 * ((j >> 3) & 1) + (j & 7)));
+  // partner's scale and zero join the lane's own as (row a, row b) halves
+  const uint32_t ssel = odd ? 0x01000504u : 0x05040100u;
+  const uint32_t zsel = odd ? 0x0c020c06u : 0x0c060c02u;
 
   // dY tile DMA (the forward matmul's x tile): load i (= DX_DMA * wave + p)
   // writes slots 64 i .. 64 i + 63, rows 4i .. 4i + 3; lane l -> row
@@ -90,8 +107,10 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
     int blk = st * DX_NT / L.block_n;
     return blk < L.nblocks ? blk : L.nblocks - 1;
   };
-  // codes, scale and zero point of row n0 + 8t + (ri & 7) + 64 (ri >> 3),
-  // columns k0w + 16 cj .. + 15 (8 bytes of INT4 codes or 4 of INT2)
+  // codes of row n0 + 8t + (ri & 7) + 64 (ri >> 3), columns k0w + 16 cj ..
+  // + 15 (8 bytes of INT4 codes or 4 of INT2) for the 8 sub-steps t, and the
+  // scale and zero point of that row for t = cj and t = cj + 4 only (the
+  // step spreads them to the other lanes)
   auto load_b = [&](int st, uint2 *cw, uint32_t *sv, uint32_t *zv) {
     const int blk = step_block(st);
     const BlockInfo bi = block_info(L, blk);
@@ -100,26 +119,34 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
     const uint32_t GPR = (uint32_t)(bits == 4 ? L.K / 128 : L.K / 64);
     const uint32_t gcol = (uint32_t)(g.k0w / (bits == 4 ? 128 : 64));
     const uint32_t ccol = (uint32_t)((g.k0w + 16 * cj) * bits / 8);
-    uint32_t co[8], gi[8];
+    auto row_ok = [&](int t, uint32_t &r) {
+      const int n = st * DX_NT + 8 * t + (ri & 7) + 64 * (ri >> 3);
+      r = (uint32_t)(n - blk * L.block_n);
+      return g.kact && n < g.N;
+    };
+    uint32_t co[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int n = st * DX_NT + 8 * t + (ri & 7) + 64 * (ri >> 3);
-      const bool ok = g.kact && n < g.N;
-      const uint32_t r = (uint32_t)(n - blk * L.block_n);
-      co[t] = ok ? (uint32_t)bi.code_off + r * RB + ccol : kOobDx;
-      gi[t] = ok ? (uint32_t)bi.grp_off + r * GPR + gcol : kOobDx;
+      uint32_t r;
+      co[t] = row_ok(t, r) ? (uint32_t)bi.code_off + r * RB + ccol : kOobDx;
     }
     if (bits == 4) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) cw[t] = ld64(cr, co[t]);
     } else {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) cw[t] = make_uint2(ld32(cr, co[t]), 0u);
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t v = ld32(cr, co[t]);
+        cw[t] = make_uint2(v, v);   // both halves of the row in one word
+      }
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      sv[t] = ld16(sr, gi[t] < kOobDx ? 2u * gi[t] : kOobDx);
-      zv[t] = ld8(zr, gi[t]);
+    for (int u = 0; u < 2; ++u) {
+      uint32_t r;
+      const bool ok = row_ok(cj + 4 * u, r);
+      const uint32_t gi = (uint32_t)bi.grp_off + r * GPR + gcol;
+      sv[u] = ld16(sr, ok ? 2u * gi : kOobDx);
+      zv[u] = ld8(zr, ok ? gi : kOobDx);
     }
   };
 
@@ -144,38 +171,62 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
     load_b(sn_, bn, sn, zn);
     __builtin_amdgcn_sched_barrier(0);
     const bool b4 = __builtin_amdgcn_readfirstlane(block_info(L, step_block(st)).bits) == 4;
-    // chunk c of a lane's 16 codes as unpack_f16_chunk wants it: INT4 takes
-    // word c as it is; INT2 spreads byte 2c to the low half and byte 2c + 1
-    // to the high half of the word
-    const uint32_t sel0 = b4 ? 0x03020100u : 0x01010000u;
-    const uint32_t sel1 = b4 ? 0x07060504u : 0x03030202u;
+    // the bit width enters as shift, mask and byte selectors, not a branch:
+    // two copies of the MFMA loop under a branch make the register
+    // allocator spill the accumulators.  t0 / t1 put columns 0..3 / 4..7 of
+    // the lane's group for row a in the low half and for row b in the high
+    // half (INT4: bytes 0-1 / 2-3 of the group's word; INT2: byte 0 / 1 of
+    // the even lane's, 2 / 3 of the odd lane's 16-code word).
     const uint32_t sh = b4 ? 4u : 2u;
     const uint32_t mask = b4 ? 0x000f000fu : 0x00030003u;
-    // unpack this lane's 16 weights of sub-step t and write them to the
-    // wave's block at [column][row]
-    auto make_b = [&](int t) {
-      const uint16_t zb = f32_to_f16_bits(-(1024.f + (float)zc[t]));
-      const half2v s2 = __builtin_bit_cast(half2v, sc[t] | (sc[t] << 16));
-      const half2v cz = __builtin_bit_cast(half2v, (uint32_t)zb | ((uint32_t)zb << 16));
-      const uint32_t cwd[2] = {__builtin_amdgcn_perm(bc[t].y, bc[t].x, sel0),
-                               __builtin_amdgcn_perm(bc[t].y, bc[t].x, sel1)};
+    const uint32_t sel0 = b4 ? 0x05040100u : (odd ? 0x0c060c02u : 0x0c040c00u);
+    const uint32_t sel1 = b4 ? 0x07060302u : (odd ? 0x0c070c03u : 0x0c050c01u);
+    // unpack the lane's 2 rows x 8 columns of sub-step t and write them to
+    // the wave's block, one dword (rows a, b) per column
+    // scale | zero << 16 of row ri for every sub-step: lane (ri, cj) holds
+    // sub-steps cj and cj + 4; two lane swaps copy row of lanes c to all four
+    uint32_t szb[8];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+    for (int u = 0; u < 2; ++u) {
+      uint32_t a = sc[u] | (zc[u] << 16), b = a;
+      swap16(a, b);                    // a: rows (0, 0, 2, 2), b: rows (1, 1, 3, 3)
+      uint32_t a2 = a, b2 = b;
+      swap32(a, a2);                   // a: row 0 everywhere, a2: row 2
+      swap32(b, b2);                   // b: row 1, b2: row 3
+      szb[4 * u + 0] = a;
+      szb[4 * u + 1] = b;
+      szb[4 * u + 2] = a2;
+      szb[4 * u + 3] = b2;
+    }
+    auto make_b = [&](int t) {
+      const uint2 own = bc[t];
+      // even lanes keep word x (columns 0..7) and send y, odd lanes the
+      // reverse (INT2 rows have both halves in x and y)
+      const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(
+          0, (int)(odd ? own.x : own.y), 0xB1, 0xF, 0xF, false);   // lanes l <-> l ^ 1
+      const uint32_t wa = odd ? recv : own.x;
+      const uint32_t wb = odd ? own.y : recv;
+      const uint32_t sz = szb[t];
+      const uint32_t szp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sz, 0xB1, 0xF, 0xF, false);
+      // -(1024 + z) for rows a and b: the zero bytes under an fp16 -1024
+      const half2v cz = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(szp, sz, zsel) | 0xE400E400u);
+      const half2v s2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(szp, sz, ssel));
+      const uint32_t tw[2] = {__builtin_amdgcn_perm(wb, wa, sel0), __builtin_amdgcn_perm(wb, wa, sel1)};
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // 1024 + q for elements e and e + 4 of chunk c, then (q - z) s
-          const uint32_t p = and_or(cwd[c] >> (sh * e), mask, 0x64006400u);
+          // 1024 + q of column 4c + e for rows a and b, then (q - z) s
+          const uint32_t p = and_or(tw[c] >> (sh * e), mask, 0x64006400u);
           const half2v v = (__builtin_bit_cast(half2v, p) + cz) * s2;
-          Wb[(16 * cj + 8 * c + e) * 16 + ri] = v.x;
-          Wb[(16 * cj + 8 * c + e + 4) * 16 + ri] = v.y;
+          Wb[wbase + 4 * (4 * c + e)] = __builtin_bit_cast(uint32_t, v);
         }
-      }
     };
     // B operand of lane (j, h): rows 8h .. 8h + 7 of column 32 nb + j
     auto read_b = [&](half8 *bf) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        bf[nb] = *reinterpret_cast<const half8 *>(&Wb[(32 * nb + j) * 16 + 8 * h]);
+        bf[nb] = *reinterpret_cast<const half8 *>(&Wb[rbase + 192 * nb]);
     };
     auto read_a = [&](int t, half8 *af) {
       const uint32_t slot = rb + (uint32_t)(t ^ (j & 7));
@@ -209,9 +260,9 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
         if (t < 4 && i < DX_DMA / 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // dY load
         if (t + 1 < 8) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);          // VALU
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);          // LDS write
-          if (i < DX_MB + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);          // VALU
+          if (i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);           // LDS write
+          if (i >= 4 && i < 4 + DX_MB + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
         }
       }
     }
@@ -221,7 +272,7 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
     lds_barrier();
   };
   uint2 b0[8], b1[8];
-  uint32_t s0[8], s1[8], z0[8], z1[8];
+  uint32_t s0[2], s1[2], z0[2], z1[2];
   dma_a(g.st0, As0, 0, DX_DMA);
   load_b(g.st0, b0, s0, z0);
   lds_barrier();
@@ -271,7 +322,7 @@ __global__ __launch_bounds__(64 * DX_NW, 1) void dx_kernel(
     float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint4 As0[DX_TILE_BYTES / 16];
   __shared__ __attribute__((aligned(16))) uint4 As1[DX_TILE_BYTES / 16];
-  __shared__ __attribute__((aligned(16))) _Float16 Wb[DX_NW * DX_WBLK];
+  __shared__ __attribute__((aligned(16))) uint32_t Wb[DX_NW * DX_WBLK];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // tile order: m fastest, so the workgroups on one XCD (every 8th id)
   // share one m tile of dY in that XCD's L2
