@@ -53,7 +53,8 @@ struct DxArgs {
   bool kact;               // the wave's columns lie below K
   const int *rexp;
   uint16_t *dx;            // bf16/fp16 output, or
-  float *part;             // the fp32 partial [M][K] of this split
+  float *part;             // the fp32 partial [M][K] of this split, or
+  float *tail;             // the fp32 part of a split tail tile (register order)
   int out_fp16;
 };
 
@@ -281,6 +282,18 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
     step(st + 1, As1, As0, b1, s1, z1, b0, s0, z0);
   }
 
+  if (g.tail) {
+    // part of a split tail tile: the accumulators in register order
+    // (wave, mb, nb, e, lane), 256 contiguous bytes per store
+#pragma unroll
+    for (int mb = 0; mb < DX_MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          g.tail[(((wave * DX_MB + mb) * 2 + nb) * 16 + e) * 64 + lane] = acc[mb][nb][e];
+    return;
+  }
   if (!g.kact) return;
   // lane (j, h) holds column k0w + 32 nb + j and rows 8(e/4) + 4h + e%4 of
   // each 32-row block
@@ -319,14 +332,18 @@ __global__ __launch_bounds__(64 * DX_NW, 1) void dx_kernel(
     const int *__restrict__ rexp, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, uint32_t code_bytes,
     uint32_t groups, uint16_t *__restrict__ dx, int out_fp16, int steps_per_split,
-    float *__restrict__ part) {
+    float *__restrict__ part, int tail_full, int tail_parts, int tail_per) {
   __shared__ __attribute__((aligned(16))) uint4 As0[DX_TILE_BYTES / 16];
   __shared__ __attribute__((aligned(16))) uint4 As1[DX_TILE_BYTES / 16];
   __shared__ __attribute__((aligned(16))) uint32_t Wb[DX_NW * DX_WBLK];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // tile order: m fastest, so the workgroups on one XCD (every 8th id)
-  // share one m tile of dY in that XCD's L2
-  const int tile = (int)blockIdx.x;
+  // share one m tile of dY in that XCD's L2; ids past tail_full are the
+  // parts of the split tail tiles
+  const int id = (int)blockIdx.x;
+  const bool tpart = id >= tail_full;
+  const int tile = tpart ? tail_full + (id - tail_full) / tail_parts : id;
+  const int pidx = tpart ? (id - tail_full) % tail_parts : 0;
   const int m_tile = tile % m_tiles, k_tile = tile / m_tiles;
   const int nsteps = Np / DX_NT;
   DxArgs g;
@@ -334,11 +351,17 @@ __global__ __launch_bounds__(64 * DX_NW, 1) void dx_kernel(
   g.m0 = m_tile * DX_TM;
   g.k0w = k_tile * DX_TK + wave * 64;
   g.kact = g.k0w < L.K;
-  g.st0 = (int)blockIdx.y * steps_per_split;
-  g.st1 = min(g.st0 + steps_per_split, nsteps);
+  if (tpart) {
+    g.st0 = pidx * tail_per;
+    g.st1 = min(g.st0 + tail_per, nsteps);
+  } else {
+    g.st0 = (int)blockIdx.y * steps_per_split;
+    g.st1 = min(g.st0 + steps_per_split, nsteps);
+  }
   g.rexp = rexp;
   g.dx = dx;
   g.part = gridDim.y > 1 ? part + (size_t)blockIdx.y * (size_t)M * (size_t)L.K : nullptr;
+  g.tail = tpart ? part + (size_t)(id - tail_full) * (DX_TM * DX_TK) : nullptr;
   g.out_fp16 = out_fp16;
   const Rsrc xr = make_rsrc(ya, ya_bytes);
   const Rsrc cr = make_rsrc(codes, code_bytes);
@@ -354,8 +377,15 @@ __global__ __launch_bounds__(256) void dx_zero_kernel(uint16_t *__restrict__ dx,
 }
 
 // dY rows padded to whole 256-row tiles, n to whole pairs of 128 steps.
+// Fewer tiles than CUs: the n range of every tile is split (fp32 partials
+// [splits][M][K]).  More: the tiles of an incomplete last round are cut
+// along n into `parts` pieces that run side by side (fp32 parts of those
+// tiles), one tile per CU at a time either way.
+constexpr int kDxCUs = 256;
+
 struct DxWs {
-  int Mp, Np, splits, per;
+  int Mp, Np, tiles, splits, per;
+  int full, rem, parts, tper;     // tail split
   size_t a_bytes, e_bytes, p_bytes;
 };
 
@@ -367,15 +397,31 @@ inline DxWs dx_workspace_of(const LayoutDev &L, int M) {
   w.Mp = (M + DX_TM - 1) / DX_TM * DX_TM;
   w.a_bytes = round256((size_t)w.Mp * (size_t)w.Np * 2u);
   w.e_bytes = round256((size_t)(M > 0 ? M : 1) * 4u);
-  // split n across workgroups until the tiles fill the CUs once, keeping
-  // at least 8 steps (4 pairs) per split
-  const int tiles = (w.Mp / DX_TM) * ((L.K + DX_TK - 1) / DX_TK);
+  w.tiles = (w.Mp / DX_TM) * ((L.K + DX_TK - 1) / DX_TK);
   const int nsteps = w.Np / DX_NT;
+  // split n until the tiles fill the CUs, keeping >= 8 steps per split
   int sp = 1;
-  while (tiles * sp < 256 && nsteps / (2 * sp) >= 8 && sp < 16) sp *= 2;
+  while (w.tiles * sp < kDxCUs && nsteps / (2 * sp) >= 8 && sp < 16) sp *= 2;
   w.per = ((nsteps + sp - 1) / sp + 1) & ~1;             // even
   w.splits = (nsteps + w.per - 1) / w.per;
   w.p_bytes = w.splits > 1 ? (size_t)w.splits * (size_t)M * (size_t)L.K * 4u : 0u;
+  // tail split of the last round, parts of >= 16 steps
+  w.full = w.tiles;
+  w.rem = 0;
+  w.parts = 1;
+  w.tper = nsteps;
+  if (w.splits == 1 && w.tiles > kDxCUs && w.tiles % kDxCUs) {
+    const int rem = w.tiles % kDxCUs;
+    int parts = kDxCUs / rem < 4 ? kDxCUs / rem : 4;
+    while (parts > 1 && nsteps / parts < 16) --parts;
+    if (parts > 1) {
+      w.rem = rem;
+      w.parts = parts;
+      w.full = w.tiles - rem;
+      w.tper = ((nsteps + parts - 1) / parts + 1) & ~1;
+      w.p_bytes = (size_t)rem * parts * DX_TM * DX_TK * 4u;
+    }
+  }
   return w;
 }
 
@@ -422,15 +468,19 @@ hipError_t launch_dx(const LayoutDev &L, int M, gq_dtype act, const void *dy,
     code_bytes += (uint64_t)L.block_n * L.K / (b4 ? 2 : 4);
     groups += (uint64_t)L.block_n * L.K / (b4 ? 128 : 64);
   }
-  const int m_tiles = w.Mp / DX_TM, k_tiles = (L.K + DX_TK - 1) / DX_TK;
+  const int m_tiles = w.Mp / DX_TM;
   const int out_fp16 = act == GQ_FP16 ? 1 : 0;
   uint16_t *dxp = reinterpret_cast<uint16_t *>(dx);
-  hipLaunchKernelGGL(dx_kernel, dim3(m_tiles * k_tiles, w.splits), dim3(64 * DX_NW), 0, s, L, M, w.Np,
-                     (uint32_t)w.a_bytes, m_tiles, ya, rexp, reinterpret_cast<const uint8_t *>(codes),
-                     scales, zeros, (uint32_t)code_bytes, (uint32_t)groups, dxp, out_fp16, w.per, part);
+  hipLaunchKernelGGL(dx_kernel, dim3(w.full + w.rem * w.parts, w.splits), dim3(64 * DX_NW), 0, s, L, M,
+                     w.Np, (uint32_t)w.a_bytes, m_tiles, ya, rexp,
+                     reinterpret_cast<const uint8_t *>(codes), scales, zeros, (uint32_t)code_bytes,
+                     (uint32_t)groups, dxp, out_fp16, w.per, part, w.full, w.parts, w.tper);
   err = hipGetLastError();
-  if (err != hipSuccess || w.splits == 1) return err;
-  return launch_splitk_reduce(part, w.splits, M, L.K, rexp, dxp, out_fp16, s);
+  if (err != hipSuccess) return err;
+  if (w.splits > 1) return launch_splitk_reduce(part, w.splits, M, L.K, rexp, dxp, out_fp16, s);
+  if (w.rem > 0)
+    return launch_tile_tail_reduce(part, w.parts, w.full, w.rem, m_tiles, M, L.K, rexp, dxp, out_fp16, s);
+  return hipSuccess;
 }
 
 }  // namespace gq

@@ -801,6 +801,13 @@ inline Workspace workspace_of(const LayoutDev &L, int M) {
 
 }  // namespace
 
+hipError_t launch_tile_tail_reduce(const float *tail, int parts, int full, int rem, int m_tiles, int M,
+                                   int N, const int *rexp, uint16_t *y, int out_fp16, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_tail_reduce_kernel, dim3(BIG_TILE_ELEMS / 1024, rem), dim3(256), 0, s, tail, parts,
+                     full, m_tiles, M, N, rexp, y, out_fp16);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep_rows(const void *x, int M, int K, int Mp, int Kp, gq_dtype act, uint16_t *xa,
                             int *rexp, hipStream_t s) {
   const uint16_t *xin = reinterpret_cast<const uint16_t *>(x);

@@ -76,6 +76,12 @@ hipError_t launch_skinny(const LayoutDev &L, int M, gq_dtype act, const void *x,
 // zero padded, with the power-of-two row exponents rexp[M] of the rescale.
 hipError_t launch_prep_rows(const void *x, int M, int K, int Mp, int Kp, gq_dtype act, uint16_t *xa,
                             int *rexp, hipStream_t s);
+// Sum the fp32 parts of split 256 x 256 tiles (register order of the 4-wave
+// MFMA 32x32 tile: wave, 32-row block, 32-column block, element, lane) in
+// part order, times 2^rexp[m], rounded; tail tile t is tile full + t of an
+// m-fastest tile order.
+hipError_t launch_tile_tail_reduce(const float *tail, int parts, int full, int rem, int m_tiles, int M,
+                                   int N, const int *rexp, uint16_t *y, int out_fp16, hipStream_t s);
 // Sum split-K fp32 partials [splits][M][N] in split order, times 2^rexp[m]
 // when rexp is not null, rounded to bf16 (or fp16).
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, const int *rexp,

@@ -164,6 +164,44 @@ def test_linear_dx_repeat_and_shared_workspace():
         assert np.array_equal(a, b)
 
 
+def _sampled_dx_check(W, bits, block_n, dy, dxb, ms, wins, rng, ncols=16):
+    """dX at rows ms and sampled columns of the 128-column windows wins; the
+    oracle quantizes each window alone (128 is a multiple of both group
+    sizes, so a window holds whole groups of every row)."""
+    N = W.shape[0]
+    got, want, bw = [], [], []
+    for w0 in wins:
+        c0 = 128 * w0
+        ref = O.quantize_pack(np.ascontiguousarray(W[:, c0:c0 + 128]), O.Layout(128, N, block_n, bits))
+        cols = sorted(set(rng.choice(128, ncols, replace=False).tolist()) | {0, 127})
+        want.append(O.linear_dx(dy[ms], ref, cols))
+        got.append(dxb[np.ix_(ms, [c0 + c for c in cols])])
+        bw.append(np.abs(O.dequant(ref).astype(np.float64))[:, cols])
+    want = np.concatenate(want, 1)
+    rounding = np.linalg.norm(O.bf16_bits_to_f64(O.f64_to_bf16_bits(want)) - want) / np.linalg.norm(want)
+    _say("normwise", dx_gate(np.concatenate(got, 1), want, dy[ms], np.concatenate(bw, 1)),
+         "bf16 rounding of the exact result alone", rounding)
+
+
+@pytest.mark.parametrize("N,bits", [(8192, [4]), (8192, [4, 2, 2, 2] * 16)])
+def test_linear_dx_tail_split(N, bits):
+    """M = 2048, K = 8448: 264 tiles of 256 x 256, so the last 8 (columns
+    8192..8447) are cut along n into 4 parts and summed by the tail
+    reduction."""
+    M, K = 2048, 8448
+    block_n = N if len(bits) == 1 else 128
+    W = S.decode_weight(8, N=N, K=K)
+    _say("dx tail split", M, N, K, len(bits), "blocks")
+    p = gq.quantize_pack(torch.from_numpy(W).cuda(), bits, block_n)
+    dy = grad(M, N, 71)
+    dxb = y_bits(gq.linear_dx(bf16_dev(dy), p))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(72)
+    ms = sorted(set(rng.choice(M, 24, replace=False).tolist()) | {0, M - 1})
+    wins = [0, 17, 63, 64, 65]                 # 64 and 65: the split tail tiles
+    _sampled_dx_check(W, bits, block_n, dy, dxb, ms, wins, rng)
+
+
 @pytest.mark.parametrize("j", [0, 1])
 def test_linear_dx_channel_mix_full_size(j):
     """The 70B-class MLP linears (Channel-mix INT4/INT2 blocks of 128
@@ -183,19 +221,4 @@ def test_linear_dx_channel_mix_full_size(j):
     rng = np.random.default_rng(40 + j)
     ms = sorted(set(rng.choice(M, 24, replace=False).tolist()) | {0, M - 1})
     wins = sorted(set(rng.choice(K // 128, 8, replace=False).tolist()) | {0, K // 128 - 1})
-    got, want, bw = [], [], []
-    for w0 in wins:
-        c0 = 128 * w0
-        ref = O.quantize_pack(np.ascontiguousarray(W[:, c0:c0 + 128]), O.Layout(128, N, 128, bits))
-        cols = sorted(set(rng.choice(128, 16, replace=False).tolist()) | {0, 127})
-        dref = O.linear_dx(dy[ms], ref, cols)
-        w_abs = np.abs(O.dequant(ref).astype(np.float64))[:, cols]
-        got.append(dxb[np.ix_(ms, [c0 + c for c in cols])])
-        want.append(dref)
-        bw.append(w_abs)
-    # one gate over the whole sample: the normwise error is a statistic of
-    # the bf16 output rounding and needs enough elements
-    want = np.concatenate(want, 1)
-    rounding = np.linalg.norm(O.bf16_bits_to_f64(O.f64_to_bf16_bits(want)) - want) / np.linalg.norm(want)
-    _say("normwise", dx_gate(np.concatenate(got, 1), want, dy[ms], np.concatenate(bw, 1)),
-         "bf16 rounding of the exact result alone", rounding)
+    _sampled_dx_check(W, bits, 128, dy, dxb, ms, wins, rng)
