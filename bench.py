@@ -277,8 +277,9 @@ def secondary(torch, gq, S, args):
 
 
 def channel_mix(torch, gq, S):
-    """Channel-mix M=2048 GEMM on the 70B-class MLP + quantize/pack of its fp32
-    weights (and a dense fp16 GEMM of the same shape for comparison)."""
+    """Channel-mix M=2048 GEMM on the 70B-class MLP, its data gradient dX,
+    quantize/pack and fake quantization of its fp32 weights (and a dense fp16
+    GEMM of the same shape for comparison)."""
     out = {}
     for j, (N, K) in enumerate(S.MLP70B_SHAPES):
         Wn, bits = S.channel_mix_weight(j)
@@ -334,7 +335,22 @@ def channel_mix(torch, gq, S):
             "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 3), "includes": "activation pre-pass + GEMM",
             "dense_fp16_torch_matmul_TFLOPS": round(tfd, 1),
             "frac_of_dense_fp16": round(tf / tfd, 3)}
-        del x, y, p
+        del x, y
+        # backward data gradient dX = dY . W_hat through the same packed
+        # weights, M = 2048 rows of output gradient (bf16)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(6000 + j)
+        dy = (torch.randn((M, N), generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        wsd = gq.workspace(gq.gq_linear_dx_workspace_bytes(p.layout, M), "cuda")
+        xt = GraphTimer(torch, lambda: gq.linear_dx(dy, p, out=dx, ws=wsd))
+        xt.run(10)
+        t, _ = xt.run(20)
+        tf = fl * 20 / t / 1e12
+        out[f"dx_channel_mix_M2048_mlp{j}"] = {
+            "N": N, "K": K, "ms": round(t / 20 * 1e3, 4), "TFLOPS": round(tf, 1),
+            "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 3), "includes": "gradient pre-pass + dX GEMM"}
+        del dy, dx, p
         torch.cuda.empty_cache()
     return out
 
