@@ -43,8 +43,41 @@ constexpr int DX_TM = 32 * DX_MB;                       // 256 rows of dX
 constexpr int DX_TK = 64 * DX_NW;                       // 256 columns of dX
 constexpr int DX_TILE_BYTES = DX_TM * DX_NT * 2;        // 64 KB of dY per step
 constexpr int DX_DMA = DX_TILE_BYTES / (1024 * DX_NW);  // 1 KB LDS loads per wave per step
-constexpr int DX_WBLK = 24 * 8 * 4;                     // dwords of a wave's weight block
+constexpr int DX_WBLK = 148 * 4;                        // dwords of a wave's weight block
 constexpr uint32_t kOobDx = 0x80000000u;                // beyond every resource
+
+// The INT4 mask of the layout in the lanes of two registers: lane l holds
+// word l and the number of INT4 blocks before it.  A step's block is then
+// found with two lane reads instead of a walk over the mask in the kernel
+// arguments (a chain of dependent scalar loads, ~1.5 us per step when it
+// ran twice per step on a 224-block layout).
+struct MaskLanes {
+  uint32_t word, pre;
+};
+
+__device__ __forceinline__ MaskLanes mask_lanes(const LayoutDev &L, int lane) {
+  MaskLanes ml{0u, 0u};
+#pragma unroll
+  for (int i = 0; i < GQ_MAX_BLOCKS / 32; ++i) {
+    const uint32_t m = L.int4_mask[i];
+    ml.word = lane == i ? m : ml.word;
+    ml.pre += i < lane ? (uint32_t)__builtin_popcount(m) : 0u;
+  }
+  return ml;
+}
+
+__device__ __forceinline__ BlockInfo block_of(const LayoutDev &L, const MaskLanes &ml, int blk) {
+  const int wi = blk >> 5;
+  const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)ml.word, wi);
+  const uint32_t c4 = (uint32_t)__builtin_amdgcn_readlane((int)ml.pre, wi) +
+                      (uint32_t)__builtin_popcount(word & ((1u << (blk & 31)) - 1u));
+  BlockInfo b;
+  b.bits = ((word >> (blk & 31)) & 1u) ? 4 : 2;
+  const uint64_t bk = (uint64_t)L.block_n * (uint64_t)L.K;
+  b.code_off = bk * (uint64_t)(blk + c4) / 4u;
+  b.grp_off = bk * (uint64_t)(2 * blk - (int)c4) / 128u;
+  return b;
+}
 
 struct DxArgs {
   int M, N, K, Np;
@@ -69,16 +102,17 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
   // odd one rows (ri - 1, ri) x columns 16 cj + 8 .. + 15: column group
   // g = 2 cj + odd of 8 columns, one dword (two rows) per column.
   const int ri = lane & 15, cj = lane >> 4;
+  const MaskLanes ml = mask_lanes(L, lane);
   const bool odd = ri & 1;
   // Wb holds column 8g + c, rows 8hh .. 8hh + 7 (hh = half of the 16
-  // rows) in one 16-byte chunk.  The two groups 2p, 2p + 1 of a half sit
-  // side by side (16 chunks) at chunk 24 (4 hh + p) + 2 (p & 1) + 4 hh: the
-  // 16 lanes of an operand read then cover 16 consecutive chunks, and the 32
-  // lanes of a write (or paired write) cycle 32 (64) different banks.
-  const uint32_t wbase = (uint32_t)(4 * (24 * (4 * (ri >> 3) + cj) + 2 * (cj & 1) + 4 * (ri >> 3) +
-                                         8 * (odd ? 1 : 0)) + ((ri >> 1) & 3));
-  const uint32_t rbase = (uint32_t)(4 * (24 * (4 * h + (j >> 4)) + 2 * ((j >> 4) & 1) + 4 * h +
-                                         8 * ((j >> 3) & 1) + (j & 7)));
+  // rows) in 16-byte chunk 9 (8 hh + g) + 4 hh + c.  LDS has 32 banks and
+  // serves a dword write half a wave per cycle: the 32 lanes of a half
+  // (4 groups g, both hh, 4 row pairs) then hit 32 different banks, since
+  // 9 (8 hh + g) + 4 hh = g + 4 hh (mod 8).  An operand read (8 lanes, one
+  // group, 8 columns) covers 8 consecutive chunks.
+  const uint32_t wbase = (uint32_t)(4 * (9 * (8 * (ri >> 3) + 2 * cj + (odd ? 1 : 0)) + 4 * (ri >> 3)) +
+                                    ((ri >> 1) & 3));
+  const uint32_t rbase = (uint32_t)(4 * (9 * (8 * h + (j >> 3)) + 4 * h + (j & 7)));
   // partner's scale and zero join the lane's own as (row a, row b) halves
   const uint32_t ssel = odd ? 0x01000504u : 0x05040100u;
   const uint32_t zsel = odd ? 0x0c020c06u : 0x0c060c02u;
@@ -108,88 +142,78 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
     int blk = st * DX_NT / L.block_n;
     return blk < L.nblocks ? blk : L.nblocks - 1;
   };
-  // codes of row n0 + 8t + (ri & 7) + 64 (ri >> 3), columns k0w + 16 cj ..
-  // + 15 (8 bytes of INT4 codes or 4 of INT2) for the 8 sub-steps t, and the
-  // scale and zero point of that row for t = cj and t = cj + 4 only (the
-  // step spreads them to the other lanes)
-  auto load_b = [&](int st, uint2 *cw, uint32_t *sv, uint32_t *zv) {
+
+  // Weights of a step: lane (ri, cj) loads, for each sub-step t, the codes
+  // of row n0 + 8t + (ri & 7) + 64 (ri >> 3) for columns k0w + 16 cj .. + 15,
+  // and the scale and zero point of that row for t = cj and t = cj + 4
+  // (spread to the other lanes later).  One 64-bit code load per row for
+  // both widths: INT4 takes its 16 columns (8 bytes); INT2 takes the
+  // 8-byte-aligned window holding its 4 bytes (a row is a multiple of 16
+  // bytes, so the window stays in the row), whose high dword is the one
+  // lanes with odd cj need.  (A load that differs by width would be a
+  // branch, and merging its two sides made the compiler wait for the
+  // loads.)  Offsets are computed at the top of a step; the loads issue
+  // over its first sub-steps, between the dY tile loads.
+  struct WAddr {
+    uint32_t co[8], so[2], zo[2];
+  };
+  auto waddr = [&](int st, WAddr &A) {
     const int blk = step_block(st);
-    const BlockInfo bi = block_info(L, blk);
-    const int bits = __builtin_amdgcn_readfirstlane(bi.bits);
+    const BlockInfo bi = block_of(L, ml, blk);
+    const int bits = bi.bits;
     const uint32_t RB = (uint32_t)(L.K * bits / 8);
     const uint32_t GPR = (uint32_t)(bits == 4 ? L.K / 128 : L.K / 64);
     const uint32_t gcol = (uint32_t)(g.k0w / (bits == 4 ? 128 : 64));
     const uint32_t ccol = (uint32_t)((g.k0w + 16 * cj) * bits / 8);
+    const uint32_t ccw = bits == 4 ? ccol : (ccol & ~7u);
     auto row_ok = [&](int t, uint32_t &r) {
       const int n = st * DX_NT + 8 * t + (ri & 7) + 64 * (ri >> 3);
       r = (uint32_t)(n - blk * L.block_n);
       return g.kact && n < g.N;
     };
-    uint32_t co[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       uint32_t r;
-      co[t] = row_ok(t, r) ? (uint32_t)bi.code_off + r * RB + ccol : kOobDx;
-    }
-    if (bits == 4) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) cw[t] = ld64(cr, co[t]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t v = ld32(cr, co[t]);
-        cw[t] = make_uint2(v, v);   // both halves of the row in one word
-      }
+      A.co[t] = row_ok(t, r) ? (uint32_t)bi.code_off + r * RB + ccw : kOobDx;
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t r;
       const bool ok = row_ok(cj + 4 * u, r);
       const uint32_t gi = (uint32_t)bi.grp_off + r * GPR + gcol;
-      sv[u] = ld16(sr, ok ? 2u * gi : kOobDx);
-      zv[u] = ld8(zr, ok ? gi : kOobDx);
+      A.so[u] = ok ? 2u * gi : kOobDx;
+      A.zo[u] = ok ? gi : kOobDx;
     }
   };
 
-  floatx16 acc[DX_MB][2];
-#pragma unroll
-  for (int mb = 0; mb < DX_MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
-
-  // one n step from LDS tile `cur` with weights (bc, sc, zc); starts the
-  // next step's dY DMA into `nxt` and its weight loads into (bn, sn, zn).
-  // On the last step both reload the same step, so every load stays
-  // unconditional.  The bit width enters as uniform shift, mask and byte
-  // selectors rather than a branch: two copies of the MFMA loop under a
-  // branch make the register allocator spill the accumulators.
-  auto step = [&](int st, const uint4 *cur, uint4 *nxt, const uint2 *bc, const uint32_t *sc,
-                  const uint32_t *zc, uint2 *bn, uint32_t *sn, uint32_t *zn) {
-    const int sn_ = st + 1 < g.st1 ? st + 1 : st;
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(sn_, bn, sn, zn);
-    __builtin_amdgcn_sched_barrier(0);
-    const bool b4 = __builtin_amdgcn_readfirstlane(block_info(L, step_block(st)).bits) == 4;
-    // the bit width enters as shift, mask and byte selectors, not a branch:
-    // two copies of the MFMA loop under a branch make the register
-    // allocator spill the accumulators.  t0 / t1 put columns 0..3 / 4..7 of
-    // the lane's group for row a in the low half and for row b in the high
-    // half (INT4: bytes 0-1 / 2-3 of the group's word; INT2: byte 0 / 1 of
-    // the even lane's, 2 / 3 of the odd lane's 16-code word).
-    const uint32_t sh = b4 ? 4u : 2u;
-    const uint32_t mask = b4 ? 0x000f000fu : 0x00030003u;
-    const uint32_t sel0 = b4 ? 0x05040100u : (odd ? 0x0c060c02u : 0x0c040c00u);
-    const uint32_t sel1 = b4 ? 0x07060302u : (odd ? 0x0c070c03u : 0x0c050c01u);
-    // unpack the lane's 2 rows x 8 columns of sub-step t and write them to
-    // the wave's block, one dword (rows a, b) per column
-    // scale | zero << 16 of row ri for every sub-step: lane (ri, cj) holds
-    // sub-steps cj and cj + 4; two lane swaps copy row of lanes c to all four
-    uint32_t szb[8];
+  // Per-step constants of the unpacking.  The bit width enters as shift,
+  // mask and byte selectors rather than a branch: two copies of the MFMA
+  // loop under a branch make the register allocator spill the
+  // accumulators.  sel0 / sel1 put columns 0..3 / 4..7 of the lane's group
+  // for row a in the low half and for row b in the high half (INT4: bytes
+  // 0-1 / 2-3 of the group's word; INT2: byte 0 / 1 of the even lane's,
+  // 2 / 3 of the odd lane's 16-code word).
+  struct Sel {
+    bool b4;
+    uint32_t xmask, sh, mask, sel0, sel1;
+  };
+  auto sel_of = [&](int st) {
+    Sel S;
+    S.b4 = block_of(L, ml, step_block(st)).bits == 4;
+    S.xmask = (S.b4 || !(cj & 1)) ? ~0u : 0u;   // word x holds the lane's columns 0..7
+    S.sh = S.b4 ? 4u : 2u;
+    S.mask = S.b4 ? 0x000f000fu : 0x00030003u;
+    S.sel0 = S.b4 ? 0x05040100u : (odd ? 0x0c060c02u : 0x0c040c00u);
+    S.sel1 = S.b4 ? 0x07060302u : (odd ? 0x0c070c03u : 0x0c050c01u);
+    return S;
+  };
+  // scale | zero << 16 of row ri for every sub-step: lane (ri, cj) holds
+  // sub-steps cj and cj + 4; two lane swaps copy the row of lanes c to all
+  // four
+  auto spread_sz = [&](const uint32_t *sv, const uint32_t *zv, uint32_t *szb) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      uint32_t a = sc[u] | (zc[u] << 16), b = a;
+      uint32_t a = sv[u] | (zv[u] << 16), b = a;
       swap16(a, b);                    // a: rows (0, 0, 2, 2), b: rows (1, 1, 3, 3)
       uint32_t a2 = a, b2 = b;
       swap32(a, a2);                   // a: row 0 everywhere, a2: row 2
@@ -199,87 +223,149 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
       szb[4 * u + 2] = a2;
       szb[4 * u + 3] = b2;
     }
-    auto make_b = [&](int t) {
-      const uint2 own = bc[t];
-      // even lanes keep word x (columns 0..7) and send y, odd lanes the
-      // reverse (INT2 rows have both halves in x and y)
-      const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(
-          0, (int)(odd ? own.x : own.y), 0xB1, 0xF, 0xF, false);   // lanes l <-> l ^ 1
-      const uint32_t wa = odd ? recv : own.x;
-      const uint32_t wb = odd ? own.y : recv;
-      const uint32_t sz = szb[t];
-      const uint32_t szp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sz, 0xB1, 0xF, 0xF, false);
-      // -(1024 + z) for rows a and b: the zero bytes under an fp16 -1024
-      const half2v cz = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(szp, sz, zsel) | 0xE400E400u);
-      const half2v s2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(szp, sz, ssel));
-      const uint32_t tw[2] = {__builtin_amdgcn_perm(wb, wa, sel0), __builtin_amdgcn_perm(wb, wa, sel1)};
+  };
+  // unpack the lane's 2 rows x 8 columns of one sub-step and write them to
+  // weight block wb, one dword (rows a, b) per column
+  auto make_b = [&](uint32_t *wb, const uint2 code, uint32_t sz, const Sel &S) {
+    // a select between the two loaded words written as a bit blend: as a
+    // select the compiler turns it into an indexed access and moves the
+    // code registers to scratch
+    const uint32_t ox = (code.x & S.xmask) | (code.y & ~S.xmask);
+    const uint32_t oy = S.b4 ? code.y : ox;   // INT2: all 16 columns in one word
+    // even lanes keep columns 0..7 and send 8..15, odd lanes the reverse
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(
+        0, (int)(odd ? ox : oy), 0xB1, 0xF, 0xF, false);   // lanes l <-> l ^ 1
+    const uint32_t wa = odd ? recv : ox;
+    const uint32_t wbw = odd ? oy : recv;
+    const uint32_t szp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sz, 0xB1, 0xF, 0xF, false);
+    // -(1024 + z) for rows a and b: the zero bytes under an fp16 -1024
+    const half2v cz = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(szp, sz, zsel) | 0xE400E400u);
+    const half2v s2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(szp, sz, ssel));
+    const uint32_t tw[2] = {__builtin_amdgcn_perm(wbw, wa, S.sel0), __builtin_amdgcn_perm(wbw, wa, S.sel1)};
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // 1024 + q of column 4c + e for rows a and b, then (q - z) s
-          const uint32_t p = and_or(tw[c] >> (sh * e), mask, 0x64006400u);
-          const half2v v = (__builtin_bit_cast(half2v, p) + cz) * s2;
-          Wb[wbase + 4 * (4 * c + e)] = __builtin_bit_cast(uint32_t, v);
-        }
-    };
-    // B operand of lane (j, h): rows 8h .. 8h + 7 of column 32 nb + j
-    auto read_b = [&](half8 *bf) {
+      for (int e = 0; e < 4; ++e) {
+        // 1024 + q of column 4c + e for rows a and b, then (q - z) s
+        const uint32_t p = and_or(tw[c] >> (S.sh * e), S.mask, 0x64006400u);
+        const half2v v = (__builtin_bit_cast(half2v, p) + cz) * s2;
+        wb[wbase + 4 * (4 * c + e)] = __builtin_bit_cast(uint32_t, v);
+      }
+  };
+  // B operand of lane (j, h): rows 8h .. 8h + 7 of column 32 nb + j
+  auto read_b = [&](const uint32_t *wb, half8 *bf) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        bf[nb] = *reinterpret_cast<const half8 *>(&Wb[rbase + 192 * nb]);
-    };
-    auto read_a = [&](int t, half8 *af) {
-      const uint32_t slot = rb + (uint32_t)(t ^ (j & 7));
+    for (int nb = 0; nb < 2; ++nb) bf[nb] = *reinterpret_cast<const half8 *>(&wb[rbase + 144 * nb]);
+  };
+  auto read_a = [&](const uint4 *tile, int t, half8 *af) {
+    const uint32_t slot = rb + (uint32_t)(t ^ (j & 7));
 #pragma unroll
-      for (int mb = 0; mb < DX_MB; ++mb) af[mb] = __builtin_bit_cast(half8, cur[mb * 512 + slot]);
-    };
-    half8 af[2][DX_MB], bf[2][2];
-    make_b(0);
-    read_b(bf[0]);
-    read_a(0, af[0]);
+    for (int mb = 0; mb < DX_MB; ++mb) af[mb] = __builtin_bit_cast(half8, tile[mb * 512 + slot]);
+  };
+  uint32_t *const Wb0 = Wb, *const Wb1 = Wb + DX_WBLK;
+
+  floatx16 acc[DX_MB][2];
+#pragma unroll
+  for (int mb = 0; mb < DX_MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
+  half8 af[2][DX_MB], bf[2][2];
+
+  // One n step from dY tile `cur`, with the step's codes bc and spread
+  // scales szc.  Sub-step t multiplies operands read during sub-step t - 1,
+  // reads those of t + 1 and unpacks the weights of t + 2 into the block
+  // that sub-step t emptied (two blocks, alternating).  The step also
+  // loads the next step's dY tile into `nxt` and its weights into (bn, sn,
+  // zn); sub-steps 6 and 7 unpack the next step's first two sub-steps, and
+  // the barrier that makes `nxt` visible sits before sub-step 7, which reads
+  // the next step's first dY operands.  On the last step the "next" step is
+  // the same step again, so every load stays unconditional.
+  auto step = [&](int st, const uint4 *cur, uint4 *nxt, const uint2 *bc, const uint32_t *szc,
+                  uint2 *bn, uint32_t *sn, uint32_t *zn, uint32_t *szn) {
+    const int sn_ = st + 1 < g.st1 ? st + 1 : st;
+    WAddr A;
+    waddr(sn_, A);
+    const Sel Sc = sel_of(st), Sn = sel_of(sn_);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int c = t & 1, n = c ^ 1;
-      // the next tile's dY, a quarter of the loads per sub-step over the
-      // first four
-      if (t < 4) dma_a(sn_, nxt, (DX_DMA / 4) * t, DX_DMA / 4);
-      if (t + 1 < 8) {
-        make_b(t + 1);
-        read_b(bf[n]);
-        read_a(t + 1, af[n]);
+      if (t == 7) {
+        __builtin_amdgcn_sched_barrier(0);
+        // every wave's part of the next dY tile has landed, and no wave
+        // reads `cur` any more
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // loads: the next dY tile over sub-steps 0..3, the next weights'
+      // scales and zero points with sub-step 0 and codes with 1 and 2
+      if (t < 4) dma_a(sn_, nxt, (DX_DMA / 4) * t, DX_DMA / 4);
+      if (t == 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          sn[u] = ld16(sr, A.so[u]);
+          zn[u] = ld8(zr, A.zo[u]);
+        }
+      }
+      if (t == 1 || t == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bn[4 * (t - 1) + q] = ld64(cr, A.co[4 * (t - 1) + q]);
+      }
+      if (t == 5) spread_sz(sn, zn, szn);
+      // operands of sub-step t + 1 (of the next step's sub-step 0 at t = 7)
+      read_b(n ? Wb1 : Wb0, bf[n]);
+      read_a(t < 7 ? cur : nxt, (t + 1) & 7, af[n]);
+      // weights of sub-step t + 2 into the block sub-step t used
+      if (t < 6)
+        make_b(c ? Wb1 : Wb0, bc[t + 2], szc[t + 2], Sc);
+      else
+        make_b(c ? Wb1 : Wb0, bn[t - 6], szn[t - 6], Sn);
 #pragma unroll
       for (int mb = 0; mb < DX_MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][mb], bf[c][nb], acc[mb][nb], 0, 0, 0);
-      // one wave per SIMD: the next sub-step's unpacking, its LDS exchange
-      // and operand reads issue between this sub-step's MFMAs
+      // one wave per SIMD: the loads, operand reads, unpacking and weight
+      // writes of this sub-step issue between its MFMAs
+      const int nvm = t == 0 ? DX_DMA / 4 + 4 : (t < 3 ? DX_DMA / 4 + 4 : (t == 3 ? DX_DMA / 4 : 0));
 #pragma unroll
       for (int i = 0; i < 2 * DX_MB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
-        if (t < 4 && i < DX_DMA / 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // dY load
-        if (t + 1 < 8) {
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);          // VALU
-          if (i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);           // LDS write
-          if (i >= 4 && i < 4 + DX_MB + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+        if (i < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // global load
+        if (i < DX_MB + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // operand read
+        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);           // VALU
+        if (i >= 2 && i < 10) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // weight write
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // the next tile's DMA has landed in every wave's part once all waves
-    // pass this barrier
-    lds_barrier();
   };
+
   uint2 b0[8], b1[8];
-  uint32_t s0[2], s1[2], z0[2], z1[2];
-  dma_a(g.st0, As0, 0, DX_DMA);
-  load_b(g.st0, b0, s0, z0);
-  lds_barrier();
+  uint32_t s0[2], s1[2], z0[2], z1[2], szA[8], szB[8];
+  {
+    // first step: its dY tile, weights and the first two weight blocks
+    WAddr A;
+    waddr(g.st0, A);
+    dma_a(g.st0, As0, 0, DX_DMA);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) b0[t] = ld64(cr, A.co[t]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s0[u] = ld16(sr, A.so[u]);
+      z0[u] = ld8(zr, A.zo[u]);
+    }
+    lds_barrier();
+    const Sel S0 = sel_of(g.st0);
+    spread_sz(s0, z0, szA);
+    make_b(Wb0, b0[0], szA[0], S0);
+    make_b(Wb1, b0[1], szA[1], S0);
+    read_b(Wb0, bf[0]);
+    read_a(As0, 0, af[0]);
+  }
   for (int st = g.st0; st < g.st1; st += 2) {
-    step(st, As0, As1, b0, s0, z0, b1, s1, z1);
-    step(st + 1, As1, As0, b1, s1, z1, b0, s0, z0);
+    step(st, As0, As1, b0, szA, b1, s1, z1, szB);
+    step(st + 1, As1, As0, b1, szB, b0, s0, z0, szA);
   }
 
   if (g.tail) {
@@ -335,7 +421,7 @@ __global__ __launch_bounds__(64 * DX_NW, 1) void dx_kernel(
     float *__restrict__ part, int tail_full, int tail_parts, int tail_per) {
   __shared__ __attribute__((aligned(16))) uint4 As0[DX_TILE_BYTES / 16];
   __shared__ __attribute__((aligned(16))) uint4 As1[DX_TILE_BYTES / 16];
-  __shared__ __attribute__((aligned(16))) uint32_t Wb[DX_NW * DX_WBLK];
+  __shared__ __attribute__((aligned(16))) uint32_t Wb[DX_NW * 2 * DX_WBLK];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // tile order: m fastest, so the workgroups on one XCD (every 8th id)
   // share one m tile of dY in that XCD's L2; ids past tail_full are the
@@ -367,7 +453,7 @@ __global__ __launch_bounds__(64 * DX_NW, 1) void dx_kernel(
   const Rsrc cr = make_rsrc(codes, code_bytes);
   const Rsrc sr = make_rsrc(scales, 2u * groups);
   const Rsrc zr = make_rsrc(zeros, groups);
-  dx_wave(L, g, As0, As1, Wb + wave * DX_WBLK, xr, cr, sr, zr, wave);
+  dx_wave(L, g, As0, As1, Wb + wave * 2 * DX_WBLK, xr, cr, sr, zr, wave);
 }
 
 // dX = 0 for an empty reduction (N == 0): a fill kernel rather than a
