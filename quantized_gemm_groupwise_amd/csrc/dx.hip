@@ -291,6 +291,10 @@ __device__ __forceinline__ void dx_wave(const LayoutDev &L, const DxArgs &g, uin
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int c = t & 1, n = c ^ 1;
+      // one scheduling region per sub-step: without it the scheduler sinks
+      // the operand reads of sub-step t + 1 to just before their MFMAs,
+      // behind this sub-step's weight writes, and waits for them there
+      __builtin_amdgcn_sched_barrier(0);
       if (t == 7) {
         __builtin_amdgcn_sched_barrier(0);
         // every wave's part of the next dY tile has landed, and no wave
