@@ -310,6 +310,56 @@ def linear_dx(dy_bf16, p: Packed, cols=None) -> np.ndarray:
     return dy @ w
 
 
+# ------------------------------------------------- KV-cache attention
+
+def kv_cache_pack(kv, bits: int) -> Packed:
+    """Quantize a key or value cache for the decode attention: kv is fp32
+    [tokens][kv_heads * head_dim]; each token row is quantized group-wise
+    along its features exactly as a weight row ([SV] KV-cache bullet: the
+    cache is compressed with the same INT4 / INT2 formats), i.e. one
+    uniform layout whose "output channels" are tokens."""
+    kv = np.asarray(kv, dtype=np.float32)
+    return quantize_pack(kv, Layout(kv.shape[1], kv.shape[0], max(1, kv.shape[0]), [bits]))
+
+
+def kv_decode_attention(q_bf16, k_packed, v_packed, k_window_bf16, v_window_bf16,
+                        batch: int, q_heads: int, kv_heads: int, head_dim: int) -> np.ndarray:
+    """One decode step of attention over a group-wise quantized KV cache, in
+    fp64 ([SV] KV-cache bullet and its techniques: the cache is stored at low
+    bit width and dequantized for attention; the newest tokens stay in full
+    precision in a window and are not quantized).
+
+    q_bf16: uint16 bf16 bits [batch][q_heads][head_dim].
+    k_packed / v_packed: Packed caches of batch * t_packed token rows (the
+      rows of sequence b are rows b * t_packed ..), or None when t_packed = 0.
+    k_window_bf16 / v_window_bf16: uint16 bf16 bits
+      [batch][t_window][kv_heads][head_dim] (t_window may be 0).
+    Query head h attends with key/value head h // (q_heads // kv_heads);
+    scores are q . k / sqrt(head_dim) over the packed tokens followed by the
+    window tokens; softmax; the output is the probability-weighted sum of the
+    values.  Returns fp64 [batch][q_heads][head_dim]."""
+    G = q_heads // kv_heads
+    q = bf16_bits_to_f64(q_bf16).reshape(batch, q_heads, head_dim)
+    kw = bf16_bits_to_f64(k_window_bf16).reshape(batch, -1, kv_heads, head_dim)
+    vw = bf16_bits_to_f64(v_window_bf16).reshape(batch, -1, kv_heads, head_dim)
+    if k_packed is not None:
+        tp = k_packed.layout.N // batch
+        kp = dequant(k_packed).astype(np.float64).reshape(batch, tp, kv_heads, head_dim)
+        vp = dequant(v_packed).astype(np.float64).reshape(batch, tp, kv_heads, head_dim)
+        keys = np.concatenate([kp, kw], axis=1)
+        vals = np.concatenate([vp, vw], axis=1)
+    else:
+        keys, vals = kw, vw
+    out = np.zeros((batch, q_heads, head_dim))
+    for b in range(batch):
+        for h in range(q_heads):
+            kh = h // G
+            s = keys[b, :, kh, :] @ q[b, h] / np.sqrt(head_dim)
+            e = np.exp(s - s.max())
+            out[b, h] = (e / e.sum()) @ vals[b, :, kh, :]
+    return out
+
+
 def f64_to_bf16_bits(a) -> np.ndarray:
     """Round fp64 values to bf16 (8 significant bits), nearest-even, with
     bf16 subnormals and overflow to infinity; returns uint16 bit patterns."""

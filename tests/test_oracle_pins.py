@@ -366,6 +366,96 @@ def test_linear_dx_exact_integer_case():
     assert np.array_equal(dx, exact)
 
 
+# ------------------------------------- KV-cache decode attention
+
+def _kv_case(rng, B, Hq, Hkv, D, tp, tw, bits, scale=1.0):
+    q = S.bf16_bits((rng.standard_normal((B, Hq, D)) * scale).astype(np.float32))
+    k = (rng.standard_normal((B * tp, Hkv * D)) * scale).astype(np.float32)
+    v = rng.standard_normal((B * tp, Hkv * D)).astype(np.float32)
+    kp = O.kv_cache_pack(k, bits) if tp else None
+    vp = O.kv_cache_pack(v, bits) if tp else None
+    kw = S.bf16_bits((rng.standard_normal((B, tw, Hkv, D)) * scale).astype(np.float32))
+    vw = S.bf16_bits(rng.standard_normal((B, tw, Hkv, D)).astype(np.float32))
+    return q, kp, vp, kw, vw
+
+
+def test_kv_attention_uniform_scores_give_the_mean():
+    """q = 0: every score is 0, softmax is uniform, the output is the plain
+    mean of the (dequantized and window) values over all tokens."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, D, tp, tw = 2, 4, 2, 128, 5, 3
+    _, kp, vp, kw, vw = _kv_case(rng, B, Hq, Hkv, D, tp, tw, 4)
+    q = np.zeros((B, Hq, D), dtype=np.uint16)
+    out = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, D)
+    vals = np.concatenate([O.dequant(vp).astype(np.float64).reshape(B, tp, Hkv, D),
+                           O.bf16_bits_to_f64(vw).reshape(B, tw, Hkv, D)], axis=1)
+    for b in range(B):
+        for h in range(Hq):
+            want = sum(vals[b, t, h // 2] for t in range(tp + tw)) / (tp + tw)
+            assert np.allclose(out[b, h], want, rtol=0, atol=1e-12)
+
+
+def test_kv_attention_one_dominant_token():
+    """A key aligned with q far above the others takes all the weight: the
+    output is that token's value (the others weigh below e^-60)."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, D, tp, tw = 1, 2, 1, 128, 9, 2
+    q, kp, vp, kw, vw = _kv_case(rng, B, Hq, Hkv, D, tp, tw, 4, scale=0.05)
+    qv = np.zeros((B, Hq, D), dtype=np.float32)
+    qv[0, :, 0] = 64.0
+    q = S.bf16_bits(qv)
+    kwv = O.bf16_bits_to_f64(kw).astype(np.float32).copy()
+    kwv[0, 1, 0, 0] = 256.0          # window token 1: score 64*256/sqrt(128) ~ 1448
+    kw = S.bf16_bits(kwv)
+    out = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, D)
+    want = O.bf16_bits_to_f64(vw)[0, 1, 0]
+    for h in range(Hq):
+        assert np.allclose(out[0, h], want, rtol=0, atol=1e-12)
+
+
+def test_kv_attention_matches_torch_sdpa():
+    """Against torch's scaled_dot_product_attention in float64 on the same
+    dequantized keys and values (key/value heads repeated for the query heads
+    they serve), INT4 and INT2, packed part and window."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(23)
+    for bits, (B, Hq, Hkv, tp, tw) in [(4, (2, 8, 2, 40, 7)), (2, (1, 4, 4, 65, 0)), (4, (1, 6, 3, 0, 5))]:
+        D = 128
+        q, kp, vp, kw, vw = _kv_case(rng, B, Hq, Hkv, D, tp, tw, bits)
+        out = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, D)
+        keys = [O.bf16_bits_to_f64(kw).reshape(B, tw, Hkv, D)]
+        vals = [O.bf16_bits_to_f64(vw).reshape(B, tw, Hkv, D)]
+        if tp:
+            keys.insert(0, O.dequant(kp).astype(np.float64).reshape(B, tp, Hkv, D))
+            vals.insert(0, O.dequant(vp).astype(np.float64).reshape(B, tp, Hkv, D))
+        K = torch.from_numpy(np.concatenate(keys, 1)).permute(0, 2, 1, 3)   # B, Hkv, T, D
+        V = torch.from_numpy(np.concatenate(vals, 1)).permute(0, 2, 1, 3)
+        K = K.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        V = V.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        Q = torch.from_numpy(O.bf16_bits_to_f64(q)).reshape(B, Hq, 1, D)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V).reshape(B, Hq, D).numpy()
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_kv_attention_head_mapping():
+    """Values constant per key/value head: query head h must return the
+    constant of head h // (q_heads / kv_heads) whatever the scores are."""
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, D, tp, tw = 1, 8, 2, 128, 6, 2
+    q, kp, _, kw, _ = _kv_case(rng, B, Hq, Hkv, D, tp, tw, 4)
+    v = np.zeros((tp, Hkv * D), dtype=np.float32)
+    v[:, :D] = 3.0
+    v[:, D:] = -5.0
+    vp = O.kv_cache_pack(v, 4)
+    vwv = np.zeros((B, tw, Hkv, D), dtype=np.float32)
+    vwv[:, :, 0] = 3.0
+    vwv[:, :, 1] = -5.0
+    out = O.kv_decode_attention(q, kp, vp, kw, S.bf16_bits(vwv), B, Hq, Hkv, D)
+    assert np.allclose(O.dequant(vp)[:, :D], 3.0) and np.allclose(O.dequant(vp)[:, D:], -5.0)
+    for h in range(Hq):
+        assert np.allclose(out[0, h], 3.0 if h < 4 else -5.0, rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------ P8 special cases
 
 def test_channel_mix_uniform_equivalence():
