@@ -199,6 +199,54 @@ gq_status gq_linear_dx(const gq_layout *layout, int32_t M, gq_dtype act, const v
                        const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                        void *dx, void *workspace, size_t workspace_bytes, void *stream);
 
+/* A group-wise quantized KV cache for one decode step of attention (the
+ * review of "A Survey of Low-bit Large Language Models": KV-cache
+ * compression with low-bit formats, a quantization window that keeps the
+ * newest tokens unquantized).  `batch` sequences of equal length; per
+ * sequence t_packed packed tokens followed by t_window dense tokens.
+ *   Packed part: the output of gq_quantize_pack for the fp32 cache
+ *   [batch * t_packed][kv_heads * head_dim] with one uniform layout
+ *   {K = kv_heads * head_dim, N = batch * t_packed, block_n = N, bits}:
+ *   one row per token (sequence b's rows are b * t_packed ..), groups of 128
+ *   (INT4) or 64 (INT2) features.  DEVICE pointers, 16-byte aligned codes.
+ *   Window: DEVICE bf16 [batch][t_window][kv_heads][head_dim], 16-byte
+ *   aligned (may be NULL when t_window is 0).
+ * Rules: head_dim = 128; q_heads / kv_heads in {1, 2, 4, 8};
+ * t_packed + t_window >= 1; t_window <= 1024; packed code bytes < 2 GiB. */
+typedef struct gq_kv_cache {
+  int32_t batch;
+  int32_t q_heads;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t bits;
+  int32_t t_packed;
+  int32_t t_window;
+  const uint32_t *k_codes;
+  const uint16_t *k_scales;
+  const uint8_t *k_zeros;
+  const uint32_t *v_codes;
+  const uint16_t *v_scales;
+  const uint8_t *v_zeros;
+  const void *k_window;
+  const void *v_window;
+} gq_kv_cache;
+
+/* Workspace gq_kv_attention needs (HOST output *bytes).  Pure host. */
+gq_status gq_kv_attention_workspace_bytes(const gq_kv_cache *cache, size_t *bytes);
+
+/* One decode step: for every sequence b and query head h (key/value head
+ * h / (q_heads / kv_heads)), out = softmax(q . K^T / sqrt(head_dim)) . V over
+ * the packed tokens (dequantized: (code - z) * S) and the window tokens.
+ *   q    DEVICE bf16 [batch][q_heads][head_dim], 16-byte aligned.
+ *   out  DEVICE bf16 [batch][q_heads][head_dim], written (round to nearest
+ *        even of an fp32 result).
+ *   workspace  DEVICE, 256-byte aligned, >= the workspace size; overwritten.
+ * q . K^T multiplies exact fp16 forms (q rescaled per head by a power of
+ * two, codes as 1024 + c, the zero point as -(1024 + z)) with fp32
+ * accumulation; softmax and P . V run in fp32.  Deterministic. */
+gq_status gq_kv_attention(const gq_kv_cache *cache, const void *q, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *gq_status_string(gq_status status);
 

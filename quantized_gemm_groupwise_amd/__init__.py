@@ -33,7 +33,7 @@ GROUP = {4: 128, 2: 64}
 # Every symbol include/gq.h declares.
 EXPORTS = ("gq_packed_bytes", "gq_quantize_pack", "gq_fake_quant", "gq_dequant",
            "gq_linear_workspace_bytes", "gq_linear", "gq_linear_dx_workspace_bytes",
-           "gq_linear_dx", "gq_status_string")
+           "gq_linear_dx", "gq_kv_attention_workspace_bytes", "gq_kv_attention", "gq_status_string")
 
 
 class GqError(RuntimeError):
@@ -45,6 +45,15 @@ class GqError(RuntimeError):
 class gq_layout(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("bits", ctypes.POINTER(ctypes.c_uint8))]
+
+
+class gq_kv_cache(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32), ("t_packed", ctypes.c_int32),
+                ("t_window", ctypes.c_int32),
+                ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("k_zeros", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p), ("v_zeros", ctypes.c_void_p),
+                ("k_window", ctypes.c_void_p), ("v_window", ctypes.c_void_p)]
 
 
 _lib = None
@@ -70,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gq_linear": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
         "gq_linear_dx_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
         "gq_linear_dx": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
+        "gq_kv_attention_workspace_bytes": ([P(gq_kv_cache), P(S)], ctypes.c_int),
+        "gq_kv_attention": ([P(gq_kv_cache), VP, VP, VP, S, VP], ctypes.c_int),
         "gq_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -154,6 +165,19 @@ def gq_linear_dx(layout, M, act, dy_ptr, codes_ptr, scales_ptr, zeros_ptr, dx_pt
     return load_library().gq_linear_dx(ctypes.byref(layout), int(M), int(act), dy_ptr, codes_ptr,
                                        scales_ptr, zeros_ptr, dx_ptr, ws_ptr, int(ws_bytes),
                                        _stream(stream))
+
+
+def gq_kv_attention_workspace_bytes(cache: gq_kv_cache) -> int:
+    b = ctypes.c_size_t()
+    st = load_library().gq_kv_attention_workspace_bytes(ctypes.byref(cache), ctypes.byref(b))
+    if st != GQ_OK:
+        raise GqError(st, "gq_kv_attention_workspace_bytes")
+    return b.value
+
+
+def gq_kv_attention(cache: gq_kv_cache, q_ptr, out_ptr, ws_ptr, ws_bytes, stream=None) -> int:
+    return load_library().gq_kv_attention(ctypes.byref(cache), q_ptr, out_ptr, ws_ptr, int(ws_bytes),
+                                          _stream(stream))
 
 
 # ------------------------------------------------------ tensor-level API
@@ -311,3 +335,42 @@ def linear_dx(dy: torch.Tensor, p: Packed, out: torch.Tensor | None = None,
     _check(gq_linear_dx(p.layout, M, act, dy.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
                         p.zeros.data_ptr(), dx.data_ptr(), wptr, wbytes, stream), "gq_linear_dx")
     return dx
+
+
+def kv_cache(batch: int, q_heads: int, kv_heads: int, k: "Packed | None", v: "Packed | None",
+             k_window: torch.Tensor | None = None, v_window: torch.Tensor | None = None) -> gq_kv_cache:
+    """Describe a KV cache: k / v are packed caches (quantize_pack of the fp32
+    cache [batch * t_packed][kv_heads * 128], one row per token) or None;
+    k_window / v_window are bf16 [batch][t_window][kv_heads][128] or None."""
+    tp = 0 if k is None else k.N // batch
+    tw = 0 if k_window is None else k_window.shape[1]
+    bits = 4
+    if k is not None:
+        bits = int(k.bits[0])
+    c = gq_kv_cache(batch, q_heads, kv_heads, 128, bits, tp, tw,
+                    k.codes.data_ptr() if k is not None else None,
+                    k.scales.data_ptr() if k is not None else None,
+                    k.zeros.data_ptr() if k is not None else None,
+                    v.codes.data_ptr() if v is not None else None,
+                    v.scales.data_ptr() if v is not None else None,
+                    v.zeros.data_ptr() if v is not None else None,
+                    k_window.data_ptr() if k_window is not None else None,
+                    v_window.data_ptr() if v_window is not None else None)
+    c._keep = (k, v, k_window, v_window)
+    return c
+
+
+def kv_attention(q: torch.Tensor, cache: gq_kv_cache, out: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step of attention of bf16 q [batch][q_heads][128] over the
+    cache; returns bf16 [batch][q_heads][128]."""
+    _cuda(q, "q")
+    if q.dtype != torch.bfloat16 or tuple(q.shape) != (cache.batch, cache.q_heads, 128):
+        raise ValueError("q must be bf16 [batch][q_heads][128]")
+    o = torch.empty_like(q) if out is None else out
+    need = gq_kv_attention_workspace_bytes(cache)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(gq_kv_attention(cache, q.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(), stream),
+           "gq_kv_attention")
+    return o

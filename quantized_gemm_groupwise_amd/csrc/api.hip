@@ -165,6 +165,40 @@ gq_status gq_linear_dx(const gq_layout *layout, int32_t M, gq_dtype act, const v
   return launched(launch_dx(L, M, act, dy, codes, scales, zeros, dx, workspace, s), s);
 }
 
+gq_status gq_kv_attention_workspace_bytes(const gq_kv_cache *cache, size_t *bytes) {
+  if (!cache || !bytes) return GQ_ERR_NULL_ARG;
+  const gq_status st = kv_check(*cache);
+  if (st != GQ_OK) return st;
+  *bytes = kv_workspace_bytes(*cache);
+  return GQ_OK;
+}
+
+gq_status gq_kv_attention(const gq_kv_cache *cache, const void *q, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (!cache) return GQ_ERR_NULL_ARG;
+  gq_status st = kv_check(*cache);
+  if (st != GQ_OK) return st;
+  const gq_kv_cache &c = *cache;
+  if ((st = check_ptr16(q)) != GQ_OK) return st;
+  if (!out) return GQ_ERR_NULL_ARG;
+  if ((uintptr_t)out & 1u) return GQ_ERR_ALIGNMENT;
+  if (c.t_packed > 0) {
+    if ((st = check_ptr16(c.k_codes)) != GQ_OK) return st;
+    if ((st = check_ptr16(c.v_codes)) != GQ_OK) return st;
+    if (!c.k_scales || !c.k_zeros || !c.v_scales || !c.v_zeros) return GQ_ERR_NULL_ARG;
+    if (((uintptr_t)c.k_scales & 1u) || ((uintptr_t)c.v_scales & 1u)) return GQ_ERR_ALIGNMENT;
+  }
+  if (c.t_window > 0) {
+    if ((st = check_ptr16(c.k_window)) != GQ_OK) return st;
+    if ((st = check_ptr16(c.v_window)) != GQ_OK) return st;
+  }
+  const size_t need = kv_workspace_bytes(c);
+  if (!workspace || workspace_bytes < need) return GQ_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 255u) return GQ_ERR_ALIGNMENT;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launched(launch_kv(c, q, out, workspace, s), s);
+}
+
 const char *gq_status_string(gq_status status) {
   switch (status) {
     case GQ_OK: return "GQ_OK: success";

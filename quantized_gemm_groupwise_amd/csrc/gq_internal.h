@@ -94,6 +94,11 @@ hipError_t launch_dx(const LayoutDev &L, int M, gq_dtype act, const void *dy,
                      const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *dx,
                      void *workspace, hipStream_t s);
 
+// Decode attention over a quantized KV cache (kv.hip).
+gq_status kv_check(const gq_kv_cache &c);
+size_t kv_workspace_bytes(const gq_kv_cache &c);
+hipError_t launch_kv(const gq_kv_cache &c, const void *q, void *out, void *workspace, hipStream_t s);
+
 // MFMA tile rows per workgroup, in 32-row blocks, for a given M.
 inline int gemm_mb(int M) { return M <= 32 ? 1 : (M <= 64 ? 2 : 4); }
 // Workspace of the MFMA path: fp16 activations, row exponents, split-K partials.

@@ -1,0 +1,154 @@
+"""GPU parity of the decode attention over a group-wise quantized KV cache
+(gq_kv_attention) against the fp64 oracle (oracle.kv_decode_attention) on
+the same seeded inputs; the packed caches come from the oracle's packing
+(byte-identical to gq_quantize_pack) uploaded to the device.
+
+Bar: normwise relative error <= 2e-3 over the output against the fp64
+oracle, and elementwise |out - ref| <= 2^-8 |ref| + 2e-3 max|v|
+(bf16 output rounding; scores are computed from exact fp16 forms with fp32
+accumulation, softmax and P . V in fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth as S
+
+pytestmark = pytest.mark.gpu
+
+gq = pytest.importorskip("quantized_gemm_groupwise_amd")
+from tests.gpu_util import bf16_dev, upload_packed, y_bits  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gq.load_library()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def kv_inputs(seed, B, Hq, Hkv, tp, tw, bits, kscale=1.0):
+    """Synthetic decode-step inputs: q and keys Gaussian (keys times kscale,
+    which sets how peaked the softmax is), values Gaussian; fp32 caches
+    quantized by the oracle, the window rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    D = 128
+    q = S.bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    k = (rng.standard_normal((B * tp, Hkv * D)) * kscale).astype(np.float32)
+    v = rng.standard_normal((B * tp, Hkv * D)).astype(np.float32)
+    kp = O.kv_cache_pack(k, bits) if tp else None
+    vp = O.kv_cache_pack(v, bits) if tp else None
+    kw = S.bf16_bits((rng.standard_normal((B, tw, Hkv, D)) * kscale).astype(np.float32))
+    vw = S.bf16_bits(rng.standard_normal((B, tw, Hkv, D)).astype(np.float32))
+    return q, kp, vp, kw, vw
+
+
+def run_gpu(q, kp, vp, kw, vw, B, Hq, Hkv):
+    kd = upload_packed(kp) if kp is not None else None
+    vd = upload_packed(vp) if vp is not None else None
+    tw = kw.shape[1]
+    kwd = bf16_dev(np.ascontiguousarray(kw)) if tw else None
+    vwd = bf16_dev(np.ascontiguousarray(vw)) if tw else None
+    cache = gq.kv_cache(B, Hq, Hkv, kd, vd, kwd, vwd)
+    out = gq.kv_attention(bf16_dev(q), cache)
+    torch.cuda.synchronize()
+    return y_bits(out).reshape(B, Hq, 128)
+
+
+def gate(out_bits, ref, vmax):
+    """Normwise over the whole output, plus the elementwise bound; returns
+    (normwise, normwise of the bf16 rounding of the exact result alone)."""
+    got = O.bf16_bits_to_f64(out_bits)
+    normwise = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    rounding = np.linalg.norm(O.bf16_bits_to_f64(O.f64_to_bf16_bits(ref)) - ref) / np.linalg.norm(ref)
+    assert normwise <= 2e-3, (normwise, rounding)
+    bound = 2.0 ** -8 * np.abs(ref) + 2e-3 * vmax
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{bad.sum()} elements outside the bound"
+    return normwise, rounding
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,tp,tw,bits", [
+    (1, 32, 8, 256, 16, 4),        # Llama-3-8B heads, whole tiles, window
+    (1, 32, 8, 100, 0, 4),         # ragged last tile, no window
+    (2, 32, 8, 77, 5, 2),          # INT2, two sequences, ragged
+    (1, 8, 8, 33, 1, 4),           # one query head per key/value head
+    (3, 16, 2, 129, 7, 2),         # 8 query heads per key/value head, 3 sequences
+    (1, 4, 4, 1, 0, 4),            # a single packed token
+    (1, 32, 8, 0, 40, 4),          # window only
+    (1, 12, 6, 300, 9, 4),         # two workgroup head groups, the second with 2 heads
+    (1, 2, 1, 500, 3, 2),          # one key/value head
+])
+def test_kv_attention_shapes(B, Hq, Hkv, tp, tw, bits):
+    q, kp, vp, kw, vw = kv_inputs(100 + tp + tw, B, Hq, Hkv, tp, tw, bits)
+    _say("kv", B, Hq, Hkv, tp, tw, bits)
+    got = run_gpu(q, kp, vp, kw, vw, B, Hq, Hkv)
+    ref = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, 128)
+    vmax = max(np.abs(O.dequant(vp)).max() if vp is not None else 0, np.abs(O.bf16_bits_to_f64(vw)).max() if tw else 0)
+    _say("normwise", gate(got, ref, vmax))
+
+
+@pytest.mark.parametrize("kscale", [0.05, 3.0])
+def test_kv_attention_flat_and_peaked(kscale):
+    """Nearly uniform and strongly peaked softmax (scores up to ~100)."""
+    B, Hq, Hkv, tp, tw = 1, 32, 8, 1000, 24
+    q, kp, vp, kw, vw = kv_inputs(7, B, Hq, Hkv, tp, tw, 4, kscale=kscale)
+    got = run_gpu(q, kp, vp, kw, vw, B, Hq, Hkv)
+    ref = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, 128)
+    gate(got, ref, np.abs(O.dequant(vp)).max())
+
+
+def test_kv_attention_long_context():
+    """32768 tokens (32640 packed + 128 window), Llama-3-8B heads, INT4:
+    the configuration the benchmark times, with its split over 255 parts."""
+    B, Hq, Hkv, tp, tw = 1, 32, 8, 32640, 128
+    q, kp, vp, kw, vw = kv_inputs(8, B, Hq, Hkv, tp, tw, 4)
+    _say("kv long context", tp, tw)
+    got = run_gpu(q, kp, vp, kw, vw, B, Hq, Hkv)
+    ref = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, 128)
+    _say("normwise", gate(got, ref, np.abs(O.dequant(vp)).max()))
+
+
+def test_kv_attention_gpu_packing_and_repeat():
+    """The cache packed on the GPU by gq_quantize_pack (one row per token)
+    gives the oracle's answer; a second call gives the same bytes."""
+    B, Hq, Hkv, tp, tw = 2, 32, 8, 200, 8
+    rng = np.random.default_rng(9)
+    q = S.bf16_bits(rng.standard_normal((B, Hq, 128)).astype(np.float32))
+    k = rng.standard_normal((B * tp, Hkv * 128)).astype(np.float32)
+    v = rng.standard_normal((B * tp, Hkv * 128)).astype(np.float32)
+    kw = S.bf16_bits(rng.standard_normal((B, tw, Hkv, 128)).astype(np.float32))
+    vw = S.bf16_bits(rng.standard_normal((B, tw, Hkv, 128)).astype(np.float32))
+    kd = gq.quantize_pack(torch.from_numpy(k).cuda(), 2)
+    vd = gq.quantize_pack(torch.from_numpy(v).cuda(), 2)
+    cache = gq.kv_cache(B, Hq, Hkv, kd, vd, bf16_dev(kw), bf16_dev(vw))
+    qd = bf16_dev(q)
+    a = y_bits(gq.kv_attention(qd, cache))
+    b2 = y_bits(gq.kv_attention(qd, cache))
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b2)
+    kp, vp = O.kv_cache_pack(k, 2), O.kv_cache_pack(v, 2)
+    ref = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, 128)
+    gate(a.reshape(B, Hq, 128), ref, np.abs(O.dequant(vp)).max())
+
+
+def test_kv_attention_errors():
+    c = gq.gq_kv_cache(1, 32, 8, 64, 4, 10, 0, None, None, None, None, None, None, None, None)
+    with pytest.raises(gq.GqError) as e:
+        gq.gq_kv_attention_workspace_bytes(c)
+    assert e.value.status == gq.GQ_ERR_SHAPE
+    c = gq.gq_kv_cache(1, 12, 8, 128, 4, 10, 0, None, None, None, None, None, None, None, None)
+    with pytest.raises(gq.GqError):
+        gq.gq_kv_attention_workspace_bytes(c)
+    c = gq.gq_kv_cache(1, 32, 8, 128, 3, 10, 0, None, None, None, None, None, None, None, None)
+    with pytest.raises(gq.GqError) as e:
+        gq.gq_kv_attention_workspace_bytes(c)
+    assert e.value.status == gq.GQ_ERR_BITS
+    c = gq.gq_kv_cache(1, 32, 8, 128, 4, 0, 0, None, None, None, None, None, None, None, None)
+    with pytest.raises(gq.GqError):
+        gq.gq_kv_attention_workspace_bytes(c)
