@@ -273,6 +273,42 @@ def secondary(torch, gq, S, args):
     torch.cuda.empty_cache()
 
     out.update(channel_mix(torch, gq, S))
+    out.update(kv_decode(torch, gq))
+    return out
+
+
+def kv_decode(torch, gq):
+    """One decode step of attention over a group-wise quantized KV cache:
+    Llama-3-8B heads (32 query, 8 key/value, dim 128), the newest 128 tokens
+    of a 32768-token context in a dense bf16 window and the rest packed INT4
+    g128 or INT2 g64; and 32 sequences of 2048 tokens (64 in the window).
+    Bytes: packed K and V (codes, scales, zeros), the window, q and out."""
+    out = {}
+    Hq, Hkv = 32, 8
+    for name, B, tp, tw, bits in [("kv_decode_32k_int4", 1, 32640, 128, 4),
+                                  ("kv_decode_32k_int2", 1, 32640, 128, 2),
+                                  ("kv_decode_b32_2k_int4", 32, 1984, 64, 4)]:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(7000 + B + bits)
+        k = torch.randn((B * tp, Hkv * 128), generator=gen, device="cuda")
+        v = torch.randn((B * tp, Hkv * 128), generator=gen, device="cuda")
+        kp, vp = gq.quantize_pack(k, bits), gq.quantize_pack(v, bits)
+        del k, v
+        kw = torch.randn((B, tw, Hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        vw = torch.randn((B, tw, Hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        q = torch.randn((B, Hq, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        cache = gq.kv_cache(B, Hq, Hkv, kp, vp, kw, vw)
+        ws = gq.workspace(gq.gq_kv_attention_workspace_bytes(cache), "cuda")
+        gt = GraphTimer(torch, lambda: gq.kv_attention(q, cache, out=o, ws=ws))
+        gt.run(20)
+        t, _ = gt.run(50)
+        nbytes = kp.nbytes() + vp.nbytes() + 2 * kw.numel() * 2 + 2 * q.numel() * 2
+        out[name] = {"batch": B, "t_packed": tp, "t_window": tw, "bits": bits, "us": round(t / 50 * 1e6, 1),
+                     "GBps": round(nbytes * 50 / t / 1e9, 1),
+                     "frac_hbm": round(nbytes * 50 / t / 1e9 / HBM_PEAK_GBS, 3), "bytes": nbytes}
+        del kp, vp, kw, vw, q, o
+        torch.cuda.empty_cache()
     return out
 
 

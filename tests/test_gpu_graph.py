@@ -78,3 +78,20 @@ def test_fake_quant_in_graph():
     lay = gq.make_layout(K, N, 128, [4, 2, 2, 4])
     out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     _graph_matches_eager(lambda: gq.gq_fake_quant(lay, W.data_ptr(), gq.GQ_BF16, out.data_ptr()), out)
+
+
+def test_kv_attention_in_graph():
+    """Packed splits, window parts and the combine, captured and replayed."""
+    B, Hq, Hkv, tp, tw = 2, 32, 8, 700, 40
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    k = torch.randn((B * tp, Hkv * 128), generator=gen, device="cuda")
+    v = torch.randn((B * tp, Hkv * 128), generator=gen, device="cuda")
+    kp, vp = gq.quantize_pack(k, 4), gq.quantize_pack(v, 4)
+    kw = torch.randn((B, tw, Hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    vw = torch.randn((B, tw, Hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, Hq, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    cache = gq.kv_cache(B, Hq, Hkv, kp, vp, kw, vw)
+    ws = gq.workspace(gq.gq_kv_attention_workspace_bytes(cache), "cuda")
+    _graph_matches_eager(lambda: gq.kv_attention(q, cache, out=o, ws=ws), o)
