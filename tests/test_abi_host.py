@@ -141,6 +141,34 @@ def test_dx_argument_errors_before_launch(lib):
     assert gq.gq_linear_dx_workspace_bytes(wide, 64) >= 2 * 64 * 256 * 4
 
 
+def test_kv_attention_argument_errors_before_launch(lib):
+    """gq_kv_attention: shape, width and pointer checks on the host."""
+    A, bad = 0x10000, 0x10008
+    def cache(**kw):
+        f = dict(batch=1, q_heads=32, kv_heads=8, head_dim=128, bits=4, t_packed=100, t_window=8,
+                 k_codes=A, k_scales=A, k_zeros=A, v_codes=A, v_scales=A, v_zeros=A, k_window=A, v_window=A)
+        f.update(kw)
+        return gq.gq_kv_cache(*[f[n] for n, _ in gq.gq_kv_cache._fields_])
+    KV = lambda c, q, o, ws, wsb: lib.gq_kv_attention(ctypes.byref(c), q, o, ws, wsb, None)
+    need = gq.gq_kv_attention_workspace_bytes(cache())
+    assert need > 0 and need % 256 == 0
+    assert KV(cache(head_dim=64), A, A, A, need) == gq.GQ_ERR_SHAPE
+    assert KV(cache(q_heads=12), A, A, A, need) == gq.GQ_ERR_SHAPE           # 12 / 8 heads
+    assert KV(cache(q_heads=48, kv_heads=3), A, A, A, need) == gq.GQ_ERR_SHAPE   # 16 per head
+    assert KV(cache(bits=3), A, A, A, need) == gq.GQ_ERR_BITS
+    assert KV(cache(t_packed=0, t_window=0), A, A, A, need) == gq.GQ_ERR_SHAPE
+    assert KV(cache(t_window=1025), A, A, A, need) == gq.GQ_ERR_SHAPE
+    assert KV(cache(), bad, A, A, need) == gq.GQ_ERR_ALIGNMENT
+    assert KV(cache(), A, None, A, need) == gq.GQ_ERR_NULL_ARG
+    assert KV(cache(k_codes=bad), A, A, A, need) == gq.GQ_ERR_ALIGNMENT
+    assert KV(cache(v_zeros=None), A, A, A, need) == gq.GQ_ERR_NULL_ARG
+    assert KV(cache(k_window=None), A, A, A, need) == gq.GQ_ERR_NULL_ARG
+    assert KV(cache(), A, A, None, need) == gq.GQ_ERR_WORKSPACE
+    assert KV(cache(), A, A, A, need - 1) == gq.GQ_ERR_WORKSPACE
+    assert KV(cache(), A, A, A + 16, need) == gq.GQ_ERR_ALIGNMENT
+    assert lib.gq_kv_attention(None, A, A, A, need, None) == gq.GQ_ERR_NULL_ARG
+
+
 def test_workspace_sizes():
     lay = gq.make_layout(4096, 14336, 14336, [4])
     # dot-product path, and the small-batch path on a wide layer up to 16
