@@ -27,7 +27,7 @@
 //     and p S z per head, so the zero point costs one FMA per token and head.
 // (An online softmax over each 32-token tile spent most of its time in the
 // per-tile cross-lane reductions.)  Each workgroup writes its (max, sum,
-// unnormalised output) per head; kv_window_kernel does the same for each 32
+// unnormalised output) per head; the first workgroups do the same for each 32
 // tokens of the window; kv_combine_kernel merges the parts with the
 // log-sum-exp rule.
 #include "gq_device.h"
@@ -53,6 +53,7 @@ struct KvArgs {
   int B, Hq, Hkv, bits, tp, tw;
   int tps;               // packed tokens per split (a multiple of KV_TT)
   int nsp;               // packed splits per sequence
+  int nwp;               // 32-token window parts per sequence
   int ns;                // parts per (sequence, head): packed splits, then 32-token window parts
   uint32_t row_bytes;    // code bytes of one token row (all heads)
   uint32_t row_groups;   // groups of one token row
@@ -66,6 +67,103 @@ __device__ __forceinline__ size_t part_index(const KvArgs &a, int b, int s, int 
   return ((size_t)b * a.ns + s) * a.Hq + h;
 }
 
+// Ordering of LDS values that one lane of a wave stores and others load.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One 32-token part of the dense bf16 window ([B][tw][Hkv][D]) for key/value
+// head kh, by one wave: its (max, sum, unnormalised output) for the G query
+// heads.  qs: this wave's LDS scratch, G * (D + 32) floats.
+template <int G>
+__device__ __forceinline__ void window_part(const KvArgs &a, int wp, int b, int kh, int lane,
+                                            const uint16_t *__restrict__ q, const uint16_t *__restrict__ kw,
+                                            const uint16_t *__restrict__ vw, float *qs,
+                                            float *__restrict__ part_o, float *__restrict__ part_ml) {
+  float *pl = qs + G * KV_D;                       // weights [G][32]
+  const int t0 = wp * KV_TT;
+  const int nt = a.tw - t0 < KV_TT ? a.tw - t0 : KV_TT;
+  const size_t tstride = (size_t)a.Hkv * KV_D;
+  // q of the G query heads, fp32
+  const uint16_t *qh = q + ((size_t)b * a.Hq + (size_t)kh * G) * KV_D;
+  for (int c = lane; c < G * KV_D / 8; c += 64) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(qh + 8 * c);
+    const uint32_t uu[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qs[8 * c + 2 * i] = bf16_bits_to_f32((uint16_t)(uu[i] & 0xffffu));
+      qs[8 * c + 2 * i + 1] = bf16_bits_to_f32((uint16_t)(uu[i] >> 16));
+    }
+  }
+  wave_lds_sync();
+  // scores: lane -> token lane / 2, features 64 (lane & 1) .. + 63
+  const int t = lane >> 1, hf = lane & 1;
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.f;
+  if (t < nt) {
+    const uint16_t *krow = kw + ((size_t)b * a.tw + t0 + t) * tstride + (size_t)kh * KV_D + 64 * hf;
+#pragma unroll 2
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(krow + 8 * c);
+      const uint32_t uu[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float k0 = bf16_bits_to_f32((uint16_t)(uu[i] & 0xffffu));
+        const float k1 = bf16_bits_to_f32((uint16_t)(uu[i] >> 16));
+        const int d = 64 * hf + 8 * c + 2 * i;
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = fmaf(qs[g * KV_D + d + 1], k1, fmaf(qs[g * KV_D + d], k0, acc[g]));
+      }
+    }
+  }
+  float mx[G], sm[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float v = acc[g] + __shfl_xor(acc[g], 1);
+    const float sc = t < nt ? v * a.scale : -__builtin_inff();
+    float m = sc;
+#pragma unroll
+    for (int d = 2; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+    const float p = t < nt ? __expf(sc - m) : 0.f;
+    float l = p;
+#pragma unroll
+    for (int d = 2; d < 64; d <<= 1) l += __shfl_xor(l, d);
+    mx[g] = m;
+    sm[g] = l;
+    if (hf == 0) pl[g * KV_TT + t] = p;
+  }
+  wave_lds_sync();
+  // P . V: lane -> features 2 lane, 2 lane + 1
+  float o[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) o[g][0] = o[g][1] = 0.f;
+  const uint16_t *vrow = vw + ((size_t)b * a.tw + t0) * tstride + (size_t)kh * KV_D + 2 * lane;
+#pragma unroll 4
+  for (int tt = 0; tt < nt; ++tt) {
+    const uint32_t v2 = *reinterpret_cast<const uint32_t *>(vrow + tt * tstride);
+    const float v0 = bf16_bits_to_f32((uint16_t)(v2 & 0xffffu)), v1 = bf16_bits_to_f32((uint16_t)(v2 >> 16));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pg = pl[g * KV_TT + tt];
+      o[g][0] = fmaf(pg, v0, o[g][0]);
+      o[g][1] = fmaf(pg, v1, o[g][1]);
+    }
+  }
+  const int part = a.nsp + wp;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const size_t pi = part_index(a, b, part, kh * G + g);
+    *reinterpret_cast<float2 *>(part_o + pi * KV_D + 2 * lane) = make_float2(o[g][0], o[g][1]);
+    if (lane == 0) {
+      part_ml[2 * pi] = mx[g];
+      part_ml[2 * pi + 1] = sm[g];
+    }
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t *__restrict__ q,
                                                         const uint8_t *__restrict__ kc,
@@ -75,18 +173,30 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
                                                         const uint16_t *__restrict__ vs,
                                                         const uint8_t *__restrict__ vz,
                                                         uint32_t code_bytes, uint32_t groups,
+                                                        const uint16_t *__restrict__ kw,
+                                                        const uint16_t *__restrict__ vw,
                                                         float *__restrict__ part_o,
                                                         float *__restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) uint4 T[2 * KV_NT][KV_TILE / 16];   // K tiles, then V tiles
   __shared__ uint32_t SZ[KV_HG][2 * KV_NT][KV_TT][2];   // scale | zero << 16 per tile, token, group
-  __shared__ __attribute__((aligned(16))) float SC[KV_HG][KV_TPS][8];       // scores
+  constexpr int SCW = G <= 4 ? 4 : 8;
+  __shared__ __attribute__((aligned(16))) float SC[KV_HG][KV_TPS][SCW];     // scores, then weights
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x, b = blockIdx.y;
+  const int b = blockIdx.y;
   const int kh0 = blockIdx.z * KV_HG;
   const int kh = kh0 + w;
   const bool active = kh < a.Hkv;
+  if ((int)blockIdx.x < a.nwp) {
+    // the first workgroups take the window's 32-token parts (they start
+    // with the first round of workgroups), in the tile memory
+    if (active)
+      window_part<G>(a, blockIdx.x, b, kh, lane, q, kw, vw, reinterpret_cast<float *>(&T[0][0]) + w * (G * KV_D + G * KV_TT),
+                     part_o, part_ml);
+    return;
+  }
+  const int split = blockIdx.x - a.nwp;
   const int nh = a.Hkv - kh0 < KV_HG ? a.Hkv - kh0 : KV_HG;      // heads of this group
   const uint32_t hbytes = (uint32_t)(KV_D * a.bits / 8);          // code bytes per token and head
   const uint32_t seg = (uint32_t)nh * hbytes;                     // code bytes per token, this group
@@ -176,14 +286,6 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
   float mrow[4];        // running max of accumulator rows 4 kq + i over this lane's tokens
 #pragma unroll
   for (int i = 0; i < 4; ++i) mrow[i] = -__builtin_inff();
-  float o[G][8], Z[G], lsum[G], mh[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    Z[g] = 0.f;
-    lsum[g] = 0.f;
-#pragma unroll
-    for (int f = 0; f < 8; ++f) o[g][f] = 0.f;
-  }
 
   // every tile of the range at once (K tiles, then V tiles), one barrier
   const int nu = 2 * ntiles;
@@ -198,138 +300,170 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
       if (u < nu) SZ[w][u][lane & 31][lane >> 5] = szs[u] | (szz[u] << 16);
   }
   lds_barrier();
-  for (int u = 0; u < nu; ++u) {
-    const uint4 *Tc = T[u];
-    const bool isv = u >= ntiles;
-    const int tau = isv ? u - ntiles : u;
-    if (u == ntiles) {
-      // the scores other lanes stored in pass 1 are read in pass 2: order
-      // them for the whole wave
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    if (u == ntiles && active) {
-      // the range's max per head, from the lanes' running maxima of their
-      // rows; head g is row g % 4 of lane group g / 4, read from its first
-      // lane (a conditional LDS store read back by the other lanes is not
-      // ordered for the compiler: it served the storing lane its own value
-      // and loaded the others before the store)
-      float mxr[4];
+  if (!active || ntiles == 0) return;
+
+  // ---- pass 1: scores of each tile's two 16-token blocks
+  for (int u = 0; u < ntiles; ++u) {
+    const uint8_t *tb8 = reinterpret_cast<const uint8_t *>(T[u]);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int n = 16 * blk + r;                 // token of this lane's B column
+      const uint32_t sz0 = SZ[w][u][n][0], sz1 = SZ[w][u][n][gph - 1];
+      floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        half8 bv;
+        const uint32_t base = (uint32_t)n * seg + (uint32_t)w * hbytes;
+        uint32_t t4, mask, shift;
+        if (a.bits == 4) {
+          t4 = *reinterpret_cast<const uint32_t *>(tb8 + base + (uint32_t)(16 * kb + 4 * kq));
+          mask = 0x000f000fu;
+          shift = 4;
+        } else {
+          const uint32_t uu = *reinterpret_cast<const uint16_t *>(tb8 + base + (uint32_t)(8 * kb + 2 * kq));
+          t4 = __builtin_amdgcn_perm(uu, uu, 0x0c010c00u);
+          mask = 0x00030003u;
+          shift = 2;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2v pp = __builtin_bit_cast(half2v, and_or(t4 >> (shift * i), mask, 0x64006400u));
+          bv[2 * i] = pp.x;
+          bv[2 * i + 1] = pp.y;
+        }
+        const uint32_t zz = (a.bits == 4 || kb < 2) ? sz0 : sz1;
+        const _Float16 zb = (_Float16)(-(1024.f + (float)(zz >> 16)));
+        half8 zv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zv[i] = zb;
+        if (a.bits == 4 || kb < 2) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], bv, acc0, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], zv, acc0, 0, 0, 0);
+        } else {
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], bv, acc1, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], zv, acc1, 0, 0, 0);
+        }
+      }
+      const float s0 = f16_bits_to_f32((uint16_t)(sz0 & 0xffffu));
+      const float s1 = f16_bits_to_f32((uint16_t)(sz1 & 0xffffu));
+      const int trel = u * KV_TT + n;             // token within the range
+      const bool valid = t_begin + trel < t_end;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float mx = mrow[i];
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-        mxr[i] = mx;
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        mh[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mxr[g & 3]), 16 * (g >> 2)));
-    }
-    if (active) {
-      const uint8_t *tb8 = reinterpret_cast<const uint8_t *>(Tc);
-      if (!isv) {
-        // ---- pass 1: scores of the tile's two 16-token blocks
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const int n = 16 * blk + r;                 // token of this lane's B column
-          const uint32_t sz0 = SZ[w][u][n][0], sz1 = SZ[w][u][n][gph - 1];
-          floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            half8 bv;
-            const uint32_t base = (uint32_t)n * seg + (uint32_t)w * hbytes;
-            uint32_t t4, mask, shift;
-            if (a.bits == 4) {
-              t4 = *reinterpret_cast<const uint32_t *>(tb8 + base + (uint32_t)(16 * kb + 4 * kq));
-              mask = 0x000f000fu;
-              shift = 4;
-            } else {
-              const uint32_t uu = *reinterpret_cast<const uint16_t *>(tb8 + base + (uint32_t)(8 * kb + 2 * kq));
-              t4 = __builtin_amdgcn_perm(uu, uu, 0x0c010c00u);
-              mask = 0x00030003u;
-              shift = 2;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const half2v pp = __builtin_bit_cast(half2v, and_or(t4 >> (shift * i), mask, 0x64006400u));
-              bv[2 * i] = pp.x;
-              bv[2 * i + 1] = pp.y;
-            }
-            const uint32_t zz = (a.bits == 4 || kb < 2) ? sz0 : sz1;
-            const _Float16 zb = (_Float16)(-(1024.f + (float)(zz >> 16)));
-            half8 zv;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) zv[i] = zb;
-            if (a.bits == 4 || kb < 2) {
-              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], bv, acc0, 0, 0, 0);
-              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], zv, acc0, 0, 0, 0);
-            } else {
-              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], bv, acc1, 0, 0, 0);
-              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], zv, acc1, 0, 0, 0);
-            }
-          }
-          const float s0 = f16_bits_to_f32((uint16_t)(sz0 & 0xffffu));
-          const float s1 = f16_bits_to_f32((uint16_t)(sz1 & 0xffffu));
-          const int trel = tau * KV_TT + n;           // token within the range
-          const bool valid = t_begin + trel < t_end;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float raw = a.bits == 4 ? s0 * acc0[i] : s0 * acc0[i] + s1 * acc1[i];
-            const float sc = valid ? raw * fr[i] : -__builtin_inff();
-            mrow[i] = fmaxf(mrow[i], sc);
-            if (4 * kq + i < G) SC[w][trel][4 * kq + i] = sc;
-          }
-        }
-      } else {
-        // ---- pass 2: P . V, lane -> features 8 fs .. 8 fs + 7, tokens 4 j + kq
-        const int fs = r;
-        const int vg = a.bits == 4 ? 0 : (fs >> 3);    // group of these features
-#pragma unroll 1
-        for (int jj = 0; jj < KV_TT / 4; ++jj) {
-          const int t = 4 * jj + kq;
-          const int trel = tau * KV_TT + t;
-          const uint32_t base = (uint32_t)t * seg + (uint32_t)w * hbytes;
-          uint32_t cw;
-          if (a.bits == 4)
-            cw = *reinterpret_cast<const uint32_t *>(tb8 + base + 4u * fs);
-          else
-            cw = *reinterpret_cast<const uint16_t *>(tb8 + base + 2u * fs);
-          const uint32_t sz = SZ[w][u][t][vg];
-          const float S = f16_bits_to_f32((uint16_t)(sz & 0xffffu));
-          const float zf = (float)(sz >> 16);
-          float c[8];
-#pragma unroll
-          for (int f = 0; f < 8; ++f) {
-            // the code under the mantissa of 2^23: exact, then minus 2^23
-            const uint32_t bitsf = a.bits == 4 ? and_or(cw >> (4 * f), 0xfu, 0x4b000000u)
-                                               : and_or(cw >> (2 * f), 0x3u, 0x4b000000u);
-            c[f] = __uint_as_float(bitsf) - 8388608.f;
-          }
-          const bool valid = t_begin + trel < t_end;
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float p = valid ? __expf(SC[w][trel][g] - mh[g]) : 0.f;
-            lsum[g] += p;
-            const float pw = p * S;
-            Z[g] = fmaf(pw, zf, Z[g]);
-#pragma unroll
-            for (int f = 0; f < 8; ++f) o[g][f] = fmaf(pw, c[f], o[g][f]);
-          }
-        }
+        const float raw = a.bits == 4 ? s0 * acc0[i] : s0 * acc0[i] + s1 * acc1[i];
+        const float sc = valid ? raw * fr[i] : -__builtin_inff();
+        mrow[i] = fmaxf(mrow[i], sc);
+        if (4 * kq + i < G) SC[w][trel][4 * kq + i] = sc;
       }
     }
   }
 
-  if (!active || ntiles == 0) return;
+  // the range's max per head, from the lanes' running maxima of their rows;
+  // head g is row g % 4 of lane group g / 4, read from its first lane (a
+  // conditional LDS store read back by the other lanes is not ordered for
+  // the compiler: it served the storing lane its own value and loaded the
+  // others before the store)
+  float mh[G];
+  {
+    float mxr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = mrow[i];
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+      mxr[i] = mx;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      mh[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mxr[g & 3]), 16 * (g >> 2)));
+  }
+  // the scores other lanes stored are read below: order them for the wave
+  wave_lds_sync();
+
+  // ---- weights p = exp(s - max), once per (token, head): lane -> token
+  // `lane` of the range (invalid tokens hold -inf, so p = 0); their sums
+  float lsum[G];
+  {
+    const bool have = lane < KV_TT * ntiles;
+    float pv[SCW];
+#pragma unroll
+    for (int g = 0; g < SCW; g += 4) {
+      const float4 v4 = have ? *reinterpret_cast<const float4 *>(&SC[w][lane][g]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pv[g] = v4.x; pv[g + 1] = v4.y; pv[g + 2] = v4.z; pv[g + 3] = v4.w;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float p = have ? __expf(pv[g] - mh[g]) : 0.f;
+      pv[g] = p;
+      float sm = p;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) sm += __shfl_xor(sm, d);
+      lsum[g] = sm;
+    }
+#pragma unroll
+    for (int g = 0; g < SCW; g += 4)
+      if (have) *reinterpret_cast<float4 *>(&SC[w][lane][g]) = make_float4(pv[g], pv[g + 1], pv[g + 2], pv[g + 3]);
+  }
+  wave_lds_sync();
+
+  // ---- pass 2: P . V, lane -> features 8 fs .. 8 fs + 7, tokens 4 j + kq
+  float o[G][8], Z[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    Z[g] = 0.f;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) o[g][f] = 0.f;
+  }
+  const int fs = r;
+  const int vg = a.bits == 4 ? 0 : (fs >> 3);        // group of these features
+  for (int u = ntiles; u < nu; ++u) {
+    const uint8_t *tb8 = reinterpret_cast<const uint8_t *>(T[u]);
+    const int tau = u - ntiles;
+    constexpr int UNR = G <= 4 ? 2 : 1;         // registers: 8 heads leave no room for two tokens
+#pragma unroll UNR
+    for (int jj = 0; jj < KV_TT / 4; ++jj) {
+      const int t = 4 * jj + kq;
+      const int trel = tau * KV_TT + t;
+      const uint32_t base = (uint32_t)t * seg + (uint32_t)w * hbytes;
+      float c[8];
+      if (a.bits == 4) {
+        // even and odd nibbles to bytes, bytes to float
+        const uint32_t cw = *reinterpret_cast<const uint32_t *>(tb8 + base + 4u * fs);
+        const uint32_t lo = cw & 0x0f0f0f0fu, hi = (cw >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          c[2 * k] = (float)((lo >> (8 * k)) & 0xffu);
+          c[2 * k + 1] = (float)((hi >> (8 * k)) & 0xffu);
+        }
+      } else {
+        const uint32_t cw = *reinterpret_cast<const uint16_t *>(tb8 + base + 2u * fs);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) c[f] = (float)((cw >> (2 * f)) & 3u);
+      }
+      const uint32_t sz = SZ[w][u][t][vg];
+      const float S = f16_bits_to_f32((uint16_t)(sz & 0xffffu));
+      const float zf = (float)(sz >> 16);
+      float pv[SCW];
+#pragma unroll
+      for (int g = 0; g < SCW; g += 4) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(&SC[w][trel][g]);
+        pv[g] = v4.x; pv[g + 1] = v4.y; pv[g + 2] = v4.z; pv[g + 3] = v4.w;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float pw = pv[g] * S;
+        Z[g] = fmaf(pw, zf, Z[g]);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) o[g][f] = fmaf(pw, c[f], o[g][f]);
+      }
+    }
+  }
+
   // sum the four token lane groups, subtract the zero-point term
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     Z[g] += __shfl_xor(Z[g], 16);
     Z[g] += __shfl_xor(Z[g], 32);
-    lsum[g] += __shfl_xor(lsum[g], 16);
-    lsum[g] += __shfl_xor(lsum[g], 32);
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       o[g][f] += __shfl_xor(o[g][f], 16);
@@ -351,151 +485,61 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
   }
 }
 
-// Window tokens (dense bf16 [B][tw][Hkv][D]): one workgroup per (32-token
-// part of the window, sequence, key/value head) writes that part's (max,
-// sum, unnormalised output) for the G query heads.
 constexpr int KV_TW_MAX = 1024;
-
-template <int G>
-__global__ __launch_bounds__(256) void kv_window_kernel(KvArgs a, const uint16_t *__restrict__ q,
-                                                        const uint16_t *__restrict__ kw,
-                                                        const uint16_t *__restrict__ vw,
-                                                        float *__restrict__ part_o,
-                                                        float *__restrict__ part_ml) {
-  __shared__ float qs[G][KV_D];
-  __shared__ float Sw[G][KV_TT];
-  const int wp = blockIdx.x, b = blockIdx.y, kh = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int t0 = wp * KV_TT;
-  const int nt = a.tw - t0 < KV_TT ? a.tw - t0 : KV_TT;
-  for (int i = tid; i < G * KV_D; i += 256)
-    qs[i / KV_D][i % KV_D] = bf16_bits_to_f32(q[((size_t)b * a.Hq + kh * G + i / KV_D) * KV_D + i % KV_D]);
-  __syncthreads();
-  const size_t tstride = (size_t)a.Hkv * KV_D;
-  const uint16_t *kbase = kw + (((size_t)b * a.tw + t0) * a.Hkv + kh) * KV_D;
-  const uint16_t *vbase = vw + (((size_t)b * a.tw + t0) * a.Hkv + kh) * KV_D;
-  // scores: 8 lanes per token, lane j takes features 16 j .. 16 j + 15
-  {
-    const int t = tid >> 3, j = tid & 7;
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    if (t < nt) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(kbase + t * tstride + 16 * j + 8 * h);
-        const uint32_t uu[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 16 * j + 8 * h + 2 * i;
-          const float k0 = bf16_bits_to_f32((uint16_t)(uu[i] & 0xffffu));
-          const float k1 = bf16_bits_to_f32((uint16_t)(uu[i] >> 16));
-#pragma unroll
-          for (int g = 0; g < G; ++g) acc[g] = fmaf(qs[g][d + 1], k1, fmaf(qs[g][d], k0, acc[g]));
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int d = 1; d < 8; d <<= 1) acc[g] += __shfl_xor(acc[g], d);
-      if (j == 0) Sw[g][t] = t < nt ? acc[g] * a.scale : -__builtin_inff();
-    }
-  }
-  __syncthreads();
-  // max and exp per head over the part's tokens (G <= 8 heads, 32 tokens)
-  float mx[G], sm[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    mx[g] = -__builtin_inff();
-    for (int t = 0; t < nt; ++t) mx[g] = fmaxf(mx[g], Sw[g][t]);
-  }
-  __syncthreads();
-  if (tid < G * KV_TT) {
-    const int g = tid / KV_TT, t = tid % KV_TT;
-    Sw[g][t] = t < nt ? __expf(Sw[g][t] - mx[g]) : 0.f;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    sm[g] = 0.f;
-    for (int t = 0; t < nt; ++t) sm[g] += Sw[g][t];
-  }
-  // P . V: thread -> (head g, feature d) pairs
-  const int part = a.nsp + wp;
-  for (int i = tid; i < G * KV_D; i += 256) {
-    const int g = i / KV_D, d = i % KV_D;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int t = 0; t < nt; ++t) acc = fmaf(Sw[g][t], bf16_bits_to_f32(vbase[t * tstride + d]), acc);
-    part_o[part_index(a, b, part, kh * G + g) * KV_D + d] = acc;
-  }
-  if (tid < G) {
-    const size_t pi = part_index(a, b, part, kh * G + tid);
-    part_ml[2 * pi] = mx[tid];
-    part_ml[2 * pi + 1] = sm[tid];
-  }
-}
 
 // out[b][h] = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s,
 // over the parts that saw tokens; bf16, round to nearest even.  One
 // workgroup per (sequence, head, quarter of the features): thread (part
-// slice ps of 32, features 4 dq .. 4 dq + 3 of the quarter) sums every 32nd
-// part, then the slices meet in LDS.
+// slice ps of 32, features 4 dq .. 4 dq + 3 of the quarter) merges every
+// 32nd part into a running (max, sum, output) in one pass over the parts,
+// then the 32 slices are merged the same way.
 __global__ __launch_bounds__(256) void kv_combine_kernel(KvArgs a, const float *__restrict__ part_o,
                                                          const float *__restrict__ part_ml,
                                                          uint16_t *__restrict__ out) {
-  __shared__ float E[KV_NS_MAX];
-  __shared__ float red[4];
   __shared__ float4 acc_s[32][8];
+  __shared__ float2 ml_s[32];
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int tid = threadIdx.x;
-  float mx = -__builtin_inff();
-  for (int s = tid; s < a.ns; s += 256) {
-    const size_t pi = part_index(a, b, s, h);
-    if (part_ml[2 * pi + 1] > 0.f) mx = fmaxf(mx, part_ml[2 * pi]);
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float den = 0.f;
-  for (int s = tid; s < a.ns; s += 256) {
-    const size_t pi = part_index(a, b, s, h);
-    const float ls = part_ml[2 * pi + 1];
-    const float e = ls > 0.f ? __expf(part_ml[2 * pi] - M) : 0.f;
-    E[s] = e;
-    den = fmaf(ls > 0.f ? ls : 0.f, e, den);
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d);
-  if ((tid & 63) == 0) red[tid >> 6] = den;
-  __syncthreads();
-  den = red[0] + red[1] + red[2] + red[3];
   const int ps = tid >> 3, dq = tid & 7;
   const int f0 = 32 * blockIdx.y;
+  float M = -__builtin_inff(), L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int s = ps; s < a.ns; s += 32) {
-    const float e = E[s];
-    const float4 v = *reinterpret_cast<const float4 *>(part_o + part_index(a, b, s, h) * KV_D + f0 + 4 * dq);
-    if (e != 0.f) {
-      acc.x = fmaf(v.x, e, acc.x);
-      acc.y = fmaf(v.y, e, acc.y);
-      acc.z = fmaf(v.z, e, acc.z);
-      acc.w = fmaf(v.w, e, acc.w);
+    const size_t pi = part_index(a, b, s, h);
+    const float2 ml = *reinterpret_cast<const float2 *>(part_ml + 2 * pi);
+    const float4 v = *reinterpret_cast<const float4 *>(part_o + pi * KV_D + f0 + 4 * dq);
+    if (ml.y > 0.f) {
+      const float Mn = fmaxf(M, ml.x);
+      const float ca = __expf(M - Mn), cb = __expf(ml.x - Mn);     // ca = 0 while M = -inf
+      L = fmaf(L, ca, ml.y * cb);
+      acc.x = fmaf(acc.x, ca, v.x * cb);
+      acc.y = fmaf(acc.y, ca, v.y * cb);
+      acc.z = fmaf(acc.z, ca, v.z * cb);
+      acc.w = fmaf(acc.w, ca, v.w * cb);
+      M = Mn;
     }
   }
   acc_s[ps][dq] = acc;
+  if (dq == 0) ml_s[ps] = make_float2(M, L);
   __syncthreads();
   if (tid < 32) {
-    float sum = 0.f;
+    float Mx = -__builtin_inff();
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) sum += reinterpret_cast<const float *>(&acc_s[k][0])[tid];
-    out[((size_t)b * a.Hq + h) * KV_D + f0 + tid] = f32_to_bf16_rne(sum / den);
+    for (int k = 0; k < 32; ++k)
+      if (ml_s[k].y > 0.f) Mx = fmaxf(Mx, ml_s[k].x);
+    float num = 0.f, den = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float2 ml = ml_s[k];
+      if (ml.y > 0.f) {
+        const float e = __expf(ml.x - Mx);
+        num = fmaf(reinterpret_cast<const float *>(&acc_s[k][0])[tid], e, num);
+        den = fmaf(ml.y, e, den);
+      }
+    }
+    out[((size_t)b * a.Hq + h) * KV_D + f0 + tid] = f32_to_bf16_rne(num / den);
   }
 }
 
@@ -525,7 +569,8 @@ inline KvPlan kv_plan(const gq_kv_cache &c) {
   a.tps = tps;
   const int nsplit = a.tp > 0 ? (a.tp + tps - 1) / tps : 0;
   a.nsp = nsplit;
-  a.ns = nsplit + (a.tw + KV_TT - 1) / KV_TT;
+  a.nwp = (a.tw + KV_TT - 1) / KV_TT;
+  a.ns = nsplit + a.nwp;
   p.o_bytes = round256((size_t)a.B * a.ns * a.Hq * KV_D * 4u);
   p.ml_bytes = round256((size_t)a.B * a.ns * a.Hq * 2 * 4u);
   return p;
@@ -536,21 +581,13 @@ hipError_t launch_kv_g(const KvPlan &p, const gq_kv_cache &c, const void *q, voi
                        float *pml, hipStream_t s) {
   const KvArgs &a = p.a;
   const uint16_t *qq = reinterpret_cast<const uint16_t *>(q);
-  if (a.tp > 0) {
-    const uint64_t code_bytes = (uint64_t)a.B * a.tp * a.row_bytes;
-    const uint64_t groups = (uint64_t)a.B * a.tp * a.row_groups;
-    hipLaunchKernelGGL((kv_packed_kernel<G>), dim3(a.nsp, a.B, p.ngroups), dim3(256), 0, s, a, qq,
-                       reinterpret_cast<const uint8_t *>(c.k_codes), c.k_scales, c.k_zeros,
-                       reinterpret_cast<const uint8_t *>(c.v_codes), c.v_scales, c.v_zeros,
-                       (uint32_t)code_bytes, (uint32_t)groups, po, pml);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.tw > 0) {
-    hipLaunchKernelGGL((kv_window_kernel<G>), dim3((a.tw + KV_TT - 1) / KV_TT, a.B, a.Hkv), dim3(256), 0, s,
-                       a, qq, reinterpret_cast<const uint16_t *>(c.k_window),
-                       reinterpret_cast<const uint16_t *>(c.v_window), po, pml);
-  }
+  const uint64_t code_bytes = (uint64_t)a.B * a.tp * a.row_bytes;
+  const uint64_t groups = (uint64_t)a.B * a.tp * a.row_groups;
+  hipLaunchKernelGGL((kv_packed_kernel<G>), dim3(a.nwp + a.nsp, a.B, p.ngroups), dim3(256), 0, s, a, qq,
+                     reinterpret_cast<const uint8_t *>(c.k_codes), c.k_scales, c.k_zeros,
+                     reinterpret_cast<const uint8_t *>(c.v_codes), c.v_scales, c.v_zeros,
+                     (uint32_t)code_bytes, (uint32_t)groups, reinterpret_cast<const uint16_t *>(c.k_window),
+                     reinterpret_cast<const uint16_t *>(c.v_window), po, pml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kv_combine_kernel, dim3(a.B * a.Hq, KV_D / 32), dim3(256), 0, s, a, po, pml,
