@@ -27,9 +27,9 @@
 //     and p S z per head, so the zero point costs one FMA per token and head.
 // (An online softmax over each 32-token tile spent most of its time in the
 // per-tile cross-lane reductions.)  Each workgroup writes its (max, sum,
-// unnormalised output) per head; the first workgroups do the same for each 32
-// tokens of the window; kv_combine_kernel merges the parts with the
-// log-sum-exp rule.
+// unnormalised output) per head; workgroup s then does the same for the
+// s-th 32 tokens of the window (one wave per head); kv_combine_kernel
+// merges the parts with the log-sum-exp rule.
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -65,6 +65,47 @@ struct KvArgs {
 // no token.
 __device__ __forceinline__ size_t part_index(const KvArgs &a, int b, int s, int h) {
   return ((size_t)b * a.ns + s) * a.Hq + h;
+}
+
+// Cross-lane sums and maxima in registers: DPP moves within rows of 16
+// lanes (quad swaps, then the half-row and row mirrors), lane swaps across
+// rows; every lane receives the result.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dppf<0xB1>(v);          // lane ^ 1
+  v += dppf<0x4E>(v);          // lane ^ 2
+  v += dppf<0x141>(v);         // mirror within 8
+  return v + dppf<0x140>(v);   // mirror within 16
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  return fmaxf(v, dppf<0x140>(v));
+}
+// v + v of lane ^ 16, v + v of lane ^ 32 (and the maxima)
+__device__ __forceinline__ float add_x16(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  swap16(x, y);
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float add_x32(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  swap32(x, y);
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float max_x16(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  swap16(x, y);
+  return fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+}
+__device__ __forceinline__ float max_x32(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  swap32(x, y);
+  return fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
 }
 
 // Ordering of LDS values that one lane of a wave stores and others load.
@@ -122,15 +163,11 @@ __device__ __forceinline__ void window_part(const KvArgs &a, int wp, int b, int 
   float mx[G], sm[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float v = acc[g] + __shfl_xor(acc[g], 1);
+    const float v = acc[g] + dppf<0xB1>(acc[g]);          // the two halves of the token
     const float sc = t < nt ? v * a.scale : -__builtin_inff();
-    float m = sc;
-#pragma unroll
-    for (int d = 2; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+    const float m = max_x32(max_x16(max16(sc)));
     const float p = t < nt ? __expf(sc - m) : 0.f;
-    float l = p;
-#pragma unroll
-    for (int d = 2; d < 64; d <<= 1) l += __shfl_xor(l, d);
+    const float l = add_x32(add_x16(sum16(hf == 0 ? p : 0.f)));
     mx[g] = m;
     sm[g] = l;
     if (hf == 0) pl[g * KV_TT + t] = p;
@@ -177,7 +214,8 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
                                                         const uint16_t *__restrict__ vw,
                                                         float *__restrict__ part_o,
                                                         float *__restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint4 T[2 * KV_NT][KV_TILE / 16];   // K tiles, then V tiles
+  __shared__ __attribute__((aligned(16))) uint4 TK[KV_NT][KV_TILE / 16];     // K tiles
+  __shared__ __attribute__((aligned(16))) uint4 TV[KV_NT][KV_TILE / 16];     // V tiles
   __shared__ uint32_t SZ[KV_HG][2 * KV_NT][KV_TT][2];   // scale | zero << 16 per tile, token, group
   constexpr int SCW = G <= 4 ? 4 : 8;
   __shared__ __attribute__((aligned(16))) float SC[KV_HG][KV_TPS][SCW];     // scores, then weights
@@ -188,18 +226,14 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
   const int kh0 = blockIdx.z * KV_HG;
   const int kh = kh0 + w;
   const bool active = kh < a.Hkv;
-  if ((int)blockIdx.x < a.nwp) {
-    // the first workgroups take the window's 32-token parts (they start
-    // with the first round of workgroups), in the tile memory
-    if (active)
-      window_part<G>(a, blockIdx.x, b, kh, lane, q, kw, vw, reinterpret_cast<float *>(&T[0][0]) + w * (G * KV_D + G * KV_TT),
-                     part_o, part_ml);
-    return;
-  }
-  const int split = blockIdx.x - a.nwp;
-  const int nh = a.Hkv - kh0 < KV_HG ? a.Hkv - kh0 : KV_HG;      // heads of this group
+  const int split = blockIdx.x;
+  // workgroup `split` takes packed split `split` (if any), then window part
+  // `split` (if any), so the window adds no workgroups while nsp >= nwp
+  if (split < a.nsp) [&]() {
   const uint32_t hbytes = (uint32_t)(KV_D * a.bits / 8);          // code bytes per token and head
-  const uint32_t seg = (uint32_t)nh * hbytes;                     // code bytes per token, this group
+  // code bytes per token of the group's 4 heads (past the last head the
+  // bytes of the next token row are loaded and not used)
+  const uint32_t seg = (uint32_t)KV_HG * hbytes;
   const uint32_t seg_off = (uint32_t)kh0 * hbytes;
   const int gph = a.bits == 4 ? 1 : 2;                            // groups per head
   const int t_begin = split * a.tps;
@@ -210,28 +244,22 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
   const Rsrc vsr = make_rsrc(vs, 2u * groups), vzr = make_rsrc(vz, groups);
   const size_t row0 = (size_t)b * a.tp;                           // first token row of the sequence
 
-  // tile u of the stream: K tile u for u < ntiles, V tile u - ntiles after.
-  // Instruction i of a tile carries 1 KB = 1024 / seg tokens, lane l ->
-  // token i * (1024 / seg) + l / (seg / 16), 16-byte piece l % (seg / 16);
-  // every offset goes in the per-lane (range-checked) offset
+  // tile tau of K or V: instruction i < ninst carries 1 KB = 1024 / seg
+  // tokens, lane l -> token i * (1024 / seg) + l / (seg / 16), 16-byte piece
+  // l % (seg / 16); each wave issues instructions w and w + 4 (past ninst or
+  // past the range the offset is out of range: the load writes zeros to LDS
+  // inside the tile), so every wave issues the same number of loads
   const int lpt = (int)(seg / 16);                                // lanes per token
-  const int ninst = (int)(KV_TT * seg / 1024);                    // >= 1
-  auto dma_tile = [&](int u, uint4 *dst) {
-    const bool isv = u >= ntiles;
-    const int tau = isv ? u - ntiles : u;
-    for (int i = w; i < ninst; i += 4) {
-      const int tok = i * (64 / lpt) + lane / lpt;
-      const int t = t_begin + tau * KV_TT + tok;
-      const uint32_t off = t < a.tp ? (uint32_t)((row0 + t) * a.row_bytes) + seg_off + 16u * (lane % lpt)
+  const int ninst = (int)(KV_TT * seg / 1024);                    // 8 (INT4) or 4 (INT2)
+  auto tile_off = [&](int tau, int i) -> uint32_t {
+    const int tok = i * (64 / lpt) + lane / lpt;
+    const int t = t_begin + tau * KV_TT + tok;
+    return (i < ninst && t < t_end) ? (uint32_t)((row0 + t) * a.row_bytes) + seg_off + 16u * (lane % lpt)
                                     : kOobKv;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vcr : kcr, (lds_void *)(dst + 64 * i), 16, off, 0, 0, 0);
-    }
   };
-  // scales and zero points of the wave's head for tile u: lane -> token
+  // scales and zero points of the wave's head for tile tau: lane -> token
   // lane % 32, group lane / 32 (INT4 has one group per head)
-  auto load_sz = [&](int u, uint32_t &sv, uint32_t &zv) {
-    const bool isv = u >= ntiles;
-    const int tau = isv ? u - ntiles : u;
+  auto load_sz = [&](int tau, bool isv, uint32_t &sv, uint32_t &zv) {
     const int tok = lane & 31, grp = (lane >> 5) & (gph - 1);
     const int t = t_begin + tau * KV_TT + tok;
     const bool ok = active && t < t_end;
@@ -263,8 +291,7 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
         amax = fmaxf(amax, fmaxf(fabsf(qv[kb][2 * i]), fabsf(qv[kb][2 * i + 1])));
       }
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = max_x32(max_x16(amax));
     int e = 0;
     if (amax > 0.f && __builtin_isfinite(amax)) {
       int ex;
@@ -287,24 +314,39 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
 #pragma unroll
   for (int i = 0; i < 4; ++i) mrow[i] = -__builtin_inff();
 
-  // every tile of the range at once (K tiles, then V tiles), one barrier
-  const int nu = 2 * ntiles;
-  for (int u = 0; u < nu; ++u) dma_tile(u, T[u]);
-  {
-    uint32_t szs[2 * KV_NT], szz[2 * KV_NT];
+  // every load of the range at once: K scales and zero points, K tiles
+  // (loads that write LDS directly), V scales and zero points, V tiles into
+  // registers (written to LDS after pass 1: the compiler cannot tell loads
+  // that write LDS apart, and would make the first LDS read of pass 1 wait
+  // for all of them)
+  uint32_t szs[2 * KV_NT], szz[2 * KV_NT];
+  uint4 vt[KV_NT][2];
 #pragma unroll
-    for (int u = 0; u < 2 * KV_NT; ++u)
-      if (u < nu) load_sz(u, szs[u], szz[u]);
+  for (int tau = 0; tau < KV_NT; ++tau) load_sz(tau, false, szs[tau], szz[tau]);
+  // (with a lambda call among the builtin's arguments the host pass of the
+  // compiler drops the kernel's launch stub: the offset goes first into a
+  // variable)
+  auto dma_k = [&](uint4 *dst, int tau, int i) {
+    const uint32_t off = tile_off(tau, i);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kcr, (lds_void *)(dst + 64 * i), 16, off, 0, 0, 0);
+  };
 #pragma unroll
-    for (int u = 0; u < 2 * KV_NT; ++u)
-      if (u < nu) SZ[w][u][lane & 31][lane >> 5] = szs[u] | (szz[u] << 16);
-  }
+  for (int tau = 0; tau < KV_NT; ++tau)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma_k(TK[tau], tau, w + 4 * j);
+#pragma unroll
+  for (int tau = 0; tau < KV_NT; ++tau) load_sz(tau, true, szs[KV_NT + tau], szz[KV_NT + tau]);
+#pragma unroll
+  for (int tau = 0; tau < KV_NT; ++tau)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vt[tau][j] = ld128(vcr, tile_off(tau, w + 4 * j));
+#pragma unroll
+  for (int u = 0; u < KV_NT; ++u) SZ[w][u][lane & 31][lane >> 5] = szs[u] | (szz[u] << 16);
   lds_barrier();
-  if (!active || ntiles == 0) return;
 
   // ---- pass 1: scores of each tile's two 16-token blocks
-  for (int u = 0; u < ntiles; ++u) {
-    const uint8_t *tb8 = reinterpret_cast<const uint8_t *>(T[u]);
+  for (int u = 0; u < (active ? ntiles : 0); ++u) {
+    const uint8_t *tb8 = reinterpret_cast<const uint8_t *>(TK[u]);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int n = 16 * blk + r;                 // token of this lane's B column
@@ -358,6 +400,16 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
     }
   }
 
+  // the V half to LDS: scales and zero points, tiles
+#pragma unroll
+  for (int u = KV_NT; u < 2 * KV_NT; ++u) SZ[w][u][lane & 31][lane >> 5] = szs[u] | (szz[u] << 16);
+#pragma unroll
+  for (int tau = 0; tau < KV_NT; ++tau)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) TV[tau][64 * (w + 4 * j) + lane] = vt[tau][j];
+  lds_barrier();
+  if (!active) return;
+
   // the range's max per head, from the lanes' running maxima of their rows;
   // head g is row g % 4 of lane group g / 4, read from its first lane (a
   // conditional LDS store read back by the other lanes is not ordered for
@@ -368,10 +420,7 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
     float mxr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float mx = mrow[i];
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-      mxr[i] = mx;
+      mxr[i] = max16(mrow[i]);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -395,10 +444,7 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
     for (int g = 0; g < G; ++g) {
       const float p = have ? __expf(pv[g] - mh[g]) : 0.f;
       pv[g] = p;
-      float sm = p;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) sm += __shfl_xor(sm, d);
-      lsum[g] = sm;
+      lsum[g] = add_x32(add_x16(sum16(p)));
     }
 #pragma unroll
     for (int g = 0; g < SCW; g += 4)
@@ -416,9 +462,9 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
   }
   const int fs = r;
   const int vg = a.bits == 4 ? 0 : (fs >> 3);        // group of these features
-  for (int u = ntiles; u < nu; ++u) {
-    const uint8_t *tb8 = reinterpret_cast<const uint8_t *>(T[u]);
-    const int tau = u - ntiles;
+  for (int tau = 0; tau < ntiles; ++tau) {
+    const uint8_t *tb8 = reinterpret_cast<const uint8_t *>(TV[tau]);
+    const int u = KV_NT + tau;
     constexpr int UNR = G <= 4 ? 2 : 1;         // registers: 8 heads leave no room for two tokens
 #pragma unroll UNR
     for (int jj = 0; jj < KV_TT / 4; ++jj) {
@@ -462,13 +508,9 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
   // sum the four token lane groups, subtract the zero-point term
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    Z[g] += __shfl_xor(Z[g], 16);
-    Z[g] += __shfl_xor(Z[g], 32);
+    Z[g] = add_x32(add_x16(Z[g]));
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      o[g][f] += __shfl_xor(o[g][f], 16);
-      o[g][f] += __shfl_xor(o[g][f], 32);
-    }
+    for (int f = 0; f < 8; ++f) o[g][f] = add_x32(add_x16(o[g][f]));
   }
   if (kq == 0) {
 #pragma unroll
@@ -483,55 +525,94 @@ __global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t
       }
     }
   }
+  }();
+  if (split < a.nwp) {
+    // the window part's scratch is the tile memory (two waves in each of
+    // TK, TV: 2 G (D + 32) floats <= 16 KB): wait for every wave
+    if (split < a.nsp) __syncthreads();
+    if (active)
+      window_part<G>(a, split, b, kh, lane, q, kw, vw, reinterpret_cast<float *>(w < 2 ? &TK[0][0] : &TV[0][0]) + (w & 1) * (G * KV_D + G * KV_TT),
+                     part_o, part_ml);
+  }
 }
 
 constexpr int KV_TW_MAX = 1024;
 
 // out[b][h] = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s,
 // over the parts that saw tokens; bf16, round to nearest even.  One
-// workgroup per (sequence, head, quarter of the features): thread (part
-// slice ps of 32, features 4 dq .. 4 dq + 3 of the quarter) merges every
-// 32nd part into a running (max, sum, output) in one pass over the parts,
-// then the 32 slices are merged the same way.
+// workgroup per (sequence, head, 4 Q features): thread (part slice ps of
+// SL, features 4 dq .. 4 dq + 3) loads 8 parts of its slice at once (every
+// SL-th part), the wave takes their max, and the thread adds them with
+// weights e^(m_s - max) into a running (max, sum, output) that is rescaled
+// when a later chunk raises the max; the SL slices are merged the same way
+// at the end.  SL = 32 (a quarter of the features per workgroup) when there
+// are few (sequence, head) pairs, SL = 8 (all features) otherwise.
+template <int SL>
 __global__ __launch_bounds__(256) void kv_combine_kernel(KvArgs a, const float *__restrict__ part_o,
                                                          const float *__restrict__ part_ml,
                                                          uint16_t *__restrict__ out) {
-  __shared__ float4 acc_s[32][8];
-  __shared__ float2 ml_s[32];
+  constexpr int Q = 256 / SL;                      // feature quads per workgroup
+  __shared__ float4 acc_s[SL][Q];
+  __shared__ float2 ml_s[SL];
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int tid = threadIdx.x;
-  const int ps = tid >> 3, dq = tid & 7;
-  const int f0 = 32 * blockIdx.y;
+  const int ps = tid / Q, dq = tid % Q;
+  const int f0 = 4 * Q * blockIdx.y;
   float M = -__builtin_inff(), L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int s = ps; s < a.ns; s += 32) {
-    const size_t pi = part_index(a, b, s, h);
-    const float2 ml = *reinterpret_cast<const float2 *>(part_ml + 2 * pi);
-    const float4 v = *reinterpret_cast<const float4 *>(part_o + pi * KV_D + f0 + 4 * dq);
-    if (ml.y > 0.f) {
-      const float Mn = fmaxf(M, ml.x);
-      const float ca = __expf(M - Mn), cb = __expf(ml.x - Mn);     // ca = 0 while M = -inf
-      L = fmaf(L, ca, ml.y * cb);
-      acc.x = fmaf(acc.x, ca, v.x * cb);
-      acc.y = fmaf(acc.y, ca, v.y * cb);
-      acc.z = fmaf(acc.z, ca, v.z * cb);
-      acc.w = fmaf(acc.w, ca, v.w * cb);
+  for (int s0 = 0; s0 < a.ns; s0 += 8 * SL) {
+    float2 ml[8];
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int sp = s0 + ps + SL * k;
+      if (sp < a.ns) {
+        const size_t pi = part_index(a, b, sp, h);
+        ml[k] = *reinterpret_cast<const float2 *>(part_ml + 2 * pi);
+        v[k] = *reinterpret_cast<const float4 *>(part_o + pi * KV_D + f0 + 4 * dq);
+      } else {
+        ml[k] = make_float2(-__builtin_inff(), 0.f);
+        v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float cm = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (ml[k].y > 0.f) cm = fmaxf(cm, ml[k].x);
+#pragma unroll
+    for (int d = Q; d < 64; d <<= 1) cm = fmaxf(cm, __shfl_xor(cm, d));
+    const float Mn = fmaxf(M, cm);
+    if (Mn > -__builtin_inff()) {
+      const float ca = __expf(M - Mn);             // 0 while M = -inf
+      L *= ca;
+      acc.x *= ca;
+      acc.y *= ca;
+      acc.z *= ca;
+      acc.w *= ca;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float e = ml[k].y > 0.f ? __expf(ml[k].x - Mn) : 0.f;
+        L = fmaf(e, ml[k].y, L);
+        acc.x = fmaf(e, v[k].x, acc.x);
+        acc.y = fmaf(e, v[k].y, acc.y);
+        acc.z = fmaf(e, v[k].z, acc.z);
+        acc.w = fmaf(e, v[k].w, acc.w);
+      }
       M = Mn;
     }
   }
   acc_s[ps][dq] = acc;
   if (dq == 0) ml_s[ps] = make_float2(M, L);
   __syncthreads();
-  if (tid < 32) {
+  if (tid < 4 * Q) {
     float Mx = -__builtin_inff();
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k)
+    for (int k = 0; k < SL; ++k)
       if (ml_s[k].y > 0.f) Mx = fmaxf(Mx, ml_s[k].x);
     float num = 0.f, den = 0.f;
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < SL; ++k) {
       const float2 ml = ml_s[k];
       if (ml.y > 0.f) {
         const float e = __expf(ml.x - Mx);
@@ -583,15 +664,19 @@ hipError_t launch_kv_g(const KvPlan &p, const gq_kv_cache &c, const void *q, voi
   const uint16_t *qq = reinterpret_cast<const uint16_t *>(q);
   const uint64_t code_bytes = (uint64_t)a.B * a.tp * a.row_bytes;
   const uint64_t groups = (uint64_t)a.B * a.tp * a.row_groups;
-  hipLaunchKernelGGL((kv_packed_kernel<G>), dim3(a.nwp + a.nsp, a.B, p.ngroups), dim3(256), 0, s, a, qq,
+  hipLaunchKernelGGL((kv_packed_kernel<G>), dim3(a.nsp > a.nwp ? a.nsp : a.nwp, a.B, p.ngroups), dim3(256), 0, s, a, qq,
                      reinterpret_cast<const uint8_t *>(c.k_codes), c.k_scales, c.k_zeros,
                      reinterpret_cast<const uint8_t *>(c.v_codes), c.v_scales, c.v_zeros,
                      (uint32_t)code_bytes, (uint32_t)groups, reinterpret_cast<const uint16_t *>(c.k_window),
                      reinterpret_cast<const uint16_t *>(c.v_window), po, pml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kv_combine_kernel, dim3(a.B * a.Hq, KV_D / 32), dim3(256), 0, s, a, po, pml,
-                     reinterpret_cast<uint16_t *>(out));
+  if (a.B * a.Hq >= 512)
+    hipLaunchKernelGGL(kv_combine_kernel<8>, dim3(a.B * a.Hq, 1), dim3(256), 0, s, a, po, pml,
+                       reinterpret_cast<uint16_t *>(out));
+  else
+    hipLaunchKernelGGL(kv_combine_kernel<32>, dim3(a.B * a.Hq, KV_D / 32), dim3(256), 0, s, a, po, pml,
+                       reinterpret_cast<uint16_t *>(out));
   return hipGetLastError();
 }
 

@@ -83,6 +83,10 @@ def gate(out_bits, ref, vmax):
     (1, 32, 8, 0, 40, 4),          # window only
     (1, 12, 6, 300, 9, 4),         # two workgroup head groups, the second with 2 heads
     (1, 2, 1, 500, 3, 2),          # one key/value head
+    (2, 8, 2, 40, 100, 2),         # more window parts than packed splits
+    (16, 32, 8, 70, 5, 4),         # 512 (sequence, head) pairs: combine over all features per workgroup
+    (1, 6, 3, 100, 4, 4),          # 3 key/value heads: a group of 3 in a 4-head tile
+    (2, 14, 7, 90, 3, 2),          # 7 key/value heads, INT2: groups of 4 and 3
 ])
 def test_kv_attention_shapes(B, Hq, Hkv, tp, tw, bits):
     q, kp, vp, kw, vw = kv_inputs(100 + tp + tw, B, Hq, Hkv, tp, tw, bits)
