@@ -541,8 +541,9 @@ constexpr int KV_TW_MAX = 1024;
 // out[b][h] = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s,
 // over the parts that saw tokens; bf16, round to nearest even.  One
 // workgroup per (sequence, head, 4 Q features): thread (part slice ps of
-// SL, features 4 dq .. 4 dq + 3) loads 8 parts of its slice at once (every
-// SL-th part), the wave takes their max, and the thread adds them with
+// SL, features 4 dq .. 4 dq + 3) loads KC parts of its slice at once (every
+// SL-th part; 12 x 32 covers a 32K-token context in one round trip), the
+// wave takes their max, and the thread adds them with
 // weights e^(m_s - max) into a running (max, sum, output) that is rescaled
 // when a later chunk raises the max; the SL slices are merged the same way
 // at the end.  SL = 32 (a quarter of the features per workgroup) when there
@@ -552,6 +553,7 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(KvArgs a, const float *
                                                          const float *__restrict__ part_ml,
                                                          uint16_t *__restrict__ out) {
   constexpr int Q = 256 / SL;                      // feature quads per workgroup
+  constexpr int KC = SL == 32 ? 12 : 8;            // parts per slice loaded at once
   __shared__ float4 acc_s[SL][Q];
   __shared__ float2 ml_s[SL];
   const int bh = blockIdx.x;
@@ -561,46 +563,48 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(KvArgs a, const float *
   const int f0 = 4 * Q * blockIdx.y;
   float M = -__builtin_inff(), L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < a.ns; s0 += 8 * SL) {
-    float2 ml[8];
-    float4 v[8];
+  for (int s0 = 0; s0 < a.ns; s0 += KC * SL) {
+    float2 ml[KC];
+    float4 v[KC];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < KC; ++k) {
+      // unconditional loads (a part past the end reads the last part and is
+      // given a zero sum below): a load under a branch was waited for inside
+      // its branch, one round trip per part
       const int sp = s0 + ps + SL * k;
-      if (sp < a.ns) {
-        const size_t pi = part_index(a, b, sp, h);
-        ml[k] = *reinterpret_cast<const float2 *>(part_ml + 2 * pi);
-        v[k] = *reinterpret_cast<const float4 *>(part_o + pi * KV_D + f0 + 4 * dq);
-      } else {
-        ml[k] = make_float2(-__builtin_inff(), 0.f);
-        v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      const size_t pi = part_index(a, b, sp < a.ns ? sp : a.ns - 1, h);
+      ml[k] = *reinterpret_cast<const float2 *>(part_ml + 2 * pi);
+      v[k] = *reinterpret_cast<const float4 *>(part_o + pi * KV_D + f0 + 4 * dq);
     }
+    __builtin_amdgcn_sched_barrier(0);             // every load issued before the first use
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+      if (s0 + ps + SL * k >= a.ns) ml[k].y = 0.f;
     float cm = -__builtin_inff();
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < KC; ++k)
       if (ml[k].y > 0.f) cm = fmaxf(cm, ml[k].x);
 #pragma unroll
     for (int d = Q; d < 64; d <<= 1) cm = fmaxf(cm, __shfl_xor(cm, d));
+    // no branch here: the loads above would be moved into it
     const float Mn = fmaxf(M, cm);
-    if (Mn > -__builtin_inff()) {
-      const float ca = __expf(M - Mn);             // 0 while M = -inf
-      L *= ca;
-      acc.x *= ca;
-      acc.y *= ca;
-      acc.z *= ca;
-      acc.w *= ca;
+    const float Ms = Mn > -__builtin_inff() ? Mn : 0.f;
+    const float ca = __expf(M - Ms);               // 0 while M = -inf
+    L *= ca;
+    acc.x *= ca;
+    acc.y *= ca;
+    acc.z *= ca;
+    acc.w *= ca;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float e = ml[k].y > 0.f ? __expf(ml[k].x - Mn) : 0.f;
-        L = fmaf(e, ml[k].y, L);
-        acc.x = fmaf(e, v[k].x, acc.x);
-        acc.y = fmaf(e, v[k].y, acc.y);
-        acc.z = fmaf(e, v[k].z, acc.z);
-        acc.w = fmaf(e, v[k].w, acc.w);
-      }
-      M = Mn;
+    for (int k = 0; k < KC; ++k) {
+      const float e = ml[k].y > 0.f ? __expf(ml[k].x - Ms) : 0.f;
+      L = fmaf(e, ml[k].y, L);
+      acc.x = fmaf(e, v[k].x, acc.x);
+      acc.y = fmaf(e, v[k].y, acc.y);
+      acc.z = fmaf(e, v[k].z, acc.z);
+      acc.w = fmaf(e, v[k].w, acc.w);
     }
+    M = Mn;
   }
   acc_s[ps][dq] = acc;
   if (dq == 0) ml_s[ps] = make_float2(M, L);
