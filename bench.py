@@ -281,13 +281,16 @@ def kv_decode(torch, gq):
     """One decode step of attention over a group-wise quantized KV cache:
     Llama-3-8B heads (32 query, 8 key/value, dim 128), the newest 128 tokens
     of a 32768-token context in a dense bf16 window and the rest packed INT4
-    g128 or INT2 g64; and 32 sequences of 2048 tokens (64 in the window).
+    g128 or INT2 g64; and 32 sequences of 2048 tokens (64 in the window);
+    and the 32768-token INT4 step with Llama-3-70B heads (64 query, 8
+    key/value: 8 query heads per key/value head).
     Bytes: packed K and V (codes, scales, zeros), the window, q and out."""
     out = {}
-    Hq, Hkv = 32, 8
-    for name, B, tp, tw, bits in [("kv_decode_32k_int4", 1, 32640, 128, 4),
-                                  ("kv_decode_32k_int2", 1, 32640, 128, 2),
-                                  ("kv_decode_b32_2k_int4", 32, 1984, 64, 4)]:
+    Hkv = 8
+    for name, B, tp, tw, bits, Hq in [("kv_decode_32k_int4", 1, 32640, 128, 4, 32),
+                                      ("kv_decode_32k_int2", 1, 32640, 128, 2, 32),
+                                      ("kv_decode_b32_2k_int4", 32, 1984, 64, 4, 32),
+                                      ("kv_decode_32k_int4_70b_heads", 1, 32640, 128, 4, 64)]:
         gen = torch.Generator(device="cuda")
         gen.manual_seed(7000 + B + bits)
         k = torch.randn((B * tp, Hkv * 128), generator=gen, device="cuda")
@@ -304,7 +307,8 @@ def kv_decode(torch, gq):
         gt.run(20)
         t, _ = gt.run(50)
         nbytes = kp.nbytes() + vp.nbytes() + 2 * kw.numel() * 2 + 2 * q.numel() * 2
-        out[name] = {"batch": B, "t_packed": tp, "t_window": tw, "bits": bits, "us": round(t / 50 * 1e6, 1),
+        out[name] = {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "t_packed": tp, "t_window": tw, "bits": bits,
+                     "us": round(t / 50 * 1e6, 1),
                      "GBps": round(nbytes * 50 / t / 1e9, 1),
                      "frac_hbm": round(nbytes * 50 / t / 1e9 / HBM_PEAK_GBS, 3), "bytes": nbytes}
         del kp, vp, kw, vw, q, o

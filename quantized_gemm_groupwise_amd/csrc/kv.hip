@@ -201,8 +201,9 @@ __device__ __forceinline__ void window_part(const KvArgs &a, int wp, int b, int 
   }
 }
 
+// (8 query heads per key/value head: 3 waves per SIMD asked for, 2 by default)
 template <int G>
-__global__ __launch_bounds__(256) void kv_packed_kernel(KvArgs a, const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 8 ? 3 : 1))) void kv_packed_kernel(KvArgs a, const uint16_t *__restrict__ q,
                                                         const uint8_t *__restrict__ kc,
                                                         const uint16_t *__restrict__ ks,
                                                         const uint8_t *__restrict__ kz,
