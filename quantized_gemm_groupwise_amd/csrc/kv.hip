@@ -12,19 +12,21 @@
 //
 // Work split (flash-decoding).  kv_packed_kernel: a workgroup of 4 waves
 // takes 4 key/value heads of one sequence (one per wave) over a range of at
-// most 256 packed tokens, in two passes over tiles of 32 tokens whose codes
-// reach LDS by buffer loads that write LDS directly, one tile ahead (the K
-// tiles, then the V tiles, as one stream):
+// most 64 packed tokens (2 tiles of 32).  It issues every load of the range
+// at once: K tiles by buffer loads that write LDS directly, V tiles into
+// registers; pass 1 starts once the K half has landed, and the V tiles are
+// written to LDS after it:
 //   pass 1, q . K^T on MFMA 16x16x32 f16: A = q of the G query heads
 //     (rescaled per head by a power of two so that its fp16 form is exact),
 //     B = the codes as exact 1024 + c, and a second MFMA per 32 features with
 //     B = the exact constant -(1024 + z), so the accumulator holds
 //     sum q (c - z) with no rounding before accumulation; the token's scale
 //     is applied in fp32 and the scores are kept in LDS;
-//   one max per head over the range;
+//   one max per head over the range; p = exp(s - max) once per token and
+//     head, in place of the score;
 //   pass 2, P . V on fp32 VALU: lane (features 8f .. 8f + 7, tokens = lane
-//     group mod 4) takes p = exp(s - max) and accumulates p S c per feature
-//     and p S z per head, so the zero point costs one FMA per token and head.
+//     group mod 4) accumulates p S c per feature and p S z per head, so the
+//     zero point costs one FMA per token and head.
 // (An online softmax over each 32-token tile spent most of its time in the
 // per-tile cross-lane reductions.)  Each workgroup writes its (max, sum,
 // unnormalised output) per head; workgroup s then does the same for the
