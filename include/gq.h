@@ -65,7 +65,8 @@ typedef enum gq_status {
   GQ_ERR_ALIGNMENT = 4,  /* a device pointer is not 16-byte aligned             */
   GQ_ERR_DTYPE = 5,      /* unsupported dtype for this argument                 */
   GQ_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required             */
-  GQ_ERR_HIP = 7         /* the HIP runtime refused a launch                    */
+  GQ_ERR_HIP = 7,        /* the HIP runtime refused a launch                    */
+  GQ_ERR_TOO_LARGE = 8   /* gq_linear_noalloc: scratch need above the static size */
 } gq_status;
 
 typedef enum gq_dtype { GQ_BF16 = 0, GQ_FP16 = 1, GQ_FP32 = 2 } gq_dtype;
@@ -171,6 +172,26 @@ gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype
 gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                     void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* gq_linear without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory around the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels and results as gq_linear (bit for bit); the
+ * workspace those kernels need is a static device array of
+ * GQ_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  The array is scratch: no kernel needs it
+ * initialised, and each call overwrites what the previous call left.
+ * Calls on one GPU that may overlap in time (on different streams) share
+ * the array and race: the caller orders them.  A call whose workspace need
+ * (gq_linear_workspace_bytes) exceeds GQ_NOALLOC_SCRATCH_BYTES returns
+ * GQ_ERR_TOO_LARGE before anything is enqueued; M <= 4, the small-batch
+ * path on most layers and prefill GEMMs up to about M * K = 2^24 fit.
+ * The first call on a device resolves that device's array address
+ * (hipGetSymbolAddress, with the device current); no call allocates. */
+#define GQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+gq_status gq_linear_noalloc(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
+                            const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                            void *y, void *stream);
 
 /* Workspace gq_linear_dx needs for this layout, M and dtype (HOST output
  * *bytes; may be 0).  Returns GQ_ERR_SHAPE where gq_linear_dx would (N not a

@@ -23,7 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgq.so")
 
 GQ_OK, GQ_ERR_NULL_ARG, GQ_ERR_SHAPE, GQ_ERR_BITS, GQ_ERR_ALIGNMENT, GQ_ERR_DTYPE, \
-    GQ_ERR_WORKSPACE, GQ_ERR_HIP = range(8)
+    GQ_ERR_WORKSPACE, GQ_ERR_HIP, GQ_ERR_TOO_LARGE = range(9)
+GQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 GQ_BF16, GQ_FP16, GQ_FP32 = 0, 1, 2
 GQ_FLAG_NONFINITE = 1
 GQ_FLAG_SCALE_OVERFLOW = 2
@@ -32,7 +33,7 @@ GROUP = {4: 128, 2: 64}
 
 # Every symbol include/gq.h declares.
 EXPORTS = ("gq_packed_bytes", "gq_quantize_pack", "gq_fake_quant", "gq_dequant",
-           "gq_linear_workspace_bytes", "gq_linear", "gq_linear_dx_workspace_bytes",
+           "gq_linear_workspace_bytes", "gq_linear", "gq_linear_noalloc", "gq_linear_dx_workspace_bytes",
            "gq_linear_dx", "gq_kv_attention_workspace_bytes", "gq_kv_attention", "gq_status_string")
 
 
@@ -77,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gq_dequant": ([L, VP, VP, VP, ctypes.c_int, VP, VP], ctypes.c_int),
         "gq_linear_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
         "gq_linear": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
+        "gq_linear_noalloc": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP], ctypes.c_int),
         "gq_linear_dx_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
         "gq_linear_dx": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
         "gq_kv_attention_workspace_bytes": ([P(gq_kv_cache), P(S)], ctypes.c_int),
@@ -149,6 +151,13 @@ def gq_linear(layout, M, act, x_ptr, codes_ptr, scales_ptr, zeros_ptr, y_ptr, ws
     return load_library().gq_linear(ctypes.byref(layout), int(M), int(act), x_ptr, codes_ptr,
                                     scales_ptr, zeros_ptr, y_ptr, ws_ptr, int(ws_bytes),
                                     _stream(stream))
+
+
+def gq_linear_noalloc(layout, M, act, x_ptr, codes_ptr, scales_ptr, zeros_ptr, y_ptr,
+                      stream=None) -> int:
+    return load_library().gq_linear_noalloc(ctypes.byref(layout), int(M), int(act), x_ptr,
+                                            codes_ptr, scales_ptr, zeros_ptr, y_ptr,
+                                            _stream(stream))
 
 
 def gq_linear_dx_workspace_bytes(layout, M: int, act: int = GQ_BF16) -> int:

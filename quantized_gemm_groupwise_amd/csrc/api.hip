@@ -3,9 +3,17 @@
 // enqueued; nothing here allocates, prints or aborts.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "gq_internal.h"
 
 using namespace gq;
+
+// Scratch memory of gq_linear_noalloc: a static device array (each GPU the
+// library runs on holds its own copy until the process ends).  Host code
+// never uses this name as an address: the device address of the current
+// GPU's copy comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[GQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -22,6 +30,53 @@ gq_status launched(hipError_t e, hipStream_t s) {
   return GQ_OK;
 }
 
+// Device address of the current GPU's scratch array, resolved once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];
+
+gq_status scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GQ_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return GQ_OK;
+}
+
+// Argument checks of gq_linear that do not concern the workspace.  *done is
+// set when there is no work (M == 0 or N == 0).
+gq_status check_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
+                       const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                       const void *y, LayoutDev *L, bool *done) {
+  gq_status st = make_layout(layout, L);
+  if (st != GQ_OK) return st;
+  if (M < 0) return GQ_ERR_SHAPE;
+  if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  *done = M == 0 || L->N == 0;
+  if (*done) return GQ_OK;
+  if ((st = check_ptr16(x)) != GQ_OK) return st;
+  if ((st = check_ptr16(codes)) != GQ_OK) return st;
+  if (!scales || !zeros || !y) return GQ_ERR_NULL_ARG;
+  if (((uintptr_t)scales & 1u) || ((uintptr_t)y & 1u)) return GQ_ERR_ALIGNMENT;
+  return GQ_OK;
+}
+
+// The kernels of gq_linear by M (workspace already checked).
+gq_status dispatch_linear(const LayoutDev &L, int32_t M, gq_dtype act, const void *x,
+                          const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                          void *y, void *workspace, hipStream_t s) {
+  if (M <= kGemvMaxM)
+    return launched(launch_gemv(L, M, act, x, codes, scales, zeros, y, s), s);
+  if (skinny_supported(L, M))
+    return launched(launch_skinny(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
+  return launched(launch_gemm(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
+}
 
 }  // namespace
 
@@ -105,26 +160,31 @@ gq_status gq_linear(const gq_layout *layout, int32_t M, gq_dtype act, const void
                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                     void *y, void *workspace, size_t workspace_bytes, void *stream) {
   LayoutDev L;
-  gq_status st = make_layout(layout, &L);
-  if (st != GQ_OK) return st;
-  if (M < 0) return GQ_ERR_SHAPE;
-  if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
-  if (M == 0 || L.N == 0) return GQ_OK;
-  if ((st = check_ptr16(x)) != GQ_OK) return st;
-  if ((st = check_ptr16(codes)) != GQ_OK) return st;
-  if (!scales || !zeros || !y) return GQ_ERR_NULL_ARG;
-  if (((uintptr_t)scales & 1u) || ((uintptr_t)y & 1u)) return GQ_ERR_ALIGNMENT;
+  bool done = false;
+  gq_status st = check_linear(layout, M, act, x, codes, scales, zeros, y, &L, &done);
+  if (st != GQ_OK || done) return st;
   const size_t need = linear_workspace_bytes(L, M, act);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return GQ_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 255u) return GQ_ERR_ALIGNMENT;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (M <= kGemvMaxM)
-    return launched(launch_gemv(L, M, act, x, codes, scales, zeros, y, s), s);
-  if (skinny_supported(L, M))
-    return launched(launch_skinny(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
-  return launched(launch_gemm(L, M, act, x, codes, scales, zeros, y, workspace, s), s);
+  return dispatch_linear(L, M, act, x, codes, scales, zeros, y, workspace, s);
+}
+
+gq_status gq_linear_noalloc(const gq_layout *layout, int32_t M, gq_dtype act, const void *x,
+                            const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                            void *y, void *stream) {
+  LayoutDev L;
+  bool done = false;
+  gq_status st = check_linear(layout, M, act, x, codes, scales, zeros, y, &L, &done);
+  if (st != GQ_OK || done) return st;
+  const size_t need = linear_workspace_bytes(L, M, act);
+  if (need > (size_t)GQ_NOALLOC_SCRATCH_BYTES) return GQ_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  if (need > 0 && (st = scratch_address(&ws)) != GQ_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return dispatch_linear(L, M, act, x, codes, scales, zeros, y, ws, s);
 }
 
 gq_status gq_linear_dx_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
@@ -209,6 +269,8 @@ const char *gq_status_string(gq_status status) {
     case GQ_ERR_DTYPE: return "GQ_ERR_DTYPE: unsupported dtype";
     case GQ_ERR_WORKSPACE: return "GQ_ERR_WORKSPACE: workspace missing or too small";
     case GQ_ERR_HIP: return "GQ_ERR_HIP: the HIP runtime refused a launch";
+    case GQ_ERR_TOO_LARGE:
+      return "GQ_ERR_TOO_LARGE: the call needs more scratch than the library's static buffer holds";
   }
   return "unknown gq_status";
 }

@@ -186,8 +186,24 @@ def test_workspace_sizes():
     assert ws >= 2 * 8 * 256 * 4 and ws % 256 == 0
 
 
+def test_noalloc_refusals_before_launch(lib):
+    """gq_linear_noalloc: the checks of gq_linear, then GQ_ERR_TOO_LARGE for a
+    call whose workspace need exceeds the static scratch, all on the host."""
+    lay = gq.make_layout(4096, 1024, 1024, [4])
+    A, bad = 0x10000, 0x10008
+    NA = lambda lay, M, act, x, y: lib.gq_linear_noalloc(ctypes.byref(lay), M, act, x, A, A, A, y, None)
+    assert NA(lay, -1, gq.GQ_BF16, A, A) == gq.GQ_ERR_SHAPE
+    assert NA(lay, 1, gq.GQ_FP32, A, A) == gq.GQ_ERR_DTYPE
+    assert NA(lay, 1, gq.GQ_BF16, bad, A) == gq.GQ_ERR_ALIGNMENT
+    assert NA(lay, 1, gq.GQ_BF16, A, None) == gq.GQ_ERR_NULL_ARG
+    assert NA(lay, 0, gq.GQ_BF16, None, None) == gq.GQ_OK
+    big = gq.make_layout(28672, 8192, 8192, [2])
+    assert gq.gq_linear_workspace_bytes(big, 2048) > gq.GQ_NOALLOC_SCRATCH_BYTES
+    assert NA(big, 2048, gq.GQ_BF16, A, A) == gq.GQ_ERR_TOO_LARGE
+
+
 def test_status_strings():
-    for st in range(8):
+    for st in range(9):
         assert gq.gq_status_string(st).startswith("GQ_")
     assert "unknown" in gq.gq_status_string(99)
 
