@@ -71,9 +71,14 @@ typedef enum gq_status {
 
 typedef enum gq_dtype { GQ_BF16 = 0, GQ_FP16 = 1, GQ_FP32 = 2 } gq_dtype;
 
-/* Device flag bits OR-ed into *flags by gq_quantize_pack. */
+/* Device flag bits OR-ed into *flags by gq_quantize_pack and gq_fake_quant. */
 #define GQ_FLAG_NONFINITE 1u      /* a group held NaN or Inf; its codes are unspecified   */
 #define GQ_FLAG_SCALE_OVERFLOW 2u /* (hi-lo)/(2^b-1) rounded to fp16 infinity (> 65504)   */
+/* A finite group whose zero point rint(-lo/S) fell outside [0, 2^b - 1] and
+ * was clamped (its values all of one sign, away from 0): its codes saturate
+ * at the clamp, so its largest (or smallest) values dequantize with an error
+ * above S/2.  Reported, not an error: the format keeps z in the code range. */
+#define GQ_FLAG_ZERO_CLAMPED 4u
 
 /* Largest number of bit-width blocks in one layout. */
 #define GQ_MAX_BLOCKS 1024

@@ -32,7 +32,9 @@ notes of the repository):
     scale; a scale that rounds to zero (hi == lo, or fp16 underflow) is
     replaced by 1.0; an fp16 overflow sets FLAG_SCALE_OVERFLOW.
   * z = clamp(round(-x_min/S), 0, 2^b - 1), stored as uint8; codes are
-    clamp(round(x/S) + z, 0, 2^b - 1).
+    clamp(round(x/S) + z, 0, 2^b - 1).  A group whose zero point was clamped
+    (all values of one sign, away from 0) is reported by FLAG_ZERO_CLAMPED:
+    its codes saturate, and the S/2 error bound does not hold for it.
   * divisions are IEEE fp32 divisions (correctly rounded), not a reciprocal
     multiply.
   * groups run along K (the input dimension) of W stored [N][K]; codes are
@@ -55,6 +57,11 @@ import numpy as np
 
 FLAG_NONFINITE = 1
 FLAG_SCALE_OVERFLOW = 2
+# A finite group whose zero point round(-x_min/S) fell outside 0..2^b-1 and
+# was clamped: a group that does not straddle zero (all values of one sign,
+# away from 0).  Its codes saturate at the clamp, so neither "x_min -> 0,
+# x_max -> 2^b-1" nor the S/2 error bound holds for it; the flag reports it.
+FLAG_ZERO_CLAMPED = 4
 
 # [GB] two-stage quantization paragraph: INT4 uses groups of 128, INT2 groups of 64.
 GROUP_SIZE = {4: 128, 2: 64}
@@ -94,6 +101,7 @@ def quantize_groups(v, bits: int, clamp_zero: bool = True):
         s16 = np.where(s16 == np.float16(0), np.float16(1.0), s16)
         S = s16.astype(np.float32)                 # exact widening
         z = np.rint(-lo / S)                       # z = round(0 - x_min / s)
+        zc = (z < 0) | (z > qm)                    # outside the integer range
         if clamp_zero:
             z = np.clip(z, np.float32(0), qm)
         q = np.rint(v / S[:, None])                # round(x / s), fp32 divide
@@ -103,6 +111,8 @@ def quantize_groups(v, bits: int, clamp_zero: bool = True):
     finite = np.isfinite(v).all(axis=1)
     gflags = np.where(finite, 0, FLAG_NONFINITE)
     gflags = gflags | np.where(finite & np.isinf(s16), FLAG_SCALE_OVERFLOW, 0)
+    if clamp_zero:
+        gflags = gflags | np.where(finite & ~np.isinf(s16) & zc, FLAG_ZERO_CLAMPED, 0)
     c = np.where(np.isnan(c), 0.0, c)
     z64 = np.where(np.isnan(z), 0.0, z).astype(np.int64)
     codes = c.astype(np.int64)

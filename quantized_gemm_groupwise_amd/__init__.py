@@ -28,13 +28,15 @@ GQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 GQ_BF16, GQ_FP16, GQ_FP32 = 0, 1, 2
 GQ_FLAG_NONFINITE = 1
 GQ_FLAG_SCALE_OVERFLOW = 2
+GQ_FLAG_ZERO_CLAMPED = 4
 GQ_MAX_BLOCKS = 1024
 GROUP = {4: 128, 2: 64}
 
 # Every symbol include/gq.h declares.
 EXPORTS = ("gq_packed_bytes", "gq_quantize_pack", "gq_fake_quant", "gq_dequant",
            "gq_linear_workspace_bytes", "gq_linear", "gq_linear_noalloc", "gq_linear_dx_workspace_bytes",
-           "gq_linear_dx", "gq_kv_attention_workspace_bytes", "gq_kv_attention", "gq_status_string")
+           "gq_linear_dx", "gq_group_plan_bytes", "gq_group_plan", "gq_linear_group",
+           "gq_kv_attention_workspace_bytes", "gq_kv_attention", "gq_status_string")
 
 
 class GqError(RuntimeError):

@@ -6,7 +6,9 @@
 // "大模型量化实战：从原理到4-bit部署的完整指南": s = (x_max - x_min)/(2^b - 1),
 // z = round(-x_min/s), Q(x) = round(x/s) + z.  The scale is stored as fp16
 // (nearest even) and the zero point and codes are computed from the stored
-// scale; z and the codes are clamped to [0, 2^b - 1].
+// scale; z and the codes are clamped to [0, 2^b - 1].  A group whose zero
+// point had to be clamped (all its values of one sign, away from 0) sets
+// GQ_FLAG_ZERO_CLAMPED: its codes saturate at the clamp.
 //
 // Dequantizer: (q - z) * s, the "Zero Point" formula of "Low-bit
 // Quantization: Slimming Large Models to the Extreme".
@@ -72,7 +74,9 @@ __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, in
   _Float16 s16 = (_Float16)s32;              // nearest even
   if (s16 == (_Float16)0.0f) s16 = (_Float16)1.0f;
   const float S = (float)s16;
-  const float z = fminf(fmaxf(rintf(-lo / S), 0.f), qm);
+  const float zr = rintf(-lo / S);
+  const float z = fminf(fmaxf(zr, 0.f), qm);
+  const bool zclamp = zr < 0.f || zr > qm;   // a group of one sign, away from 0
   uint32_t packed = 0;
   float fq[8];
 #pragma unroll
@@ -101,6 +105,7 @@ __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, in
     if (flags) {
       uint32_t f = finite ? 0u : GQ_FLAG_NONFINITE;
       if (finite && __builtin_isinf(S)) f |= GQ_FLAG_SCALE_OVERFLOW;
+      else if (finite && zclamp) f |= GQ_FLAG_ZERO_CLAMPED;
       if (f && active) atomicOr(flags, f);
     }
     return;
@@ -120,6 +125,7 @@ __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, in
   if (flags) {
     uint32_t f = finite ? 0u : GQ_FLAG_NONFINITE;
     if (finite && __builtin_isinf(S)) f |= GQ_FLAG_SCALE_OVERFLOW;
+    else if (finite && zclamp) f |= GQ_FLAG_ZERO_CLAMPED;
     if (f) atomicOr(flags, f);
   }
 }

@@ -180,7 +180,8 @@ def test_fake_quant_flags_and_edge_groups():
     torch.cuda.synchronize()
     exp = O.fake_quant(W, L)
     assert np.array_equal(out.cpu().numpy()[:4], exp[:4])
-    assert int(flags.item()) == O.FLAG_NONFINITE
+    # rows 1 and 2 do not straddle zero: their zero points clamp
+    assert int(flags.item()) == O.FLAG_NONFINITE | O.FLAG_ZERO_CLAMPED == O.quantize_pack(W, L).flags
 
 
 # ------------------------------------------------------------- linear

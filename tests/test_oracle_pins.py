@@ -94,6 +94,45 @@ def test_exact_scale_groups(bits):
             assert (c[i] - z) % 2 == 0 and abs(2 * (c[i] - z) - n2) == 1
 
 
+# ------------------------------------------------- one-sided groups
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_zero_clamp_flag_one_sided_groups(bits):
+    """A group that does not straddle zero has round(-x_min/S) outside the
+    code range ([QP] 2.2 keeps z inside it), so z is clamped and the codes
+    saturate; such a group, and only such a group, carries FLAG_ZERO_CLAMPED.
+    Constructed with an exactly representable scale S = 2^-4: the values
+    below are multiples of S/8, so every quotient v/S is exact."""
+    Q = O.qmax(bits)
+    g = O.GROUP_SIZE[bits]
+    S0 = 2.0 ** -4
+    def grp(lo_steps, hi_steps):
+        v = np.full(g, lo_steps * S0, np.float32)
+        v[1] = hi_steps * S0
+        v[2:] = np.linspace(lo_steps, hi_steps, g - 2).round(3).astype(np.float32) * np.float32(S0)
+        v[2:] = np.clip(np.round(v[2:] / (S0 / 8)) * (S0 / 8), lo_steps * S0, hi_steps * S0)
+        return v
+    rows = [grp(5, 5 + Q),        # all positive: -lo/S = -5 -> z clamps to 0
+            grp(-5 - Q, -5),      # all negative: -lo/S = 5 + Q -> z clamps to Q
+            grp(-2, Q - 2),       # straddles zero: z = 2, no flag
+            grp(0, Q)]            # touches zero: z = 0 exactly, no flag
+    q = O.quantize_groups(np.stack(rows), bits)
+    assert np.all(q["scale"].astype(np.float64) == S0)
+    assert list(q["group_flags"]) == [O.FLAG_ZERO_CLAMPED, O.FLAG_ZERO_CLAMPED, 0, 0]
+    assert q["flags"] == O.FLAG_ZERO_CLAMPED
+    assert list(q["zero"]) == [0, Q, 2, 0]
+    c = q["codes"].astype(np.int64)
+    # positive group: codes are round(v/S) clamped at Q, so the largest values saturate
+    assert c[0, 0] == min(5, Q) and c[0, 1] == Q
+    # negative group: codes round(v/S) + Q clamped at 0
+    assert c[1, 0] == 0 and c[1, 1] == max(Q - 5, 0)
+    # the straddling groups keep the endpoint and S/2 statements
+    for r in (2, 3):
+        assert c[r, 0] == 0 and c[r, 1] == Q
+        err = np.abs((c[r] - q["zero"][r]) * S0 - rows[r].astype(np.float64))
+        assert np.all(err <= S0 / 2)
+
+
 # ------------------------------------------------- P3 random-data endpoints
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -114,6 +153,7 @@ def test_endpoint_and_error_bounds_random(bits):
     lo, hi = q["lo"].astype(np.float64), q["hi"].astype(np.float64)
     raw_z = np.rint(-q["lo"] / q["scale"].astype(np.float32))
     assert np.all(raw_z == z)                          # no clamped zero on this data
+    assert q["flags"] == 0                             # and none reported
     rows = np.arange(G.shape[0])
     c_lo = c[rows, np.argmin(G, axis=1)]
     c_hi = c[rows, np.argmax(G, axis=1)]
