@@ -233,6 +233,29 @@ def _cuda(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_tensor(t: torch.Tensor, name: str, shape, dtype, device):
+    """Refuse, before any call into the C ABI, a tensor whose shape, dtype,
+    device or layout differs from what the kernels will read or write: the
+    ABI sees only a pointer."""
+    _cuda(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _check_packed(p: "Packed", device, name="packed"):
+    cb, sb, zb = gq_packed_bytes(p.layout)
+    if p.codes.numel() < cb or p.scales.numel() * 2 < sb or p.zeros.numel() < zb:
+        raise ValueError(f"{name}: buffers smaller than its layout needs")
+    for t, n in ((p.codes, "codes"), (p.scales, "scales"), (p.zeros, "zeros")):
+        _cuda(t, f"{name}.{n}")
+        if t.device != torch.device(device):
+            raise ValueError(f"{name}.{n} must be on {device}, got {t.device}")
+
+
 def empty_packed(K: int, N: int, bits, block_n: int | None = None, device="cuda") -> Packed:
     bits = [int(bits)] if isinstance(bits, int) else [int(b) for b in bits]
     block_n = N if block_n is None else int(block_n)
@@ -291,16 +314,26 @@ def fake_quant(w: torch.Tensor, bits, block_n: int | None = None, dtype=torch.fl
 
 
 _ws_cache: dict = {}
+_ws_retired: list = []
 
 
-def workspace(nbytes: int, device) -> torch.Tensor | None:
-    """A cached device workspace of at least nbytes (per device)."""
+def workspace(nbytes: int, device, stream=None) -> torch.Tensor | None:
+    """A cached device workspace of at least nbytes, one per (device, stream):
+    calls on different streams never share scratch, and calls on one stream
+    are ordered by it.  A buffer that is outgrown is kept alive (never
+    returned to the allocator), since a HIP graph captured earlier, or a
+    kernel still queued, may hold its address."""
     if nbytes == 0:
         return None
-    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, _stream(stream))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if ws is not None:
+            _ws_retired.append(ws)
+            nbytes = max(nbytes, 2 * ws.numel())
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device("cuda", idx))
         _ws_cache[key] = ws
     return ws
 
@@ -315,12 +348,16 @@ def linear(x: torch.Tensor, p: Packed, out: torch.Tensor | None = None, ws: torc
     if act not in (GQ_BF16, GQ_FP16):
         raise ValueError("x must be bfloat16 or float16")
     M = x.shape[0]
+    _check_packed(p, x.device)
     y = torch.empty((M, p.N), dtype=x.dtype, device=x.device) if out is None else out
+    _check_tensor(y, "out", (M, p.N), x.dtype, x.device)
     need = gq_linear_workspace_bytes(p.layout, M, act)
     if ws is None:
-        ws = workspace(need, x.device)
+        ws = workspace(need, x.device, stream)
+    elif ws.numel() * ws.element_size() < need or not ws.is_cuda or ws.device != x.device:
+        raise ValueError(f"ws must be a device buffer on {x.device} of at least {need} bytes")
     wptr = ws.data_ptr() if ws is not None else None
-    wbytes = ws.numel() if ws is not None else 0
+    wbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(gq_linear(p.layout, M, act, x.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
                      p.zeros.data_ptr(), y.data_ptr(), wptr, wbytes, stream), "gq_linear")
     return y
@@ -337,15 +374,73 @@ def linear_dx(dy: torch.Tensor, p: Packed, out: torch.Tensor | None = None,
     if act not in (GQ_BF16, GQ_FP16):
         raise ValueError("dy must be bfloat16 or float16")
     M = dy.shape[0]
+    _check_packed(p, dy.device)
     dx = torch.empty((M, p.K), dtype=dy.dtype, device=dy.device) if out is None else out
+    _check_tensor(dx, "out", (M, p.K), dy.dtype, dy.device)
     need = gq_linear_dx_workspace_bytes(p.layout, M, act)
     if ws is None:
-        ws = workspace(need, dy.device)
+        ws = workspace(need, dy.device, stream)
+    elif ws.numel() * ws.element_size() < need or not ws.is_cuda or ws.device != dy.device:
+        raise ValueError(f"ws must be a device buffer on {dy.device} of at least {need} bytes")
     wptr = ws.data_ptr() if ws is not None else None
-    wbytes = ws.numel() if ws is not None else 0
+    wbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(gq_linear_dx(p.layout, M, act, dy.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
                         p.zeros.data_ptr(), dx.data_ptr(), wptr, wbytes, stream), "gq_linear_dx")
     return dx
+
+
+class GroupPlan:
+    """A grouped decode call: the host plan bytes, their device copy, and the
+    tensors the plan points to (kept alive with it)."""
+
+    def __init__(self, host, dev, keep, M, act):
+        self.host = host
+        self.dev = dev
+        self._keep = keep
+        self.M = M
+        self.act = act
+
+
+def group_plan(items, M: int | None = None) -> GroupPlan:
+    """Plan y_i = x_i . W_hat_i^T for a list of (x, packed, y) triples (bf16 or
+    fp16 x [M][K], M <= 4, outputs preallocated [M][N]); run it with
+    linear_group(plan)."""
+    if not items:
+        raise ValueError("group_plan needs at least one (x, packed, y)")
+    x0 = items[0][0]
+    M = x0.shape[0] if M is None else int(M)
+    act = _DT.get(x0.dtype)
+    if act not in (GQ_BF16, GQ_FP16):
+        raise ValueError("x must be bfloat16 or float16")
+    dev = x0.device
+    citems, keep = [], []
+    for i, (x, p, y) in enumerate(items):
+        _cuda(x, f"x[{i}]")
+        _cuda(y, f"y[{i}]")
+        if x.dtype != x0.dtype or y.dtype != x0.dtype:
+            raise ValueError(f"item {i}: x and y must share the dtype of the first x")
+        if tuple(x.shape) != (M, p.K) or tuple(y.shape) != (M, p.N):
+            raise ValueError(f"item {i}: x must be [{M}][{p.K}] and y [{M}][{p.N}]")
+        if x.device != dev or y.device != dev or p.codes.device != dev:
+            raise ValueError(f"item {i}: every tensor must be on {dev}")
+        citems.append(gq_group_item(p.layout, x.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(),
+                                    p.zeros.data_ptr(), y.data_ptr()))
+        keep.append((x, p, y))
+    n = gq_group_plan_bytes(citems, M, act)
+    host = ctypes.create_string_buffer(n)
+    _check(gq_group_plan(citems, M, act, host, n), "gq_group_plan")
+    buf = torch.frombuffer(bytearray(host.raw), dtype=torch.uint8)
+    plan_dev = torch.empty(n + 16, dtype=torch.uint8, device=dev)
+    off = (-plan_dev.data_ptr()) % 16
+    plan_dev = plan_dev[off:off + n]
+    plan_dev.copy_(buf)
+    torch.cuda.synchronize(dev)
+    return GroupPlan(host, plan_dev, keep, M, act)
+
+
+def linear_group(plan: GroupPlan, stream=None) -> None:
+    """Run every linear of a grouped plan (outputs land in the plan's y)."""
+    _check(gq_linear_group(plan.host, plan.dev.data_ptr(), stream), "gq_linear_group")
 
 
 def kv_cache(batch: int, q_heads: int, kv_heads: int, k: "Packed | None", v: "Packed | None",
@@ -353,11 +448,28 @@ def kv_cache(batch: int, q_heads: int, kv_heads: int, k: "Packed | None", v: "Pa
     """Describe a KV cache: k / v are packed caches (quantize_pack of the fp32
     cache [batch * t_packed][kv_heads * 128], one row per token) or None;
     k_window / v_window are bf16 [batch][t_window][kv_heads][128] or None."""
-    tp = 0 if k is None else k.N // batch
-    tw = 0 if k_window is None else k_window.shape[1]
-    bits = 4
+    if (k is None) != (v is None) or (k_window is None) != (v_window is None):
+        raise ValueError("k and v (and k_window and v_window) are given together or not at all")
+    if batch < 1 or kv_heads < 1:
+        raise ValueError("batch and kv_heads must be positive")
+    F = kv_heads * 128
+    tp, bits = 0, 4
     if k is not None:
-        bits = int(k.bits[0])
+        for name, c in (("k", k), ("v", v)):
+            if c.K != F or c.block_n != c.N or len(c.bits) != 1:
+                raise ValueError(f"{name} must be a uniform packed cache of rows of {F} features")
+            if c.N % batch != 0:
+                raise ValueError(f"{name}: {c.N} rows do not split into {batch} sequences")
+        if (v.N, v.bits) != (k.N, k.bits):
+            raise ValueError("k and v must have the same rows and bit-width")
+        tp, bits = k.N // batch, int(k.bits[0])
+        _check_packed(k, k.codes.device, "k")
+        _check_packed(v, k.codes.device, "v")
+    tw = 0
+    if k_window is not None:
+        tw = k_window.shape[1] if k_window.dim() == 4 else -1
+        for name, w in (("k_window", k_window), ("v_window", v_window)):
+            _check_tensor(w, name, (batch, tw, kv_heads, 128), torch.bfloat16, k_window.device)
     c = gq_kv_cache(batch, q_heads, kv_heads, 128, bits, tp, tw,
                     k.codes.data_ptr() if k is not None else None,
                     k.scales.data_ptr() if k is not None else None,
@@ -375,13 +487,19 @@ def kv_attention(q: torch.Tensor, cache: gq_kv_cache, out: torch.Tensor | None =
                  ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """One decode step of attention of bf16 q [batch][q_heads][128] over the
     cache; returns bf16 [batch][q_heads][128]."""
-    _cuda(q, "q")
-    if q.dtype != torch.bfloat16 or tuple(q.shape) != (cache.batch, cache.q_heads, 128):
-        raise ValueError("q must be bf16 [batch][q_heads][128]")
+    _check_tensor(q, "q", (cache.batch, cache.q_heads, 128), torch.bfloat16, q.device)
     o = torch.empty_like(q) if out is None else out
+    _check_tensor(o, "out", (cache.batch, cache.q_heads, 128), torch.bfloat16, q.device)
+    for t in getattr(cache, "_keep", ()):
+        if isinstance(t, Packed):
+            _check_packed(t, q.device, "cache")
+        elif isinstance(t, torch.Tensor) and t.device != q.device:
+            raise ValueError(f"the cache must be on {q.device}")
     need = gq_kv_attention_workspace_bytes(cache)
     if ws is None:
-        ws = workspace(need, q.device)
+        ws = workspace(need, q.device, stream)
+    elif ws.numel() * ws.element_size() < need or not ws.is_cuda or ws.device != q.device:
+        raise ValueError(f"ws must be a device buffer on {q.device} of at least {need} bytes")
     _check(gq_kv_attention(cache, q.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(), stream),
            "gq_kv_attention")
     return o
