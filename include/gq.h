@@ -198,6 +198,50 @@ gq_status gq_linear_noalloc(const gq_layout *layout, int32_t M, gq_dtype act, co
                             const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                             void *y, void *stream);
 
+/* ---------------------------------------------------------- grouped decode
+ * Many independent decode linears (M <= 4) in as few launches as their
+ * kernel classes allow, for a Layer-mix model pass (GreenBitAI's Layer-mix
+ * layout: one bit-width per linear; the survey review, section 6.2: the
+ * speed-up of weight-only quantization is the weight bytes not moved, so a
+ * decode pass should stream its packed weights without a launch ramp and
+ * tail per linear).  Each output is y_i = x_i . W_hat_i^T exactly as
+ * gq_linear computes it for M <= 4 (same arithmetic, same rounding, bit for
+ * bit).  Linears may mix INT4, INT2 and Channel-mix layouts and shapes; they
+ * share M and the activation dtype.  Outputs must not alias inputs or each
+ * other: the linears of one call run concurrently.
+ *
+ * Use: gq_group_plan_bytes, then gq_group_plan into a HOST buffer of that
+ * size; copy the bytes unchanged into DEVICE memory (16-byte aligned) once;
+ * then every gq_linear_group(plan, plan_dev, stream) runs the whole group.
+ * The plan records the device pointers of every item, so it is rebuilt when
+ * a buffer moves.  No workspace is needed. */
+typedef struct gq_group_item {
+  gq_layout layout;       /* bit map of the linear (HOST bits, read by gq_group_plan only) */
+  const void *x;          /* DEVICE [M][K] act, 16-byte aligned                        */
+  const uint32_t *codes;  /* DEVICE packed codes, 16-byte aligned                      */
+  const uint16_t *scales; /* DEVICE fp16 bit patterns, 2-byte aligned                  */
+  const uint8_t *zeros;   /* DEVICE uint8                                              */
+  void *y;                /* DEVICE [M][N] act, 2-byte aligned, written                */
+} gq_group_item;
+
+/* Bytes of the plan of `count` items (HOST output *bytes).  Checks every item
+ * as gq_linear would (GQ_ERR_SHAPE also for M outside 1..4 or count outside
+ * 1..65535).  Pure host computation. */
+gq_status gq_group_plan_bytes(int32_t count, const gq_group_item *items, int32_t M, gq_dtype act,
+                              size_t *bytes);
+
+/* Encode the plan into `plan` (HOST, plan_bytes >= gq_group_plan_bytes).
+ * Pure host computation; returns the same errors as gq_group_plan_bytes and
+ * GQ_ERR_WORKSPACE when plan_bytes is too small. */
+gq_status gq_group_plan(int32_t count, const gq_group_item *items, int32_t M, gq_dtype act,
+                        void *plan, size_t plan_bytes);
+
+/* Run every linear of a plan.  plan: the HOST plan (launch configuration);
+ * plan_dev: a DEVICE byte copy of it, 16-byte aligned, which the kernels
+ * read (it must equal `plan`; it is not checked on the device).  Returns
+ * GQ_ERR_SHAPE if `plan` is not a plan of this library version. */
+gq_status gq_linear_group(const void *plan, const void *plan_dev, void *stream);
+
 /* Workspace gq_linear_dx needs for this layout, M and dtype (HOST output
  * *bytes; may be 0).  Returns GQ_ERR_SHAPE where gq_linear_dx would (N not a
  * multiple of 8, or buffers past 2 GiB).  Pure host computation. */

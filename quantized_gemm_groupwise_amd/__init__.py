@@ -50,6 +50,11 @@ class gq_layout(ctypes.Structure):
                 ("bits", ctypes.POINTER(ctypes.c_uint8))]
 
 
+class gq_group_item(ctypes.Structure):
+    _fields_ = [("layout", gq_layout), ("x", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
 class gq_kv_cache(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32), ("t_packed", ctypes.c_int32),
@@ -83,6 +88,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gq_linear_noalloc": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP], ctypes.c_int),
         "gq_linear_dx_workspace_bytes": ([L, I32, ctypes.c_int, P(S)], ctypes.c_int),
         "gq_linear_dx": ([L, I32, ctypes.c_int, VP, VP, VP, VP, VP, VP, S, VP], ctypes.c_int),
+        "gq_group_plan_bytes": ([I32, P(gq_group_item), I32, ctypes.c_int, P(S)], ctypes.c_int),
+        "gq_group_plan": ([I32, P(gq_group_item), I32, ctypes.c_int, VP, S], ctypes.c_int),
+        "gq_linear_group": ([VP, VP, VP], ctypes.c_int),
         "gq_kv_attention_workspace_bytes": ([P(gq_kv_cache), P(S)], ctypes.c_int),
         "gq_kv_attention": ([P(gq_kv_cache), VP, VP, VP, S, VP], ctypes.c_int),
         "gq_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -176,6 +184,24 @@ def gq_linear_dx(layout, M, act, dy_ptr, codes_ptr, scales_ptr, zeros_ptr, dx_pt
     return load_library().gq_linear_dx(ctypes.byref(layout), int(M), int(act), dy_ptr, codes_ptr,
                                        scales_ptr, zeros_ptr, dx_ptr, ws_ptr, int(ws_bytes),
                                        _stream(stream))
+
+
+def gq_group_plan_bytes(items, M: int, act: int = GQ_BF16) -> int:
+    arr = (gq_group_item * len(items))(*items)
+    b = ctypes.c_size_t()
+    st = load_library().gq_group_plan_bytes(len(items), arr, int(M), int(act), ctypes.byref(b))
+    if st != GQ_OK:
+        raise GqError(st, "gq_group_plan_bytes")
+    return b.value
+
+
+def gq_group_plan(items, M: int, act: int, plan_buf, plan_bytes: int) -> int:
+    arr = (gq_group_item * len(items))(*items)
+    return load_library().gq_group_plan(len(items), arr, int(M), int(act), plan_buf, int(plan_bytes))
+
+
+def gq_linear_group(plan_buf, plan_dev_ptr, stream=None) -> int:
+    return load_library().gq_linear_group(plan_buf, plan_dev_ptr, _stream(stream))
 
 
 def gq_kv_attention_workspace_bytes(cache: gq_kv_cache) -> int:

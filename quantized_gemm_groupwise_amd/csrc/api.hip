@@ -187,6 +187,28 @@ gq_status gq_linear_noalloc(const gq_layout *layout, int32_t M, gq_dtype act, co
   return dispatch_linear(L, M, act, x, codes, scales, zeros, y, ws, s);
 }
 
+gq_status gq_group_plan_bytes(int32_t count, const gq_group_item *items, int32_t M, gq_dtype act,
+                              size_t *bytes) {
+  if (!bytes) return GQ_ERR_NULL_ARG;
+  return gemv_group_plan(count, items, M, act, nullptr, 0, bytes);
+}
+
+gq_status gq_group_plan(int32_t count, const gq_group_item *items, int32_t M, gq_dtype act,
+                        void *plan, size_t plan_bytes) {
+  if (!plan) return GQ_ERR_NULL_ARG;
+  return gemv_group_plan(count, items, M, act, plan, plan_bytes, nullptr);
+}
+
+gq_status gq_linear_group(const void *plan, const void *plan_dev, void *stream) {
+  gq_status st = gemv_group_check(plan);
+  if (st != GQ_OK) return st;
+  if ((st = check_ptr16(plan_dev)) != GQ_OK) return st;
+  const GroupPlanHeader &H = *static_cast<const GroupPlanHeader *>(plan);
+  if (H.nclass == 0) return GQ_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launched(launch_gemv_group(H, plan_dev, s), s);
+}
+
 gq_status gq_linear_dx_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
                                        size_t *bytes) {
   if (!bytes) return GQ_ERR_NULL_ARG;

@@ -36,6 +36,10 @@
 // accumulator per position class.  Per group the zero point and scale are
 // applied as s * (sum x*q - z * sum x), i.e. sum x*(q-z)*s up to fp32
 // rounding.
+#include <string.h>
+
+#include <mutex>
+
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -445,13 +449,17 @@ __host__ __device__ constexpr int stage_bytes(int bits, int M, int nslice_row, i
 // One workgroup: stage x chunk by chunk, stream the wave's R rows.
 // ONE: every row of the layout fits one load group and one staged chunk
 // (chosen at launch, so each kernel holds the registers of one path only).
+// stage == false: x of this linear is already in LDS from the workgroup's
+// previous row tile (only when a row fits one staged chunk; the caller keeps
+// the workgroup's waves in step).
 template <int BITS, int ACT, int M, int R, int NL, int SS, bool ONE>
 __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &bi, int blk,
                                            int n0, bool active, const uint16_t *__restrict__ x,
                                            const uint8_t *__restrict__ codes,
                                            const uint16_t *__restrict__ scales,
                                            const uint8_t *__restrict__ zeros,
-                                           uint16_t *__restrict__ y, uint32_t *lds) {
+                                           uint16_t *__restrict__ y, uint32_t *lds,
+                                           bool stage = true) {
   using Gm = Geo<BITS>;
   const int lane = threadIdx.x & (kLanes - 1);
   const int K = L.K;
@@ -492,26 +500,32 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
     // so slice i waits only for the loads issued before it
     LoadGroup<BITS, R, NL> g;
     StageRegs<SS> st;
-    stage_x_load<BITS, M, SS>(st, xr, xbytes, K, 0, nslice_row);
+    if (stage) stage_x_load<BITS, M, SS>(st, xr, xbytes, K, 0, nslice_row);
     __builtin_amdgcn_sched_barrier(0);
     issue_group<BITS, R, NL, false>(g, 0, nslice_row, lane, rr);
     __builtin_amdgcn_sched_barrier(0);
-    stage_x_store<BITS, ACT, M, SS>(st, nslice_row, pairs, sums);
-    lds_barrier();
+    if (stage) {
+      stage_x_store<BITS, ACT, M, SS>(st, nslice_row, pairs, sums);
+      lds_barrier();
+    }
     compute_group<BITS, ACT, M, R, NL>(g, 0, nslice_row, 0, lane, pairs, sums, nslice_row, acc);
   } else {
+    // a row that fits one chunk keeps x staged when stage is false
+    const bool restage = stage || nslice_row > CHUNK;
     for (int c0 = 0; c0 < nslice_row; c0 += CHUNK) {
       const int cn = nslice_row - c0 < CHUNK ? nslice_row - c0 : CHUNK;
       const int cend = c0 + cn;
       if (c0 > 0) lds_barrier();               // previous chunk fully read
       LoadGroup<BITS, R, NL> g;
       StageRegs<SS> st;
-      stage_x_load<BITS, M, SS>(st, xr, xbytes, K, c0 * Gm::SK, cn);
+      if (restage) stage_x_load<BITS, M, SS>(st, xr, xbytes, K, c0 * Gm::SK, cn);
       __builtin_amdgcn_sched_barrier(0);
       issue_group<BITS, R, NL, true>(g, c0, cend, lane, rr);
       __builtin_amdgcn_sched_barrier(0);
-      stage_x_store<BITS, ACT, M, SS>(st, cn, pairs, sums);
-      lds_barrier();
+      if (restage) {
+        stage_x_store<BITS, ACT, M, SS>(st, cn, pairs, sums);
+        lds_barrier();
+      }
       for (int s = c0;;) {
         compute_group<BITS, ACT, M, R, NL>(g, s, cend, c0, lane, pairs, sums, cn, acc);
         s += NL;
@@ -568,6 +582,76 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint1
       gemv_block<4, ACT, M, R, NL, SS, ONE>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
     else
       gemv_block<2, ACT, M, R, NL, SS, ONE>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
+  }
+}
+
+// Grouped decode, one class of a plan: a persistent grid.  Workgroup w of G
+// takes the class's row tiles whose start cost falls in [w C / G,
+// (w + 1) C / G), walking the segment list in order, and runs each tile
+// exactly as the single-linear kernel's workgroup of that tile would (same
+// arithmetic, same order: the outputs are the same bits).  x of a linear is
+// staged once per workgroup while consecutive tiles stay in that linear.
+// Every branch below depends only on the workgroup and the plan, so the
+// waves of a workgroup meet the same barriers.
+template <int ACT, int M, int BITS, int SS, bool ONE>
+__global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__restrict__ plan,
+                                                              int cls) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  constexpr int R = kGroupR, NL = kGroupNL;
+  if constexpr (chunk_slices(BITS, M, SS) < 1) {
+    return;                                 // never launched: SS too small for M
+  } else {
+  const GroupPlanHeader &H = *reinterpret_cast<const GroupPlanHeader *>(plan);
+  const GroupClass &C = H.cls[cls];
+  const GroupSeg *segs = reinterpret_cast<const GroupSeg *>(plan + H.segs_off) + C.seg0;
+  const GroupItemDev *items = reinterpret_cast<const GroupItemDev *>(plan + H.items_off);
+  const int nseg = C.nseg;
+  const int64_t cost = C.cost;
+  const int64_t G = gridDim.x, w = blockIdx.x;
+  const int64_t c0 = cost * w / G, c1 = cost * (w + 1) / G;
+  // the last segment starting at or before c0
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].cost0 <= c0) lo = mid;
+    else hi = mid - 1;
+  }
+  int si = lo;
+  // its first tile starting at or after c0
+  int t = (int)((c0 - segs[si].cost0 + segs[si].tile_cost - 1) / segs[si].tile_cost);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+  int prev_item = -1;
+  while (si < nseg) {
+    const int item = segs[si].item, ntiles = segs[si].ntiles;
+    if (t >= ntiles) {
+      ++si;
+      t = 0;
+      continue;
+    }
+    if (segs[si].cost0 + (int64_t)t * segs[si].tile_cost >= c1) break;
+    const GroupItemDev &I = items[item];
+    const LayoutDev &L = I.L;
+    const int nb = (segs[si].tile0 + t) * kGroupTile;
+    const int n0 = nb + wave * R;
+    const int ns = (L.K * BITS / 8 + 1023) >> 10;
+    // restage when the linear changes, or every tile when a row does not
+    // fit one staged chunk; the barrier lets every wave finish reading the
+    // previous x first
+    const bool stage = item != prev_item || ns > chunk_slices(BITS, M, SS);
+    if (stage && prev_item >= 0) lds_barrier();
+    BlockInfo bi = {BITS, 0, 0};
+    int blk = 0;
+    if (!I.uniform) {
+      blk = nb / L.block_n;
+      bi = block_info(L, blk);
+    }
+    gemv_block<BITS, ACT, M, R, NL, SS, ONE>(
+        L, bi, blk, n0, n0 < L.N, reinterpret_cast<const uint16_t *>(I.x),
+        reinterpret_cast<const uint8_t *>(I.codes), reinterpret_cast<const uint16_t *>(I.scales),
+        reinterpret_cast<const uint8_t *>(I.zeros), reinterpret_cast<uint16_t *>(I.y), lds, stage);
+    prev_item = item;
+    ++t;
+  }
   }
 }
 
@@ -651,7 +735,219 @@ hipError_t launch_act(const LayoutDev &L, int M, const void *x, const uint32_t *
   }
 }
 
+typedef void (*GroupKernel)(const uint8_t *, int);
+
+template <int ACT, int M, int BITS>
+GroupKernel group_kernel_bits(int ss, bool one) {
+  if (chunk_slices(BITS, M, ss) < 1) return nullptr;   // not a configuration the plan picks
+  if (ss == 1) return one ? gemv_group_kernel<ACT, M, BITS, 1, true> : gemv_group_kernel<ACT, M, BITS, 1, false>;
+  if (ss == 2) return one ? gemv_group_kernel<ACT, M, BITS, 2, true> : gemv_group_kernel<ACT, M, BITS, 2, false>;
+  return one ? gemv_group_kernel<ACT, M, BITS, 4, true> : gemv_group_kernel<ACT, M, BITS, 4, false>;
+}
+
+template <int ACT, int M>
+GroupKernel group_kernel_m(int bits, int ss, bool one) {
+  return bits == 4 ? group_kernel_bits<ACT, M, 4>(ss, one) : group_kernel_bits<ACT, M, 2>(ss, one);
+}
+
+GroupKernel group_kernel(int act, int M, int bits, int ss, bool one) {
+  const bool bf = act == GQ_BF16;
+  switch (M) {
+    case 1: return bf ? group_kernel_m<0, 1>(bits, ss, one) : group_kernel_m<1, 1>(bits, ss, one);
+    case 2: return bf ? group_kernel_m<0, 2>(bits, ss, one) : group_kernel_m<1, 2>(bits, ss, one);
+    case 3: return bf ? group_kernel_m<0, 3>(bits, ss, one) : group_kernel_m<1, 3>(bits, ss, one);
+    default: return bf ? group_kernel_m<0, 4>(bits, ss, one) : group_kernel_m<1, 4>(bits, ss, one);
+  }
+}
+
+// Resident workgroups per CU of a kernel at an LDS size, and CUs of the
+// current device; each queried once and kept.
+int resident_grid(GroupKernel k, int lds) {
+  struct Entry { GroupKernel k; int lds; int dev; int grid; };
+  static std::mutex mu;
+  static Entry cache[256];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == k && cache[i].lds == lds && cache[i].dev == dev) return cache[i].grid;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(k), kThreads,
+                                                   lds) != hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int grid = per_cu * cus;
+  if (used < 256) cache[used++] = {k, lds, dev, grid};
+  return grid;
+}
+
+// Kernel configuration of one bit-width of a linear: the single-linear
+// launch's choices (staging sub-units, one load group per row or streamed
+// rows), with R and NL fixed for the group.
+struct WidthCfg {
+  int ss, one, lds;
+};
+
+WidthCfg width_cfg(int bits, int K, int M) {
+  const int ns = (K * bits / 8 + 1023) / 1024;
+  const int units = M * kLanes * (bits == 4 ? 2 : 4) * ns;
+  const int need = (units + kThreads - 1) / kThreads;
+  WidthCfg c;
+  c.ss = need <= 1 ? 1 : (need <= 2 ? 2 : kStageSubMax);
+  c.one = ns <= kGroupNL && ns <= chunk_slices(bits, M, c.ss);
+  c.lds = stage_bytes(bits, M, ns, c.ss);
+  return c;
+}
+
+inline int class_key(int bits, const WidthCfg &c) { return (bits == 4 ? 0 : 16) + c.ss * 2 + c.one; }
+
 }  // namespace
+
+gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype act, void *plan,
+                          size_t plan_bytes, size_t *need) {
+  if (!items) return GQ_ERR_NULL_ARG;
+  if (count < 1 || count > 65535 || M < 1 || M > kGemvMaxM) return GQ_ERR_SHAPE;
+  if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  // pass 1: check every item, count segments and classes
+  int nkeys = 0, keys[kGroupMaxClasses];
+  int64_t nseg = 0;
+  for (int i = 0; i < count; ++i) {
+    const gq_group_item &it = items[i];
+    LayoutDev L;
+    gq_status st = make_layout(&it.layout, &L);
+    if (st != GQ_OK) return st;
+    if (L.N == 0) continue;
+    if ((st = check_ptr16(it.x)) != GQ_OK) return st;
+    if ((st = check_ptr16(it.codes)) != GQ_OK) return st;
+    if (!it.scales || !it.zeros || !it.y) return GQ_ERR_NULL_ARG;
+    if (((uintptr_t)it.scales & 1u) || ((uintptr_t)it.y & 1u)) return GQ_ERR_ALIGNMENT;
+    int prev = -1;
+    for (int b = 0; b < L.nblocks; ++b) {
+      const int bits = block_info(L, b).bits;
+      if (bits != prev) ++nseg;
+      prev = bits;
+      const int key = class_key(bits, width_cfg(bits, L.K, M));
+      bool seen = false;
+      for (int k = 0; k < nkeys; ++k) seen |= keys[k] == key;
+      if (!seen) keys[nkeys++] = key;   // at most 2 widths x 3 x 2 <= 12 keys
+    }
+  }
+  if (nseg > INT32_MAX / 2) return GQ_ERR_SHAPE;
+  const size_t items_off = (sizeof(GroupPlanHeader) + 15) & ~(size_t)15;
+  const size_t segs_off = items_off + (size_t)count * sizeof(GroupItemDev);
+  const size_t bytes = segs_off + (size_t)nseg * sizeof(GroupSeg);
+  if (need) *need = bytes;
+  if (!plan) return GQ_OK;
+  if (plan_bytes < bytes) return GQ_ERR_WORKSPACE;
+  uint8_t *P = static_cast<uint8_t *>(plan);
+  memset(P, 0, bytes);
+  GroupPlanHeader &H = *reinterpret_cast<GroupPlanHeader *>(P);
+  H.magic = kGroupMagic;
+  H.version = kGroupVersion;
+  H.bytes = bytes;
+  H.count = count;
+  H.M = M;
+  H.act = act;
+  H.items_off = items_off;
+  H.segs_off = segs_off;
+  GroupItemDev *dst = reinterpret_cast<GroupItemDev *>(P + items_off);
+  for (int i = 0; i < count; ++i) {
+    GroupItemDev &D = dst[i];
+    make_layout(&items[i].layout, &D.L);
+    D.x = items[i].x;
+    D.codes = items[i].codes;
+    D.scales = items[i].scales;
+    D.zeros = items[i].zeros;
+    D.y = items[i].y;
+    D.uniform = D.L.nblocks == 1;
+  }
+  // classes in key order; inside a class, linears in call order and their
+  // runs of same-width blocks in block order
+  for (int a = 1; a < nkeys; ++a)
+    for (int b = a; b > 0 && keys[b - 1] > keys[b]; --b) {
+      const int tk = keys[b]; keys[b] = keys[b - 1]; keys[b - 1] = tk;
+    }
+  GroupSeg *segs = reinterpret_cast<GroupSeg *>(P + segs_off);
+  int si = 0;
+  for (int k = 0; k < nkeys; ++k) {
+    GroupClass &C = H.cls[k];
+    C.seg0 = si;
+    C.bits = keys[k] < 16 ? 4 : 2;
+    C.ss = (keys[k] & 15) / 2;
+    C.one = keys[k] & 1;
+    int64_t cost = 0;
+    int tiles = 0;
+    for (int i = 0; i < count; ++i) {
+      const LayoutDev &L = dst[i].L;
+      if (L.N == 0) continue;
+      const WidthCfg c = width_cfg(C.bits, L.K, M);
+      if (class_key(C.bits, c) != keys[k]) continue;
+      const int tile_cost = L.K * C.bits;   // code bytes of a tile of 8 rows
+      for (int b = 0; b < L.nblocks;) {
+        if (block_info(L, b).bits != C.bits) { ++b; continue; }
+        int e = b;
+        while (e < L.nblocks && block_info(L, e).bits == C.bits) ++e;
+        const int t0 = b * L.block_n / kGroupTile;
+        const int t1 = e == L.nblocks ? (L.N + kGroupTile - 1) / kGroupTile : e * L.block_n / kGroupTile;
+        GroupSeg &S = segs[si++];
+        S.item = i;
+        S.tile0 = t0;
+        S.ntiles = t1 - t0;
+        S.tile_cost = tile_cost;
+        S.cost0 = cost;
+        cost += (int64_t)S.ntiles * tile_cost;
+        tiles += S.ntiles;
+        b = e;
+      }
+      if (c.lds > C.lds) C.lds = c.lds;
+    }
+    C.nseg = si - C.seg0;
+    C.cost = cost;
+    C.tiles = tiles;
+  }
+  H.nclass = nkeys;
+  H.nseg = si;
+  return GQ_OK;
+}
+
+gq_status gemv_group_check(const void *plan) {
+  if (!plan) return GQ_ERR_NULL_ARG;
+  const GroupPlanHeader &H = *static_cast<const GroupPlanHeader *>(plan);
+  if (H.magic != kGroupMagic || H.version != kGroupVersion) return GQ_ERR_SHAPE;
+  if (H.count < 1 || H.M < 1 || H.M > kGemvMaxM || (H.act != GQ_BF16 && H.act != GQ_FP16))
+    return GQ_ERR_SHAPE;
+  if (H.nclass < 0 || H.nclass > kGroupMaxClasses || H.nseg < 0) return GQ_ERR_SHAPE;
+  if (H.items_off + (uint64_t)H.count * sizeof(GroupItemDev) > H.segs_off ||
+      H.segs_off + (uint64_t)H.nseg * sizeof(GroupSeg) != H.bytes)
+    return GQ_ERR_SHAPE;
+  int seg = 0;
+  for (int c = 0; c < H.nclass; ++c) {
+    const GroupClass &C = H.cls[c];
+    if (C.seg0 != seg || C.nseg < 1 || (C.bits != 4 && C.bits != 2) ||
+        (C.ss != 1 && C.ss != 2 && C.ss != 4) || C.lds < 0 || C.lds > kLdsBytes || C.cost < 1 ||
+        C.tiles < 1)
+      return GQ_ERR_SHAPE;
+    seg += C.nseg;
+  }
+  return seg == H.nseg ? GQ_OK : GQ_ERR_SHAPE;
+}
+
+hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hipStream_t s) {
+  const uint8_t *p = static_cast<const uint8_t *>(plan_dev);
+  for (int c = 0; c < H.nclass; ++c) {
+    const GroupClass &C = H.cls[c];
+    const GroupKernel k = group_kernel(H.act, H.M, C.bits, C.ss, C.one != 0);
+    if (!k) return hipErrorInvalidConfiguration;
+    int grid = resident_grid(k, C.lds);
+    if (grid <= 0) return hipErrorInvalidConfiguration;
+    if (grid > C.tiles) grid = C.tiles;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), C.lds, s, p, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_gemv(const LayoutDev &L, int M, gq_dtype act, const void *x,
                        const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,

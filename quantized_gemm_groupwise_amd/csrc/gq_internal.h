@@ -62,6 +62,80 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
                        const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros,
                        void *y, void *workspace, hipStream_t s);
 
+// ------------------------------------------------------- grouped decode
+
+// Plan of a grouped decode call (gq_group_plan / gq_linear_group).  The
+// caller keeps a byte copy in device memory, which the kernels read; the
+// host copy gives the launch configuration.
+//
+// Work is cut into row tiles of 4 * kGroupR output channels (the GEMV's
+// workgroup tile).  The tiles of one bit-width and kernel configuration form
+// a class, launched once as a persistent grid: workgroup w of G takes the
+// tiles whose start falls in [w C / G, (w + 1) C / G) of the class's cost
+// (packed code bytes, so long and short rows balance), in order.  A class is
+// a list of segments, runs of consecutive tiles of one linear (a Channel-mix
+// linear gives one segment per run of same-width blocks).
+constexpr uint32_t kGroupMagic = 0x50475147u;   // "GQGP"
+constexpr uint32_t kGroupVersion = 2;
+constexpr int kGroupMaxClasses = 12;
+constexpr int kGroupR = 2;                       // rows per wave
+constexpr int kGroupNL = 2;                      // 1 KB slices per load group
+constexpr int kGroupTile = 4 * kGroupR;          // rows per tile
+
+struct GroupClass {
+  int32_t seg0;        // first segment of the class
+  int32_t nseg;        // segments
+  int32_t bits;        // 4 or 2
+  int32_t ss;          // x staging sub-units per thread (1, 2 or 4)
+  int32_t one;         // 1: every row fits one load group and one staged chunk
+  int32_t lds;         // dynamic LDS bytes
+  int32_t tiles;       // tiles in the class
+  int32_t pad;
+  int64_t cost;        // total cost
+};
+
+struct GroupPlanHeader {
+  uint32_t magic;
+  uint32_t version;
+  uint64_t bytes;      // size of the whole plan
+  int32_t count;       // linears
+  int32_t M;
+  int32_t act;         // gq_dtype of x and y
+  int32_t nclass;
+  int32_t nseg;
+  int32_t pad;
+  uint64_t items_off;  // byte offset of GroupItemDev[count]
+  uint64_t segs_off;   // byte offset of GroupSeg[nseg]
+  GroupClass cls[kGroupMaxClasses];
+};
+
+struct GroupItemDev {
+  LayoutDev L;
+  const void *x;
+  const void *codes;
+  const void *scales;
+  const void *zeros;
+  void *y;
+  int32_t uniform;     // 1: one block (no per-tile block lookup)
+  int32_t pad[3];
+};
+
+struct GroupSeg {
+  int32_t item;
+  int32_t tile0;       // first tile of the run, in the linear's tiles
+  int32_t ntiles;
+  int32_t tile_cost;   // cost of one tile
+  int64_t cost0;       // class cost before the run
+};
+
+// Host: size of the plan (plan == nullptr) or the plan itself, after
+// checking every item; gemv.hip.
+gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype act, void *plan,
+                          size_t plan_bytes, size_t *need);
+// Host: sanity checks of a host plan before its launches.
+gq_status gemv_group_check(const void *plan);
+hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hipStream_t s);
+
 // Largest M served by the dot-product (GEMV) kernel; larger M goes to MFMA.
 constexpr int kGemvMaxM = 4;
 // Largest M served by the small-batch MFMA kernel (bf16/fp16 activations

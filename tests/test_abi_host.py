@@ -202,6 +202,43 @@ def test_noalloc_refusals_before_launch(lib):
     assert NA(big, 2048, gq.GQ_BF16, A, A) == gq.GQ_ERR_TOO_LARGE
 
 
+def test_group_plan_refusals_and_size(lib):
+    """Grouped decode plans: argument checks on the host, the plan size, and a
+    refused launch of anything that is not a plan."""
+    A, bad = 0x10000, 0x10008
+    lay = gq.make_layout(4096, 1024, 1024, [4])
+    mix = gq.make_layout(1024, 384, 128, [4, 2, 4])
+    it = lambda l, x=A, c=A, y=A: gq.gq_group_item(l, x, c, A, A, y)
+    items = [it(lay), it(mix)]
+    n = gq.gq_group_plan_bytes(items, 1)
+    # header, two records, one int32 per workgroup of 8 rows
+    assert n > (1024 // 8 + 384 // 8) * 4
+    assert gq.gq_group_plan_bytes(items, 4) == n
+    for M in (0, 5):
+        with pytest.raises(gq.GqError):
+            gq.gq_group_plan_bytes(items, M)
+    with pytest.raises(gq.GqError):
+        gq.gq_group_plan_bytes(items, 1, gq.GQ_FP32)
+    for bad_item in (it(lay, x=bad), it(lay, c=bad), it(lay, y=A + 1), it(lay, x=None),
+                     it(gq.make_layout(100, 1024, 1024, [4]))):
+        with pytest.raises(gq.GqError):
+            gq.gq_group_plan_bytes([it(lay), bad_item], 1)
+    buf = ctypes.create_string_buffer(n)
+    assert gq.gq_group_plan(items, 1, gq.GQ_BF16, buf, n - 1) == gq.GQ_ERR_WORKSPACE
+    assert gq.gq_group_plan(items, 1, gq.GQ_BF16, buf, n) == gq.GQ_OK
+    # the launch refuses a misaligned device copy and anything not a plan
+    assert lib.gq_linear_group(buf, bad, None) == gq.GQ_ERR_ALIGNMENT
+    junk = ctypes.create_string_buffer(n)
+    assert lib.gq_linear_group(junk, A, None) == gq.GQ_ERR_SHAPE
+    assert lib.gq_linear_group(None, A, None) == gq.GQ_ERR_NULL_ARG
+    # a group of empty linears needs no launch
+    empty = gq.make_layout(512, 0, 1, [])
+    n0 = gq.gq_group_plan_bytes([it(empty, x=None, c=None, y=None)], 1)
+    b0 = ctypes.create_string_buffer(n0)
+    assert gq.gq_group_plan([it(empty, x=None, c=None, y=None)], 1, gq.GQ_BF16, b0, n0) == gq.GQ_OK
+    assert lib.gq_linear_group(b0, A, None) == gq.GQ_OK
+
+
 def test_status_strings():
     for st in range(9):
         assert gq.gq_status_string(st).startswith("GQ_")
