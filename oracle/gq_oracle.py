@@ -333,7 +333,8 @@ def kv_cache_pack(kv, bits: int) -> Packed:
 
 
 def kv_decode_attention(q_bf16, k_packed, v_packed, k_window_bf16, v_window_bf16,
-                        batch: int, q_heads: int, kv_heads: int, head_dim: int) -> np.ndarray:
+                        batch: int, q_heads: int, kv_heads: int, head_dim: int,
+                        return_abs: bool = False):
     """One decode step of attention over a group-wise quantized KV cache, in
     fp64 ([SV] KV-cache bullet and its techniques: the cache is stored at low
     bit width and dequantized for attention; the newest tokens stay in full
@@ -347,7 +348,8 @@ def kv_decode_attention(q_bf16, k_packed, v_packed, k_window_bf16, v_window_bf16
     Query head h attends with key/value head h // (q_heads // kv_heads);
     scores are q . k / sqrt(head_dim) over the packed tokens followed by the
     window tokens; softmax; the output is the probability-weighted sum of the
-    values.  Returns fp64 [batch][q_heads][head_dim]."""
+    values.  Returns fp64 [batch][q_heads][head_dim]; with return_abs, also
+    sum_t p_t |v_t| per output (the scale an error bound of P . V takes)."""
     G = q_heads // kv_heads
     q = bf16_bits_to_f64(q_bf16).reshape(batch, q_heads, head_dim)
     kw = bf16_bits_to_f64(k_window_bf16).reshape(batch, -1, kv_heads, head_dim)
@@ -361,13 +363,16 @@ def kv_decode_attention(q_bf16, k_packed, v_packed, k_window_bf16, v_window_bf16
     else:
         keys, vals = kw, vw
     out = np.zeros((batch, q_heads, head_dim))
+    absw = np.zeros((batch, q_heads, head_dim))
     for b in range(batch):
         for h in range(q_heads):
             kh = h // G
             s = keys[b, :, kh, :] @ q[b, h] / np.sqrt(head_dim)
             e = np.exp(s - s.max())
-            out[b, h] = (e / e.sum()) @ vals[b, :, kh, :]
-    return out
+            p = e / e.sum()
+            out[b, h] = p @ vals[b, :, kh, :]
+            absw[b, h] = p @ np.abs(vals[b, :, kh, :])
+    return (out, absw) if return_abs else out
 
 
 def f64_to_bf16_bits(a) -> np.ndarray:

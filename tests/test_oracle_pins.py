@@ -433,6 +433,13 @@ def test_kv_attention_uniform_scores_give_the_mean():
         for h in range(Hq):
             want = sum(vals[b, t, h // 2] for t in range(tp + tw)) / (tp + tw)
             assert np.allclose(out[b, h], want, rtol=0, atol=1e-12)
+    # the error-bound scale sum_t p_t |v_t| is then the mean magnitude
+    out2, absw = O.kv_decode_attention(q, kp, vp, kw, vw, B, Hq, Hkv, D, return_abs=True)
+    assert np.array_equal(out2, out)
+    for b in range(B):
+        for h in range(Hq):
+            want = sum(np.abs(vals[b, t, h // 2]) for t in range(tp + tw)) / (tp + tw)
+            assert np.allclose(absw[b, h], want, rtol=0, atol=1e-12)
 
 
 def test_kv_attention_one_dominant_token():
