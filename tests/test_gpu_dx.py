@@ -219,6 +219,9 @@ def test_linear_dx_channel_mix_full_size(j):
     torch.cuda.synchronize()
     dxb = y_bits(dx)
     rng = np.random.default_rng(40 + j)
-    ms = sorted(set(rng.choice(M, 24, replace=False).tolist()) | {0, M - 1})
-    wins = sorted(set(rng.choice(K // 128, 8, replace=False).tolist()) | {0, K // 128 - 1})
-    _sampled_dx_check(W, bits, 128, dy, dxb, ms, wins, rng)
+    # two rows of every 256-row band of m and one 128-column window in every
+    # 256-column band of k: every 256 x 256 tile of dX (the tail-split tiles
+    # of the last round included) holds sampled outputs
+    ms = sorted({int(t + rng.integers(256)) for t in range(0, M, 256) for _ in range(2)} | {0, M - 1})
+    wins = sorted({2 * t + int(rng.integers(2)) for t in range(K // 256)} | {0, K // 128 - 1})
+    _sampled_dx_check(W, bits, 128, dy, dxb, ms, wins, rng, ncols=4)
