@@ -321,13 +321,18 @@ __device__ __forceinline__ void issue_group(LoadGroup<BITS, R, NL> &g, int slice
     if (LIM && sl >= lim) off = gi = kOutOfRange;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      g.cw[i][r] = ld128(rr.c[r], off);
-      g.sb[i][r] = ld16(rr.s[r], gi == kOutOfRange ? gi : 2u * gi);
-      g.zb[i][r] = ld8(rr.z[r], gi);
+      g.cw[i][r] = ld128_nt(rr.c[r], off);
+      g.sb[i][r] = ld16_nt(rr.s[r], gi == kOutOfRange ? gi : 2u * gi);
+      g.zb[i][r] = ld8_nt(rr.z[r], gi);
     }
   }
 }
 
+// The x pairs of one slice are read from LDS a chunk at a time (the pairs
+// one code word, or one pair of INT4 words, multiplies), and every row of the
+// wave consumes a chunk before the next is read: only one chunk of x per M
+// row is held in registers.  Each row's accumulation order does not depend
+// on this interleaving.
 template <int BITS, int ACT, int M, int R, int NL>
 __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, int slice0,
                                               int nslice_row, int chunk_slice0, int lane,
@@ -342,38 +347,43 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
     const int sl = slice0 + i;
     if (sl < nslice_row) {
     const int lsl = sl - chunk_slice0;          // slice within the staged chunk
-    uint32_t xp[M][Gm::PW];
     float xs[M], xb[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int ms = m * chunk_nslice + lsl;
-      const uint4 *src = pairs + (ms * (Gm::PW / 4)) * kLanes + lane;
-#pragma unroll
-      for (int q = 0; q < Gm::PW / 4; ++q) {
-        const uint4 t = src[q * kLanes];
-        xp[m][4 * q + 0] = t.x; xp[m][4 * q + 1] = t.y;
-        xp[m][4 * q + 2] = t.z; xp[m][4 * q + 3] = t.w;
-      }
       const float *s = sums + (ms * Gm::NSUM) * kLanes + lane;
       xs[m] = s[0];
       if constexpr (BITS == 2) xb[m] = s[kLanes];
     }
+    // x pair words [8c, 8c + 8) of row m of this slice
+    auto read_chunk = [&](int c, uint32_t (&xc)[M][8]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t wv[4] = {g.cw[i][r].x, g.cw[i][r].y, g.cw[i][r].z, g.cw[i][r].w};
-      const float S = f16_bits_to_f32((uint16_t)g.sb[i][r]);
-      const float zz = (float)g.zb[i][r];
-      if constexpr (BITS == 4) {
-        // nibble t of each 16-bit half of word w gives the pair for
-        // activation pair 4w + t; words (0,1) and (2,3) are shifted as one
-        // 64-bit value, the bits that cross into the low word are masked off
-        const uint32_t mask = 0x000f000fu;
-        float pa[M], pb[M];
+      for (int m = 0; m < M; ++m) {
+        const int ms = m * chunk_nslice + lsl;
+        const uint4 *src = pairs + (ms * (Gm::PW / 4)) * kLanes + lane;
+        const uint4 a = src[(2 * c) * kLanes], b = src[(2 * c + 1) * kLanes];
+        xc[m][0] = a.x; xc[m][1] = a.y; xc[m][2] = a.z; xc[m][3] = a.w;
+        xc[m][4] = b.x; xc[m][5] = b.y; xc[m][6] = b.z; xc[m][7] = b.w;
+      }
+    };
+    if constexpr (BITS == 4) {
+      // nibble t of each 16-bit half of word w gives the pair for
+      // activation pair 4w + t; words (0,1) and (2,3) are shifted as one
+      // 64-bit value, the bits that cross into the low word are masked off
+      const uint32_t mask = 0x000f000fu;
+      float pa[R][M], pb[R][M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.f;
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint64_t w64 = ((uint64_t)wv[2 * h + 1] << 32) | wv[2 * h];
+        for (int m = 0; m < M; ++m) pa[r][m] = pb[r][m] = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t xc[M][8];
+        read_chunk(h, xc);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t lo = h ? g.cw[i][r].z : g.cw[i][r].x, hi = h ? g.cw[i][r].w : g.cw[i][r].y;
+          const uint64_t w64 = ((uint64_t)hi << 32) | lo;
           uint64_t sh[4];
           sh[0] = w64;
           sh[1] = shr64<4>(w64);
@@ -385,43 +395,60 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
             const uint32_t q1 = and_or((uint32_t)(sh[t] >> 32), mask, bias);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-              pa[m] = dot2<ACT>(q0, xp[m][4 * (2 * h) + t], pa[m]);
-              pb[m] = dot2<ACT>(q1, xp[m][4 * (2 * h + 1) + t], pb[m]);
+              pa[r][m] = dot2<ACT>(q0, xc[m][t], pa[r][m]);
+              pb[r][m] = dot2<ACT>(q1, xc[m][4 + t], pb[r][m]);
             }
           }
         }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float S = f16_bits_to_f32((uint16_t)g.sb[i][r]);
+        const float zz = (float)g.zb[i][r];
 #pragma unroll
         for (int m = 0; m < M; ++m)
-          acc[r][m] = fmaf(S, fmaf(-(BIASF + zz), xs[m], pa[m] + pb[m]), acc[r][m]);
-      } else {
-        const uint32_t m1 = 0x00030003u, m4 = 0x000c000cu, m16 = 0x00300030u;
-        float p1[M], p4[M], p16[M];
+          acc[r][m] = fmaf(S, fmaf(-(BIASF + zz), xs[m], pa[r][m] + pb[r][m]), acc[r][m]);
+      }
+    } else {
+      const uint32_t m1 = 0x00030003u, m4 = 0x000c000cu, m16 = 0x00300030u;
+      float p1[R][M], p4[R][M], p16[R][M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) p1[m] = p4[m] = p16[m] = 0.f;
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t w0 = wv[w], w6 = wv[w] >> 6, w12 = wv[w] >> 12;
+        for (int m = 0; m < M; ++m) p1[r][m] = p4[r][m] = p16[r][m] = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t xq[M][8];
+        read_chunk(w, xq);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t wv = w == 0 ? g.cw[i][r].x : w == 1 ? g.cw[i][r].y : w == 2 ? g.cw[i][r].z : g.cw[i][r].w;
+          const uint32_t w0 = wv, w6 = wv >> 6, w12 = wv >> 12;
           const uint32_t q0 = and_or(w0, m1, bias), q1 = and_or(w0, m4, bias);
           const uint32_t q2 = and_or(w0, m16, bias), q3 = and_or(w6, m1, bias);
           const uint32_t q4 = and_or(w6, m4, bias), q5 = and_or(w6, m16, bias);
           const uint32_t q6 = and_or(w12, m1, bias), q7 = and_or(w12, m4, bias);
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            const uint32_t *xq = &xp[m][8 * w];
-            p1[m] = dot2<ACT>(q0, xq[0], p1[m]);
-            p4[m] = dot2<ACT>(q1, xq[1], p4[m]);
-            p16[m] = dot2<ACT>(q2, xq[2], p16[m]);
-            p1[m] = dot2<ACT>(q3, xq[3], p1[m]);
-            p4[m] = dot2<ACT>(q4, xq[4], p4[m]);
-            p16[m] = dot2<ACT>(q5, xq[5], p16[m]);
-            p1[m] = dot2<ACT>(q6, xq[6], p1[m]);
-            p4[m] = dot2<ACT>(q7, xq[7], p4[m]);
+            p1[r][m] = dot2<ACT>(q0, xq[m][0], p1[r][m]);
+            p4[r][m] = dot2<ACT>(q1, xq[m][1], p4[r][m]);
+            p16[r][m] = dot2<ACT>(q2, xq[m][2], p16[r][m]);
+            p1[r][m] = dot2<ACT>(q3, xq[m][3], p1[r][m]);
+            p4[r][m] = dot2<ACT>(q4, xq[m][4], p4[r][m]);
+            p16[r][m] = dot2<ACT>(q5, xq[m][5], p16[r][m]);
+            p1[r][m] = dot2<ACT>(q6, xq[m][6], p1[r][m]);
+            p4[r][m] = dot2<ACT>(q7, xq[m][7], p4[r][m]);
           }
         }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float S = f16_bits_to_f32((uint16_t)g.sb[i][r]);
+        const float zz = (float)g.zb[i][r];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           // sum x*q = p1 + p4/4 + p16/16 - B*(X1 + X4/4 + X16/16)
-          const float xq = fmaf(p16[m], 0.0625f, fmaf(p4[m], 0.25f, p1[m])) - xb[m];
+          const float xq = fmaf(p16[r][m], 0.0625f, fmaf(p4[r][m], 0.25f, p1[r][m])) - xb[m];
           acc[r][m] = fmaf(S, fmaf(-zz, xs[m], xq), acc[r][m]);
         }
       }
@@ -585,19 +612,72 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint1
   }
 }
 
-// Grouped decode, one class of a plan: a persistent grid.  Workgroup w of G
-// takes the class's row tiles whose start cost falls in [w C / G,
-// (w + 1) C / G), walking the segment list in order, and runs each tile
-// exactly as the single-linear kernel's workgroup of that tile would (same
-// arithmetic, same order: the outputs are the same bits).  x of a linear is
-// staged once per workgroup while consecutive tiles stay in that linear.
-// Every branch below depends only on the workgroup and the plan, so the
-// waves of a workgroup meet the same barriers.
-template <int ACT, int M, int BITS, int SS, bool ONE>
+// ------------------------------------------------------- grouped decode
+
+// Buffer resources of a wave's R rows starting at output channel n0 (rows
+// past N get empty resources: they load zeros and are never stored).
+template <int BITS, int R>
+__device__ __forceinline__ void tile_rows(const LayoutDev &L, const BlockInfo &bi, int blk, int n0,
+                                          const uint8_t *codes, const uint16_t *scales,
+                                          const uint8_t *zeros, RowRsrc<R> &rr) {
+  using Gm = Geo<BITS>;
+  const int RB = L.K * BITS / 8, GPR = L.K / Gm::G;
+  const int r0 = n0 - blk * L.block_n;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool live = n0 + r < L.N;
+    const uint64_t row = live ? (uint64_t)(r0 + r) : 0u;
+    rr.c[r] = make_rsrc(codes + bi.code_off + row * (uint64_t)RB, live ? (uint32_t)RB : 0u);
+    rr.s[r] = make_rsrc(scales + bi.grp_off + row * (uint64_t)GPR, live ? 2u * GPR : 0u);
+    rr.z[r] = make_rsrc(zeros + bi.grp_off + row * (uint64_t)GPR, live ? (uint32_t)GPR : 0u);
+  }
+}
+
+// The wave's R * M sums reduced across lanes; one lane per output stores.
+template <int ACT, int M, int R>
+__device__ __forceinline__ void reduce_store(const float (&acc)[R][M], int lane, int n0, int N,
+                                             uint16_t *y) {
+  constexpr int V0 = R * M;
+  constexpr int V = V0 <= 1 ? 1 : V0 <= 2 ? 2 : V0 <= 4 ? 4 : V0 <= 8 ? 8 : 16;
+  float vals[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) vals[v] = v < V0 ? acc[v / M][v % M] : 0.f;
+  const float tot = wave_reduce_multi<V>(vals, lane);
+  const int idx = reduced_index<V>(lane);
+  if ((lane & ((64 / V) - 1)) == 0 && idx < V0) {
+    const int r = idx / M, m = idx % M;
+    if (n0 + r < N) y[(int64_t)m * N + n0 + r] = ACT == 0 ? f32_to_bf16_rne(tot) : f32_to_f16_bits(tot);
+  }
+}
+
+// Position in a class's tile list: segment si, tile t of that segment; T is
+// the class tile index, [T0, T1) the workgroup's current chunk.
+struct TilePos {
+  int si, t, T, T0, T1;
+};
+
+// Grouped decode, one class of a plan.  Workgroup w of G takes the class's
+// chunks of `chunk` tiles w, w + G, ... (a grid of one workgroup per tile
+// when chunk is 1 and G the tile count; a persistent grid otherwise),
+// walking the segment list in order, and runs each tile with the
+// single-linear kernel's arithmetic and order (the outputs are the same
+// bits).  x of a linear is staged once per workgroup while consecutive
+// tiles stay in that linear.  Every branch below depends only on the
+// workgroup and the plan, so the waves of a workgroup meet the same
+// barriers.
+//
+// PIPE (every row fits one load group and one staged chunk): software
+// pipelined -- each wave issues the loads of its next tile before it works
+// on the current one, so two tiles of codes are in flight per wave; the
+// pipeline restarts where the linear changes (x must be restaged first).
+// Otherwise each tile runs the single-linear kernel's workgroup body (rows
+// in one load group when ONE, else streamed group by group).
+template <int ACT, int M, int BITS, int SS, int NL, bool ONE, bool PIPE>
 __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__restrict__ plan,
-                                                              int cls) {
+                                                              int cls, int chunk) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  constexpr int R = kGroupR, NL = kGroupNL;
+  constexpr int R = kGroupR;
+  using Gm = Geo<BITS>;
   if constexpr (chunk_slices(BITS, M, SS) < 1) {
     return;                                 // never launched: SS too small for M
   } else {
@@ -606,51 +686,152 @@ __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__r
   const GroupSeg *segs = reinterpret_cast<const GroupSeg *>(plan + H.segs_off) + C.seg0;
   const GroupItemDev *items = reinterpret_cast<const GroupItemDev *>(plan + H.items_off);
   const int nseg = C.nseg;
-  const int64_t cost = C.cost;
-  const int64_t G = gridDim.x, w = blockIdx.x;
-  const int64_t c0 = cost * w / G, c1 = cost * (w + 1) / G;
-  // the last segment starting at or before c0
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (segs[mid].cost0 <= c0) lo = mid;
-    else hi = mid - 1;
-  }
-  int si = lo;
-  // its first tile starting at or after c0
-  int t = (int)((c0 - segs[si].cost0 + segs[si].tile_cost - 1) / segs[si].tile_cost);
+  const int G = gridDim.x, w = blockIdx.x;
+  const int tiles = C.tiles;
+  // the segment holding class tile T
+  auto seg_of_tile = [&](int T) -> int {
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (segs[mid].ctile0 <= T) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  // chunks w, w + G, ... of `chunk` tiles
+  if ((int64_t)w * chunk >= tiles) return;
+  TilePos pos;
+  pos.T0 = pos.T = w * chunk;
+  pos.T1 = pos.T + chunk < tiles ? pos.T + chunk : tiles;
+  pos.si = seg_of_tile(pos.T);
+  pos.t = pos.T - segs[pos.si].ctile0;
+  // normalize p (after p.t and p.T advanced by one) to a real tile, and say
+  // whether the workgroup has one
+  auto settle = [&](TilePos &p) -> bool {
+    if (p.T >= p.T1) {                      // next chunk of this workgroup
+      if ((int64_t)p.T0 + (int64_t)G * chunk >= tiles) return false;
+      p.T0 = p.T = p.T0 + G * chunk;
+      p.T1 = p.T + chunk < tiles ? p.T + chunk : tiles;
+      p.si = seg_of_tile(p.T);
+      p.t = p.T - segs[p.si].ctile0;
+      return true;
+    }
+    while (p.t >= segs[p.si].ntiles) {
+      ++p.si;
+      p.t = 0;
+    }
+    return true;
+  };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-  int prev_item = -1;
-  while (si < nseg) {
-    const int item = segs[si].item, ntiles = segs[si].ntiles;
-    if (t >= ntiles) {
-      ++si;
-      t = 0;
-      continue;
+  const int lane = threadIdx.x & (kLanes - 1);
+
+  if constexpr (ONE && PIPE) {
+    uint4 *pairs = reinterpret_cast<uint4 *>(lds);
+    int item = segs[pos.si].item;
+    // first output channel of the wave in tile p, its block, and its rows
+    auto rows_of = [&](const TilePos &p, RowRsrc<R> &rr) -> int {
+      const GroupItemDev &I = items[segs[p.si].item];
+      const int nb = (segs[p.si].tile0 + p.t) * kGroupTile;
+      const int n0 = nb + wave * R;
+      BlockInfo bi = {BITS, 0, 0};
+      int blk = 0;
+      if (!I.uniform) {
+        blk = nb / I.L.block_n;
+        bi = block_info(I.L, blk);
+      }
+      tile_rows<BITS, R>(I.L, bi, blk, n0, reinterpret_cast<const uint8_t *>(I.codes),
+                         reinterpret_cast<const uint16_t *>(I.scales),
+                         reinterpret_cast<const uint8_t *>(I.zeros), rr);
+      return n0;
+    };
+    auto stage = [&](int it) {
+      const GroupItemDev &I = items[it];
+      const int K = I.L.K;
+      const int ns = (K * BITS / 8 + 1023) >> 10;
+      const uint32_t xbytes = (uint32_t)(M * K) * 2u;
+      StageRegs<SS> st;
+      stage_x_load<BITS, M, SS>(st, make_rsrc(I.x, xbytes), xbytes, K, 0, ns);
+      stage_x_store<BITS, ACT, M, SS>(st, ns, pairs,
+                                      reinterpret_cast<float *>(lds + M * ns * Gm::PW * kLanes));
+      lds_barrier();
+    };
+    // work on tile p (codes in g), after issuing the loads of the next tile
+    // of the same linear into gn; returns false when the range is done
+    auto step = [&](TilePos &p, int &n0, LoadGroup<BITS, R, NL> &g, LoadGroup<BITS, R, NL> &gn,
+                    int &n0n) -> bool {
+      TilePos q = {p.si, p.t + 1, p.T + 1, p.T0, p.T1};
+      const bool more = settle(q);
+      const bool same = more && segs[q.si].item == item;
+      if (same) {
+        RowRsrc<R> rr;
+        n0n = rows_of(q, rr);
+        issue_group<BITS, R, NL, false>(gn, 0, NL, lane, rr);
+      }
+      const GroupItemDev &I = items[item];
+      const int K = I.L.K;
+      const int ns = (K * BITS / 8 + 1023) >> 10;
+      const uint4 *pr = pairs;
+      const float *sm = reinterpret_cast<const float *>(lds + M * ns * Gm::PW * kLanes);
+      float acc[R][M];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+      compute_group<BITS, ACT, M, R, NL>(g, 0, ns, 0, lane, pr, sm, ns, acc);
+      reduce_store<ACT, M, R>(acc, lane, n0, I.L.N, reinterpret_cast<uint16_t *>(I.y));
+      if (!more) return false;
+      if (!same) {
+        // the next tile is in another linear: restage x, then its loads
+        item = segs[q.si].item;
+        lds_barrier();
+        stage(item);
+        RowRsrc<R> rr;
+        n0n = rows_of(q, rr);
+        issue_group<BITS, R, NL, false>(gn, 0, NL, lane, rr);
+      }
+      p = q;
+      return true;
+    };
+    stage(item);
+    LoadGroup<BITS, R, NL> ga, gb;
+    int n0a = 0, n0b = 0;
+    {
+      RowRsrc<R> rr;
+      n0a = rows_of(pos, rr);
+      issue_group<BITS, R, NL, false>(ga, 0, NL, lane, rr);
     }
-    if (segs[si].cost0 + (int64_t)t * segs[si].tile_cost >= c1) break;
-    const GroupItemDev &I = items[item];
-    const LayoutDev &L = I.L;
-    const int nb = (segs[si].tile0 + t) * kGroupTile;
-    const int n0 = nb + wave * R;
-    const int ns = (L.K * BITS / 8 + 1023) >> 10;
-    // restage when the linear changes, or every tile when a row does not
-    // fit one staged chunk; the barrier lets every wave finish reading the
-    // previous x first
-    const bool stage = item != prev_item || ns > chunk_slices(BITS, M, SS);
-    if (stage && prev_item >= 0) lds_barrier();
-    BlockInfo bi = {BITS, 0, 0};
-    int blk = 0;
-    if (!I.uniform) {
-      blk = nb / L.block_n;
-      bi = block_info(L, blk);
+    while (true) {
+      if (!step(pos, n0a, ga, gb, n0b)) break;
+      if (!step(pos, n0b, gb, ga, n0a)) break;
     }
-    gemv_block<BITS, ACT, M, R, NL, SS, ONE>(
-        L, bi, blk, n0, n0 < L.N, reinterpret_cast<const uint16_t *>(I.x),
-        reinterpret_cast<const uint8_t *>(I.codes), reinterpret_cast<const uint16_t *>(I.scales),
-        reinterpret_cast<const uint8_t *>(I.zeros), reinterpret_cast<uint16_t *>(I.y), lds, stage);
-    prev_item = item;
-    ++t;
+  } else {
+    int prev_item = -1;
+    do {
+      const int item = segs[pos.si].item;
+      const GroupItemDev &I = items[item];
+      const LayoutDev &L = I.L;
+      const int nb = (segs[pos.si].tile0 + pos.t) * kGroupTile;
+      const int n0 = nb + wave * R;
+      const int ns = (L.K * BITS / 8 + 1023) >> 10;
+      // restage when the linear changes, or every tile when a row does not
+      // fit one staged chunk; the barrier lets every wave finish reading
+      // the previous x first
+      const bool stage = item != prev_item || ns > chunk_slices(BITS, M, SS);
+      if (stage && prev_item >= 0) lds_barrier();
+      BlockInfo bi = {BITS, 0, 0};
+      int blk = 0;
+      if (!I.uniform) {
+        blk = nb / L.block_n;
+        bi = block_info(L, blk);
+      }
+      gemv_block<BITS, ACT, M, R, NL, SS, ONE>(
+          L, bi, blk, n0, n0 < L.N, reinterpret_cast<const uint16_t *>(I.x),
+          reinterpret_cast<const uint8_t *>(I.codes), reinterpret_cast<const uint16_t *>(I.scales),
+          reinterpret_cast<const uint8_t *>(I.zeros), reinterpret_cast<uint16_t *>(I.y), lds, stage);
+      prev_item = item;
+      ++pos.t;
+      ++pos.T;
+    } while (settle(pos));
   }
   }
 }
@@ -735,28 +916,39 @@ hipError_t launch_act(const LayoutDev &L, int M, const void *x, const uint32_t *
   }
 }
 
-typedef void (*GroupKernel)(const uint8_t *, int);
+typedef void (*GroupKernel)(const uint8_t *, int, int);
+
+// one: 0 streamed rows, 1 rows of one slice (one-slice load groups), 2 rows
+// of two slices; pipe: the software-pipelined persistent body
+template <int ACT, int M, int BITS, int SS>
+GroupKernel group_kernel_ss(int one, bool pipe) {
+  if (one == 1)
+    return pipe ? gemv_group_kernel<ACT, M, BITS, SS, 1, true, true> : gemv_group_kernel<ACT, M, BITS, SS, 1, true, false>;
+  if (one == 2)
+    return pipe ? gemv_group_kernel<ACT, M, BITS, SS, 2, true, true> : gemv_group_kernel<ACT, M, BITS, SS, 2, true, false>;
+  return gemv_group_kernel<ACT, M, BITS, SS, kGroupNL, false, false>;
+}
 
 template <int ACT, int M, int BITS>
-GroupKernel group_kernel_bits(int ss, bool one) {
+GroupKernel group_kernel_bits(int ss, int one, bool pipe) {
   if (chunk_slices(BITS, M, ss) < 1) return nullptr;   // not a configuration the plan picks
-  if (ss == 1) return one ? gemv_group_kernel<ACT, M, BITS, 1, true> : gemv_group_kernel<ACT, M, BITS, 1, false>;
-  if (ss == 2) return one ? gemv_group_kernel<ACT, M, BITS, 2, true> : gemv_group_kernel<ACT, M, BITS, 2, false>;
-  return one ? gemv_group_kernel<ACT, M, BITS, 4, true> : gemv_group_kernel<ACT, M, BITS, 4, false>;
+  if (ss == 1) return group_kernel_ss<ACT, M, BITS, 1>(one, pipe);
+  if (ss == 2) return group_kernel_ss<ACT, M, BITS, 2>(one, pipe);
+  return group_kernel_ss<ACT, M, BITS, 4>(one, pipe);
 }
 
 template <int ACT, int M>
-GroupKernel group_kernel_m(int bits, int ss, bool one) {
-  return bits == 4 ? group_kernel_bits<ACT, M, 4>(ss, one) : group_kernel_bits<ACT, M, 2>(ss, one);
+GroupKernel group_kernel_m(int bits, int ss, int one, bool pipe) {
+  return bits == 4 ? group_kernel_bits<ACT, M, 4>(ss, one, pipe) : group_kernel_bits<ACT, M, 2>(ss, one, pipe);
 }
 
-GroupKernel group_kernel(int act, int M, int bits, int ss, bool one) {
+GroupKernel group_kernel(int act, int M, int bits, int ss, int one, bool pipe) {
   const bool bf = act == GQ_BF16;
   switch (M) {
-    case 1: return bf ? group_kernel_m<0, 1>(bits, ss, one) : group_kernel_m<1, 1>(bits, ss, one);
-    case 2: return bf ? group_kernel_m<0, 2>(bits, ss, one) : group_kernel_m<1, 2>(bits, ss, one);
-    case 3: return bf ? group_kernel_m<0, 3>(bits, ss, one) : group_kernel_m<1, 3>(bits, ss, one);
-    default: return bf ? group_kernel_m<0, 4>(bits, ss, one) : group_kernel_m<1, 4>(bits, ss, one);
+    case 1: return bf ? group_kernel_m<0, 1>(bits, ss, one, pipe) : group_kernel_m<1, 1>(bits, ss, one, pipe);
+    case 2: return bf ? group_kernel_m<0, 2>(bits, ss, one, pipe) : group_kernel_m<1, 2>(bits, ss, one, pipe);
+    case 3: return bf ? group_kernel_m<0, 3>(bits, ss, one, pipe) : group_kernel_m<1, 3>(bits, ss, one, pipe);
+    default: return bf ? group_kernel_m<0, 4>(bits, ss, one, pipe) : group_kernel_m<1, 4>(bits, ss, one, pipe);
   }
 }
 
@@ -795,12 +987,13 @@ WidthCfg width_cfg(int bits, int K, int M) {
   const int need = (units + kThreads - 1) / kThreads;
   WidthCfg c;
   c.ss = need <= 1 ? 1 : (need <= 2 ? 2 : kStageSubMax);
-  c.one = ns <= kGroupNL && ns <= chunk_slices(bits, M, c.ss);
+  // one-load-group rows: 1 or 2 slices (the load group's size), else 0
+  c.one = (ns <= kGroupNL && ns <= chunk_slices(bits, M, c.ss)) ? ns : 0;
   c.lds = stage_bytes(bits, M, ns, c.ss);
   return c;
 }
 
-inline int class_key(int bits, const WidthCfg &c) { return (bits == 4 ? 0 : 16) + c.ss * 2 + c.one; }
+inline int class_key(int bits, const WidthCfg &c) { return (bits == 4 ? 0 : 16) + c.ss * 3 + c.one; }
 
 }  // namespace
 
@@ -830,7 +1023,7 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
       const int key = class_key(bits, width_cfg(bits, L.K, M));
       bool seen = false;
       for (int k = 0; k < nkeys; ++k) seen |= keys[k] == key;
-      if (!seen) keys[nkeys++] = key;   // at most 2 widths x 3 x 2 <= 12 keys
+      if (!seen) keys[nkeys++] = key;   // at most 2 widths x 3 x 3 = 18 keys
     }
   }
   if (nseg > INT32_MAX / 2) return GQ_ERR_SHAPE;
@@ -874,16 +1067,14 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
     GroupClass &C = H.cls[k];
     C.seg0 = si;
     C.bits = keys[k] < 16 ? 4 : 2;
-    C.ss = (keys[k] & 15) / 2;
-    C.one = keys[k] & 1;
-    int64_t cost = 0;
+    C.ss = (keys[k] & 15) / 3;
+    C.one = (keys[k] & 15) % 3;
     int tiles = 0;
     for (int i = 0; i < count; ++i) {
       const LayoutDev &L = dst[i].L;
       if (L.N == 0) continue;
       const WidthCfg c = width_cfg(C.bits, L.K, M);
       if (class_key(C.bits, c) != keys[k]) continue;
-      const int tile_cost = L.K * C.bits;   // code bytes of a tile of 8 rows
       for (int b = 0; b < L.nblocks;) {
         if (block_info(L, b).bits != C.bits) { ++b; continue; }
         int e = b;
@@ -894,16 +1085,13 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
         S.item = i;
         S.tile0 = t0;
         S.ntiles = t1 - t0;
-        S.tile_cost = tile_cost;
-        S.cost0 = cost;
-        cost += (int64_t)S.ntiles * tile_cost;
+        S.ctile0 = tiles;
         tiles += S.ntiles;
         b = e;
       }
       if (c.lds > C.lds) C.lds = c.lds;
     }
     C.nseg = si - C.seg0;
-    C.cost = cost;
     C.tiles = tiles;
   }
   H.nclass = nkeys;
@@ -925,8 +1113,8 @@ gq_status gemv_group_check(const void *plan) {
   for (int c = 0; c < H.nclass; ++c) {
     const GroupClass &C = H.cls[c];
     if (C.seg0 != seg || C.nseg < 1 || (C.bits != 4 && C.bits != 2) ||
-        (C.ss != 1 && C.ss != 2 && C.ss != 4) || C.lds < 0 || C.lds > kLdsBytes || C.cost < 1 ||
-        C.tiles < 1)
+        (C.ss != 1 && C.ss != 2 && C.ss != 4) || C.one < 0 || C.one > kGroupNL || C.lds < 0 ||
+        C.lds > kLdsBytes || C.tiles < 1)
       return GQ_ERR_SHAPE;
     seg += C.nseg;
   }
@@ -937,12 +1125,20 @@ hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hip
   const uint8_t *p = static_cast<const uint8_t *>(plan_dev);
   for (int c = 0; c < H.nclass; ++c) {
     const GroupClass &C = H.cls[c];
-    const GroupKernel k = group_kernel(H.act, H.M, C.bits, C.ss, C.one != 0);
-    if (!k) return hipErrorInvalidConfiguration;
-    int grid = resident_grid(k, C.lds);
-    if (grid <= 0) return hipErrorInvalidConfiguration;
-    if (grid > C.tiles) grid = C.tiles;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), C.lds, s, p, c);
+    // a class with many tiles per resident workgroup runs as a persistent,
+    // software-pipelined grid taking chunks of kGroupChunk tiles in turn; a
+    // small one as one workgroup per tile (the hardware dispatcher then
+    // overlaps the workgroups' start and end, and no workgroup pays the
+    // pipeline's extra registers for a single tile)
+    const GroupKernel kp = group_kernel(H.act, H.M, C.bits, C.ss, C.one, true);
+    if (!kp) return hipErrorInvalidConfiguration;
+    const int resident = resident_grid(kp, C.lds);
+    if (resident <= 0) return hipErrorInvalidConfiguration;
+    const bool persist = (int64_t)C.tiles >= (int64_t)kGroupPersistTiles * resident;
+    const GroupKernel k = persist ? kp : group_kernel(H.act, H.M, C.bits, C.ss, C.one, false);
+    const int chunk = persist ? kGroupChunk : 1;
+    int grid = persist ? resident : C.tiles;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), C.lds, s, p, c, chunk);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

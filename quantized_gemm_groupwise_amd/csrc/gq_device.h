@@ -34,6 +34,20 @@ __device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t off, uint32_t soff = 0
 __device__ __forceinline__ uint32_t ld8(Rsrc r, uint32_t off, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
 }
+// The same loads with the nontemporal cache policy (NT): for data read
+// exactly once, such as packed codes, scales and zero points streamed by a
+// decode kernel, so they do not displace reused lines from the caches.
+constexpr int kNT = 2;
+__device__ __forceinline__ uint4 ld128_nt(Rsrc r, uint32_t off, uint32_t soff = 0) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t ld16_nt(Rsrc r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, kNT);
+}
+__device__ __forceinline__ uint32_t ld8_nt(Rsrc r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, kNT);
+}
 
 // (a & m) | o in one VALU op: gfx950's three-input bitwise op with truth
 // table 0xEA (bit i of the table is the result for input bits

@@ -71,27 +71,28 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 // Work is cut into row tiles of 4 * kGroupR output channels (the GEMV's
 // workgroup tile).  The tiles of one bit-width and kernel configuration form
 // a class, launched once as a persistent grid: workgroup w of G takes the
-// tiles whose start falls in [w C / G, (w + 1) C / G) of the class's cost
-// (packed code bytes, so long and short rows balance), in order.  A class is
-// a list of segments, runs of consecutive tiles of one linear (a Channel-mix
-// linear gives one segment per run of same-width blocks).
+// tiles of the class in chunks dealt round-robin (chunk c to workgroup
+// c mod G).  A class is a list of segments, runs of consecutive tiles of one
+// linear (a Channel-mix linear gives one segment per run of same-width
+// blocks).
 constexpr uint32_t kGroupMagic = 0x50475147u;   // "GQGP"
 constexpr uint32_t kGroupVersion = 2;
-constexpr int kGroupMaxClasses = 12;
+constexpr int kGroupMaxClasses = 18;
 constexpr int kGroupR = 2;                       // rows per wave
 constexpr int kGroupNL = 2;                      // 1 KB slices per load group
 constexpr int kGroupTile = 4 * kGroupR;          // rows per tile
+constexpr int kGroupChunk = 4;                   // tiles per chunk of a persistent launch
+constexpr int kGroupPersistTiles = 4;            // tiles per resident workgroup to persist
 
 struct GroupClass {
   int32_t seg0;        // first segment of the class
   int32_t nseg;        // segments
   int32_t bits;        // 4 or 2
   int32_t ss;          // x staging sub-units per thread (1, 2 or 4)
-  int32_t one;         // 1: every row fits one load group and one staged chunk
+  int32_t one;         // rows of 1 or 2 slices fit one load group and staged chunk; 0: streamed
   int32_t lds;         // dynamic LDS bytes
   int32_t tiles;       // tiles in the class
   int32_t pad;
-  int64_t cost;        // total cost
 };
 
 struct GroupPlanHeader {
@@ -124,8 +125,7 @@ struct GroupSeg {
   int32_t item;
   int32_t tile0;       // first tile of the run, in the linear's tiles
   int32_t ntiles;
-  int32_t tile_cost;   // cost of one tile
-  int64_t cost0;       // class cost before the run
+  int32_t ctile0;      // class tiles before the run
 };
 
 // Host: size of the plan (plan == nullptr) or the plan itself, after

@@ -217,13 +217,13 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
   for (int j = 0; j < SPS; ++j) {
     const int u = tid + SK_THREADS * j, pair = u / PS, piece = u % PS;
     const bool ok = u < SK_PAIRS * PS && pair / KW < a.nvalid;
-    spv[j] = ld128(sr, ok ? ((2u * run_start(pair)) & ~15u) + 16u * piece : SK_OOB);
+    spv[j] = ld128_nt(sr, ok ? ((2u * run_start(pair)) & ~15u) + 16u * piece : SK_OOB);
   }
 #pragma unroll
   for (int j = 0; j < SPZ; ++j) {
     const int u = tid + SK_THREADS * j, pair = u / PZ, piece = u % PZ;
     const bool ok = u < SK_PAIRS * PZ && pair / KW < a.nvalid;
-    zpv[j] = ld128(zr, ok ? (run_start(pair) & ~15u) + 16u * piece : SK_OOB);
+    zpv[j] = ld128_nt(zr, ok ? (run_start(pair) & ~15u) + 16u * piece : SK_OOB);
   }
 
   // ---- codes of the lane's channel and k-way, straight to registers.
@@ -251,7 +251,7 @@ __device__ __forceinline__ void skinny_tile(const SkArgs &a, Rsrc xr, Rsrc cr, R
     const int lstep = BITS == 4 ? gs : gs + (g >> 1);
     const uint32_t off = (crow != SK_OOB && lstep < ke) ? crow + (uint32_t)gs * STEPB + 16u * g
                                                         : SK_OOB;
-    const uint4 v = ld128(cr, off);
+    const uint4 v = ld128_nt(cr, off);
     cw[s][0] = v.x; cw[s][1] = v.y; cw[s][2] = v.z; cw[s][3] = v.w;
   };
   __builtin_amdgcn_sched_barrier(0);
