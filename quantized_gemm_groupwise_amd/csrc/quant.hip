@@ -19,10 +19,14 @@
 // through in FP32).  Same groups, scale, zero point and codes as the packing
 // quantizer; the output is (c - z) * s, exact in fp32, rounded to nearest
 // even for bf16 / fp16.
+#include <mutex>
+
 #include "gq_internal.h"
 
 namespace gq {
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kSeg = 512;          // weights per wave-segment: 64 lanes x 8
@@ -34,54 +38,84 @@ constexpr int kLanes = 64;
 // MODE kPack writes codes, scale and zero point; the other modes write the
 // fake-quantized weights of the lane to orow (0 bf16, 1 fp16, 2 fp32).
 constexpr int kPack = -1;
+// v: the lane's 8 weights (zeros for lanes past the row end, active false).
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
 template <int BITS, int MODE>
-__device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, int K, int kl,
+__device__ __forceinline__ void quant_segment(const float (&v)[8], bool active, int kl,
                                               uint8_t *__restrict__ crow,
                                               uint16_t *__restrict__ srow,
                                               uint8_t *__restrict__ zrow, void *__restrict__ orow,
                                               uint32_t *flags) {
   constexpr int G = BITS == 4 ? 128 : 64;
-  constexpr int LPG = G / 8;  // lanes per group
-  const bool active = kl < K;
-  float v[8];
-  if (active) {
-    const float4 a = *reinterpret_cast<const float4 *>(wrow + kl);
-    const float4 b = *reinterpret_cast<const float4 *>(wrow + kl + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  constexpr int LPG = G / 8;  // lanes per group: 16 (one DPP row) or 8 (half a row)
+  const int lane = threadIdx.x & (kLanes - 1);
+  // IEEE 754-2019 minimum / maximum (NaN-propagating, v_minimum3 /
+  // v_maximum3): they need no operand canonicalization, and a group holding
+  // NaN gets unspecified codes anyway (it is flagged below)
+  auto mn = [](float a, float b) { return __builtin_elementwise_minimum(a, b); };
+  auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  float lo = mn(mn(mn(v[0], v[1]), mn(v[2], v[3])), mn(mn(v[4], v[5]), mn(v[6], v[7])));
+  float hi = mx(mx(mx(v[0], v[1]), mx(v[2], v[3])), mx(mx(v[4], v[5]), mx(v[6], v[7])));
+  // butterfly inside the group's lanes: xor 1, xor 2 (quads), then the
+  // mirrors that pair the quads of a half row and the halves of a row
+  lo = mn(lo, dppf<0xb1>(lo));
+  hi = mx(hi, dppf<0xb1>(hi));
+  lo = mn(lo, dppf<0x4e>(lo));
+  hi = mx(hi, dppf<0x4e>(hi));
+  lo = mn(lo, dppf<0x141>(lo));             // row_half_mirror
+  hi = mx(hi, dppf<0x141>(hi));
+  if constexpr (LPG == 16) {
+    lo = mn(lo, dppf<0x140>(lo));           // row_mirror
+    hi = mx(hi, dppf<0x140>(hi));
   }
-  float lo = v[0], hi = v[0];
-  bool finite = __builtin_isfinite(v[0]);
+  // NaN or Inf anywhere in the group (min and max skip NaN)
+  bool nf = false;
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    lo = fminf(lo, v[i]);
-    hi = fmaxf(hi, v[i]);
-    finite = finite && __builtin_isfinite(v[i]);
-  }
-  int nonfinite = finite ? 0 : 1;
-#pragma unroll
-  for (int off = 1; off < LPG; off <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, off));
-    hi = fmaxf(hi, __shfl_xor(hi, off));
-    nonfinite |= __shfl_xor(nonfinite, off);
-  }
-  finite = nonfinite == 0;   // whole group
+  for (int i = 0; i < 8; ++i) nf |= !__builtin_isfinite(v[i]);
+  const uint64_t nfm = __ballot(nf);
+  const bool finite = ((nfm >> (lane & ~(LPG - 1))) & ((1ull << LPG) - 1)) == 0;
   const float qm = (float)((1 << BITS) - 1);
   const float s32 = (hi - lo) / qm;          // correctly rounded fp32 divide
   _Float16 s16 = (_Float16)s32;              // nearest even
   if (s16 == (_Float16)0.0f) s16 = (_Float16)1.0f;
   const float S = (float)s16;
-  const float zr = rintf(-lo / S);
-  const float z = fminf(fmaxf(zr, 0.f), qm);
+  // round(x / S) with x / S the correctly rounded fp32 quotient, for -lo
+  // (the zero point) and the 8 weights.  Only the integer a quotient rounds
+  // to matters, so it is taken from x * (1/S) (relative error below 2^-22
+  // against x / S) wherever that lies clear of the midpoints n + 1/2; a lane
+  // with a quotient within the margin of a midpoint (ties among them)
+  // divides exactly instead.
+  const float rS = __builtin_amdgcn_rcpf(S);
+  auto near_mid = [](float q, float n) {
+    return fabsf(q - n) >= fmaf(-fabsf(q), 0x1p-20f, 0.5f - 0x1p-30f);
+  };
+  const float zq = -lo * rS;
+  float zr = rintf(zq);
+  bool exact = near_mid(zq, zr);
+  float qn[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = v[i] * rS;
+    qn[i] = rintf(q);
+    exact |= near_mid(q, qn[i]);
+  }
+  if (exact) {
+    zr = rintf(-lo / S);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qn[i] = rintf(v[i] / S);
+  }
+  const float z = __builtin_amdgcn_fmed3f(zr, 0.f, qm);
   const bool zclamp = zr < 0.f || zr > qm;   // a group of one sign, away from 0
   uint32_t packed = 0;
   float fq[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float c = fminf(fmaxf(rintf(v[i] / S) + z, 0.f), qm);
+    const float c = __builtin_amdgcn_fmed3f(qn[i] + z, 0.f, qm);
     packed |= ((uint32_t)c) << (BITS * i);
     fq[i] = (c - z) * S;                     // exact: |c - z| <= 15, S has 11 bits
   }
@@ -116,7 +150,6 @@ __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, in
   } else {
     *reinterpret_cast<uint16_t *>(crow + (kl >> 2)) = (uint16_t)packed;
   }
-  const int lane = threadIdx.x & (kLanes - 1);
   if ((lane & (LPG - 1)) == 0) {
     const int gi = kl / G;
     srow[gi] = __builtin_bit_cast(uint16_t, s16);
@@ -130,37 +163,123 @@ __device__ __forceinline__ void quant_segment(const float *__restrict__ wrow, in
   }
 }
 
+// A wave walks a contiguous range of the layout's 512-weight segments (row
+// by row, segment by segment), loading the next segment before it works on
+// the current one, so every wave keeps two segments' reads in flight.  The
+// grid holds as many waves as the chip keeps resident, so the loads of the
+// whole launch overlap with the arithmetic of the waves.
 template <int MODE>
 __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
     LayoutDev L, const float *__restrict__ w, uint8_t *__restrict__ codes,
     uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros, void *__restrict__ wout,
     uint32_t *flags, int segs_per_row) {
-  const int wave = threadIdx.x / kLanes;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int lane = threadIdx.x & (kLanes - 1);
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
   const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
   const int64_t total = (int64_t)L.N * segs_per_row;
-  if (gw >= total) return;
-  const int n = (int)(gw / segs_per_row);
-  const int seg = (int)(gw - (int64_t)n * segs_per_row);
-  const int blk = n / L.block_n;
-  const int r = n - blk * L.block_n;
-  const BlockInfo bi = block_info(L, blk);
-  const float *wrow = w + (int64_t)n * L.K;
-  const int kl = seg * kSeg + lane * 8;
-  void *orow = nullptr;
-  if (MODE != kPack)
-    orow = reinterpret_cast<uint8_t *>(wout) + (int64_t)n * L.K * (MODE == 2 ? 4 : 2);
-  if (bi.bits == 4) {
-    uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)(L.K / 2) : nullptr;
-    const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(L.K / 128);
-    quant_segment<4, MODE>(wrow, L.K, kl, crow, MODE == kPack ? scales + g0 : nullptr,
-                           MODE == kPack ? zeros + g0 : nullptr, orow, flags);
-  } else {
-    uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)(L.K / 4) : nullptr;
-    const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(L.K / 64);
-    quant_segment<2, MODE>(wrow, L.K, kl, crow, MODE == kPack ? scales + g0 : nullptr,
-                           MODE == kPack ? zeros + g0 : nullptr, orow, flags);
+  const int64_t u0 = total * gw / nw, u1 = total * (gw + 1) / nw;
+  if (u0 >= u1) return;
+  int n = (int)(u0 / segs_per_row);
+  int seg = (int)(u0 - (int64_t)n * segs_per_row);
+  const int K = L.K;
+  // loads of segment (n, seg): lanes past the row end load nothing
+  auto load = [&](int nn, int sg, float (&v)[8]) {
+    const int kl = sg * kSeg + lane * 8;
+    if (kl < K) {
+      const float *src = w + (int64_t)nn * K + kl;
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
+      const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + 4));
+      v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+      v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+  };
+  // two segments in flight ahead of the one being quantized
+  auto advance = [&](int &nn, int &sg) {
+    if (++sg == segs_per_row) { sg = 0; ++nn; }
+  };
+  float cur[8], nx1[8];
+  load(n, seg, cur);
+  int n1 = n, s1 = seg;
+  advance(n1, s1);
+  if (u0 + 1 < u1) load(n1, s1, nx1);
+  // the row's block, advanced row by row (the block changes every block_n
+  // rows; its offsets grow by the previous block's size)
+  int blk = n / L.block_n;
+  int r = n - blk * L.block_n;
+  BlockInfo bi = block_info(L, blk);
+  for (int64_t u = u0; u < u1; ++u) {
+    // the segment after the next, loaded before this one is quantized
+    int n2 = n1, s2 = s1;
+    advance(n2, s2);
+    float nx2[8];
+    if (u + 2 < u1) load(n2, s2, nx2);
+    const int nn = n1;
+    const int kl = seg * kSeg + lane * 8;
+    const bool active = kl < K;
+    void *orow = nullptr;
+    if (MODE != kPack) orow = reinterpret_cast<uint8_t *>(wout) + (int64_t)n * K * (MODE == 2 ? 4 : 2);
+    if (bi.bits == 4) {
+      uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)(K / 2) : nullptr;
+      const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(K / 128);
+      quant_segment<4, MODE>(cur, active, kl, crow, MODE == kPack ? scales + g0 : nullptr,
+                             MODE == kPack ? zeros + g0 : nullptr, orow, flags);
+    } else {
+      uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)(K / 4) : nullptr;
+      const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(K / 64);
+      quant_segment<2, MODE>(cur, active, kl, crow, MODE == kPack ? scales + g0 : nullptr,
+                             MODE == kPack ? zeros + g0 : nullptr, orow, flags);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      cur[i] = nx1[i];
+      nx1[i] = nx2[i];
+    }
+    if (nn != n && ++r == L.block_n) {
+      // next block: its codes and groups follow this block's
+      const uint64_t bk = (uint64_t)L.block_n * (uint64_t)K;
+      bi.code_off += bk * (uint64_t)bi.bits / 8u;
+      bi.grp_off += bk / (bi.bits == 4 ? 128u : 64u);
+      ++blk;
+      r = 0;
+      if (blk < L.nblocks) bi.bits = ((L.int4_mask[blk >> 5] >> (blk & 31)) & 1u) ? 4 : 2;
+    }
+    n = n1;
+    seg = s1;
+    n1 = n2;
+    s1 = s2;
   }
+}
+
+// Workgroups of quantize_pack_kernel<MODE> the current device keeps
+// resident (queried once per kernel and device), capped by the work.
+template <int MODE>
+int quant_grid(int64_t waves) {
+  static std::mutex mu;
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int per = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    per = cached[dev];
+    if (!per) {
+      int per_cu = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &per_cu, reinterpret_cast<const void *>(quantize_pack_kernel<MODE>), kWaves * kLanes, 0) !=
+              hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        per_cu = cus = 0;
+      per = per_cu * cus;
+      if (per > 0) cached[dev] = per;
+    }
+  }
+  if (per <= 0) per = 2048;
+  const int64_t need = (waves + kWaves - 1) / kWaves;
+  return (int)(need < per ? need : per);
 }
 
 // ------------------------------------------------------------ dequant
@@ -229,7 +348,7 @@ hipError_t launch_quantize_pack(const LayoutDev &L, const float *w, uint32_t *co
   if (L.N == 0) return hipSuccess;
   const int segs = (L.K + kSeg - 1) / kSeg;
   const int64_t waves = (int64_t)L.N * segs;
-  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  const int blocks = quant_grid<kPack>(waves);
   hipLaunchKernelGGL(quantize_pack_kernel<kPack>, dim3((unsigned)blocks), dim3(kWaves * kLanes), 0, s,
                      L, w, reinterpret_cast<uint8_t *>(codes), scales, zeros, nullptr, flags, segs);
   return hipGetLastError();
@@ -240,16 +359,16 @@ hipError_t launch_fake_quant(const LayoutDev &L, const float *w, gq_dtype out, v
   if (L.N == 0) return hipSuccess;
   const int segs = (L.K + kSeg - 1) / kSeg;
   const int64_t waves = (int64_t)L.N * segs;
-  const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves)), block(kWaves * kLanes);
+  const dim3 block(kWaves * kLanes);
   switch (out) {
     case GQ_BF16:
-      hipLaunchKernelGGL(quantize_pack_kernel<0>, grid, block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
+      hipLaunchKernelGGL(quantize_pack_kernel<0>, dim3(quant_grid<0>(waves)), block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
       break;
     case GQ_FP16:
-      hipLaunchKernelGGL(quantize_pack_kernel<1>, grid, block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
+      hipLaunchKernelGGL(quantize_pack_kernel<1>, dim3(quant_grid<1>(waves)), block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
       break;
     default:
-      hipLaunchKernelGGL(quantize_pack_kernel<2>, grid, block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
+      hipLaunchKernelGGL(quantize_pack_kernel<2>, dim3(quant_grid<2>(waves)), block, 0, s, L, w, nullptr, nullptr, nullptr, w_out, flags, segs);
       break;
   }
   return hipGetLastError();
