@@ -3,21 +3,29 @@
 Headline workload (the `value`): one decode step of the four Llama-3-8B
 linear shapes (N x K = 14336x4096 up/gate, 4096x14336 down, 4096x4096 q/o,
 1024x4096 k/v), weights INT4 with groups of 128, M = 1 bf16 activation row.
-A step is one gq_linear per shape; value = algorithmic bytes of the step
-(packed codes + fp16 scales + uint8 zeros + x + y) / step time.  Weights are
-resident in HBM and 16 copies are rotated (1.16 GB) so the 256 MB Infinity
-Cache cannot serve them.  Steps run as replays of a captured HIP graph.
+A step is one grouped decode call (gq_linear_group) over the four linears;
+value = algorithmic bytes of the step (packed codes + fp16 scales + uint8
+zeros + x + y) / step time.  Weights are resident in HBM and 16 copies are
+rotated (1.16 GB) so the 256 MB Infinity Cache cannot serve them.  Steps
+run as replays of a captured HIP graph.
 
 The same JSON line carries:
-  roofline      the up/gate GEMV kernel alone, bytes per launch / average
-                launch time (HIP events around rotating graph replays),
-                against 8 TB/s HBM; traffic from committed rocprofv3 PMC
-                counters when they were taken on the current kernel source.
-  cpu_baseline  the CPU oracle (tests' reference implementation) timed on
-                a bounded sample of the same workload on this host.
-  secondary     INT2 decode step, INT2 M=4/16, the 224-linear Layer-mix
-                pass, the Channel-mix M=2048 GEMMs (TFLOPS vs 2.5 PFLOP/s
-                bf16/fp16 dense) and quantize+pack of their fp32 weights.
+  roofline      the step's dominant launch (the grouped kernel over the
+                three K = 4096 linears; the down projection's longer rows
+                run in a second launch), bytes per launch / average launch
+                time (HIP events around rotating graph replays on the
+                launching stream), against 8 TB/s HBM; traffic from
+                committed rocprofv3 PMC counters when they were taken on the
+                current kernel source.
+  cpu_baseline  the CPU oracle (the tests' reference implementation) timed on
+                a bounded sample of the same workload on this host, BLAS on
+                every core the process may use; plus a quantize+pack sample.
+  secondary     the same step as four single-linear launches, the INT2 step,
+                INT2 M=4/16, the 224-linear Layer-mix pass (one grouped call
+                and a 224-launch graph), streaming ceilings of black-box torch
+                kernels, the Channel-mix M=2048 GEMMs (TFLOPS vs 2.5 PFLOP/s
+                bf16/fp16 dense), quantize+pack and fake quantization, dX,
+                and KV-cache decode attention.
 """
 from __future__ import annotations
 
@@ -35,7 +43,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
 METRIC = "W4/W2 GEMV effective HBM GB/s (% of peak) + M=2048 GEMM TFLOPS"
-PMC_FILE = os.path.join(ROOT, "profiles", "gemv_int4_upgate_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "gemv_group_int4_decode_pmc.json")
 
 
 def log(*a):
@@ -128,10 +136,21 @@ def decode_pass(gq, sets, xs, ys, c, shapes=None):
         gq.linear(xs[j], sets[j][c], out=ys[j])
 
 
-def time_steps(torch, gq, sets, xs, ys, copies, steps, warmup):
-    """Time exactly `steps` decode steps (graph of `copies` steps + remainder)."""
-    full = GraphTimer(torch, lambda: [decode_pass(gq, sets, xs, ys, c) for c in range(copies)])
-    single = [GraphTimer(torch, lambda c=c: decode_pass(gq, sets, xs, ys, c)) for c in range(copies)]
+def group_plans(gq, sets, xs, ys, copies, shapes=(0, 1, 2, 3)):
+    """One grouped-decode plan per rotated copy of the step's linears."""
+    return [gq.group_plan([(xs[j], sets[j][c], ys[j]) for j in shapes]) for c in range(copies)]
+
+
+def time_steps(torch, gq, sets, xs, ys, copies, steps, warmup, plans=None):
+    """Time exactly `steps` decode steps (graph of `copies` steps + remainder);
+    a step is one grouped call when plans are given, else one gq_linear per
+    linear."""
+    if plans is not None:
+        step = lambda c: gq.linear_group(plans[c])
+    else:
+        step = lambda c: decode_pass(gq, sets, xs, ys, c)
+    full = GraphTimer(torch, lambda: [step(c) for c in range(copies)])
+    single = [GraphTimer(torch, lambda c=c: step(c)) for c in range(copies)]
 
     def run(n):
         t = torch
@@ -159,6 +178,43 @@ def kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=40):
     return t / (reps * copies)
 
 
+def group_avg(torch, gq, plans, reps=40):
+    """Average duration of one grouped call (rotating plans)."""
+    gt = GraphTimer(torch, lambda: [gq.linear_group(p) for p in plans])
+    gt.run(4)
+    t, _ = gt.run(reps)
+    return t / (reps * len(plans))
+
+
+def ceilings(torch):
+    """Streaming rates of black-box torch kernels on this GPU, as context for
+    the fractions of 8 TB/s: a float32 sum (reads the buffer once) and a
+    device copy (reads and writes it), over 1 GB and over 30 MB buffers
+    (the 30 MB case rotates 36 buffers, 1.08 GB, past the Infinity Cache)."""
+    out = {}
+    for label, nbytes, count in (("1GB", 1 << 30, 1), ("30MB", 30 << 20, 36)):
+        bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(count)]
+        dsts = [torch.empty_like(b) for b in bufs]
+        acc = torch.empty((), dtype=torch.float32, device="cuda")
+        reps = 20 if count == 1 else 2
+        st = GraphTimer(torch, lambda: [torch.sum(b, dim=0, out=acc) for b in bufs])
+        st.run(2)
+        t, _ = st.run(reps)
+        ct = GraphTimer(torch, lambda: [d.copy_(b) for b, d in zip(bufs, dsts)])
+        ct.run(2)
+        tc, _ = ct.run(reps)
+        n = reps * count
+        out[f"torch_sum_read_{label}"] = {"GBps": round(nbytes * n / t / 1e9, 1),
+                                          "frac_hbm": round(nbytes * n / t / 1e9 / HBM_PEAK_GBS, 3),
+                                          "us_per_call": round(t / n * 1e6, 2)}
+        out[f"torch_copy_read_write_{label}"] = {"GBps": round(2 * nbytes * n / tc / 1e9, 1),
+                                                 "frac_hbm": round(2 * nbytes * n / tc / 1e9 / HBM_PEAK_GBS, 3),
+                                                 "us_per_call": round(tc / n * 1e6, 2)}
+        del bufs, dsts
+        torch.cuda.empty_cache()
+    return out
+
+
 def pmc_traffic():
     """Calibrated HBM bytes per launch from the committed PMC summary, if the
     kernel source it was taken on is the current one."""
@@ -173,19 +229,45 @@ def pmc_traffic():
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(S, nsteps):
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        for lib in threadpool_info():
+            if lib.get("user_api") == "blas":
+                blas = f"{lib.get('internal_api')} {lib.get('version')} ({lib.get('threading_layer')})"
+                break
+    except ImportError:  # pragma: no cover
+        pass
+    return model, blas
+
+
+def cpu_baseline(S, nsteps, gpu_value):
+    """The oracle timed on this host: the decode step (unpack, fp64 dequant,
+    fp64 matmul with BLAS on every core the process may use) and, apart, a
+    sample of the Channel-mix quantize+pack (single-process numpy)."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
     prep = []
     nbytes = 0
     for j, (N, K) in enumerate(S.LLAMA3_8B_SHAPE_LIST):
         p = O.quantize_pack(S.decode_weight(j), O.Layout(K, N, N, [4]))
         prep.append((S.decode_x(j, 1), p))
         nbytes += decode_bytes(N, K, 4, 1)
-    ctx = threadpool_limits(1) if threadpool_limits else None
+    ctx = threadpool_limits(cores) if threadpool_limits else None
     if ctx:
         ctx.__enter__()
     try:
@@ -197,10 +279,27 @@ def cpu_baseline(S, nsteps):
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
-    return {"value": round(nbytes * nsteps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+    value = nbytes * nsteps / dt / 1e9
+    # quantize+pack: 1024 rows of the 28672 x 8192 Channel-mix matrix (8 blocks)
+    W, bits = S.channel_mix_weight(0)
+    rows = 1024
+    Ws = np.ascontiguousarray(W[:rows])
+    del W
+    lay = O.Layout(Ws.shape[1], rows, 128, bits[: rows // 128])
+    tq = time.perf_counter()
+    qp = O.quantize_pack(Ws, lay)
+    tq = time.perf_counter() - tq
+    qbytes = Ws.nbytes + qp.codes.nbytes + qp.scales.nbytes + qp.zeros.nbytes
+    model, blas = cpu_info()
+    return {"value": round(value, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{nsteps} decode steps (4 INT4 g128 Llama-3-8B linears, M=1) through "
-                      f"oracle.linear (unpack, fp64 dequant, fp64 matmul), {dt:.1f} s on 1 thread"}
+                      f"oracle.linear (unpack, fp64 dequant, fp64 matmul), {dt:.1f} s, BLAS on "
+                      f"{cores} threads",
+            "cpu_model": model, "blas": blas,
+            "gpu_over_cpu": round(gpu_value / value, 1),
+            "quantize_pack": {"GBps": round(qbytes / tq / 1e9, 4), "cores": 1, "seconds": round(tq, 2),
+                              "sample": f"oracle.quantize_pack of {rows} x 8192 fp32 rows of the "
+                                        "28672 x 8192 Channel-mix matrix (numpy, one process)"}}
 
 
 def secondary(torch, gq, S, args):
@@ -208,10 +307,18 @@ def secondary(torch, gq, S, args):
     # INT2 decode step (M=1) and INT2 M=4/16 on up/gate
     copies2 = 32
     sets, xs, ys, nb = build_decode(torch, gq, S, 2, 1, copies2)
-    t, _ = time_steps(torch, gq, sets, xs, ys, copies2, 256, 32)
+    plans = group_plans(gq, sets, xs, ys, copies2)
+    t, _ = time_steps(torch, gq, sets, xs, ys, copies2, 256, 32, plans=plans)
+    tl, _ = time_steps(torch, gq, sets, xs, ys, copies2, 256, 32)
     out["int2_decode_step_M1"] = {"GBps": round(nb * 256 / t / 1e9, 1),
                                   "frac_hbm": round(nb * 256 / t / 1e9 / HBM_PEAK_GBS, 3),
-                                  "us_per_step": round(t / 256 * 1e6, 2), "bytes_per_step": nb}
+                                  "us_per_step": round(t / 256 * 1e6, 2), "bytes_per_step": nb,
+                                  "launch": "one grouped call (gq_linear_group)"}
+    out["int2_decode_step_M1_per_linear"] = {"GBps": round(nb * 256 / tl / 1e9, 1),
+                                             "frac_hbm": round(nb * 256 / tl / 1e9 / HBM_PEAK_GBS, 3),
+                                             "us_per_step": round(tl / 256 * 1e6, 2),
+                                             "launch": "four gq_linear calls"}
+    del plans
     per = {}
     for j, name in enumerate(("up_gate", "down", "q_o", "k_v")):
         N, K = S.LLAMA3_8B_SHAPE_LIST[j]
@@ -251,7 +358,24 @@ def secondary(torch, gq, S, args):
     torch.cuda.synchronize()
     params = sum(N * K for (_, _, N, K, _) in assign)
     lm = {"linears": len(assign), "int4_linears": n4, "bpw": round(pbytes * 8 / params, 4),
-          "packed_bytes": pbytes}
+          "packed_bytes": pbytes,
+          "weights": "drawn on the GPU with torch's generator (normal, sigma 0.02, 0.5% of input "
+                     "channels x20: the decode recipe's distribution, not its values; timing does "
+                     "not depend on the values)"}
+    lg = dict(lm)
+    for M in (1, 2, 4):
+        xs = {K: torch.from_numpy(S.layer_mix_x(K, M).view(np.int16)).cuda().view(torch.bfloat16)
+              for K in (4096, 14336)}
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for (_, _, N, K, _) in assign]
+        plan = gq.group_plan([(xs[p.K], p, y) for p, y in zip(packs, ys)])
+        gt = GraphTimer(torch, lambda: gq.linear_group(plan))
+        gt.run(3)
+        t, _ = gt.run(10)
+        b = pbytes + sum(2 * M * K + 2 * M * N for (_, _, N, K, _) in assign)
+        lg[f"M{M}"] = {"ms_per_pass": round(t / 10 * 1e3, 4), "GBps": round(b * 10 / t / 1e9, 1),
+                       "frac_hbm": round(b * 10 / t / 1e9 / HBM_PEAK_GBS, 3)}
+        del ys, xs, plan
+    out["layer_mix_pass_grouped"] = lg
     for M in (1, 8, 32):
         xs = {K: torch.from_numpy(S.layer_mix_x(K, M).view(np.int16)).cuda().view(torch.bfloat16)
               for K in (4096, 14336)}
@@ -271,6 +395,7 @@ def secondary(torch, gq, S, args):
     out["layer_mix_pass_graph"] = lm
     del packs
     torch.cuda.empty_cache()
+    out["streaming_ceilings"] = ceilings(torch)
 
     out.update(channel_mix(torch, gq, S))
     out.update(kv_decode(torch, gq))
@@ -426,45 +551,62 @@ def main():
     steps = args.steps
     log(f"bench: building INT4 decode weights ({copies} rotated copies)")
     sets, xs, ys, nbytes = build_decode(torch, gq, S, 4, 1, copies)
-    log("bench: timing decode steps")
-    t, wall = time_steps(torch, gq, sets, xs, ys, copies, steps, args.warmup)
+    plans = group_plans(gq, sets, xs, ys, copies)
+    log("bench: timing decode steps (one grouped call per step)")
+    t, wall = time_steps(torch, gq, sets, xs, ys, copies, steps, args.warmup, plans=plans)
     value = nbytes * steps / t / 1e9
     log(f"bench: {value:.1f} GB/s ({t / steps * 1e6:.2f} us/step, wall {wall / steps * 1e6:.2f} us/step)")
+    tl, _ = time_steps(torch, gq, sets, xs, ys, copies, steps, args.warmup)
+    per_linear_step = {"GBps": round(nbytes * steps / tl / 1e9, 1),
+                       "frac_hbm": round(nbytes * steps / tl / 1e9 / HBM_PEAK_GBS, 4),
+                       "us_per_step": round(tl / steps * 1e6, 2), "launch": "four gq_linear calls"}
 
-    # roofline: the up/gate GEMV kernel (largest launch of the step)
-    N, K = S.LLAMA3_8B_SHAPE_LIST[0]
-    per_launch = decode_bytes(N, K, 4, 1)
-    avg = kernel_avg(torch, gq, sets, xs, ys, 0, copies)
+    # roofline: the step's dominant launch, the grouped kernel over the three
+    # K = 4096 linears (up/gate, q/o, k/v); the down projection (K = 14336)
+    # streams its rows in a second launch
+    dom = (0, 2, 3)
+    dom_plans = group_plans(gq, sets, xs, ys, copies, shapes=dom)
+    per_launch = sum(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[j], 4, 1) for j in dom)
+    avg = group_avg(torch, gq, dom_plans)
     achieved = per_launch / avg / 1e9
+    down_plans = group_plans(gq, sets, xs, ys, copies, shapes=(1,))
+    avg_down = group_avg(torch, gq, down_plans)
     per_linear = {}
     for j, name in enumerate(("up_gate", "down", "q_o", "k_v")):
         Nj, Kj = S.LLAMA3_8B_SHAPE_LIST[j]
-        a = avg if j == 0 else kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=20)
+        a = kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=20)
         per_linear[name] = {"us": round(a * 1e6, 2), "GBps": round(decode_bytes(Nj, Kj, 4, 1) / a / 1e9, 1)}
-    log(f"bench: up/gate GEMV {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
+    log(f"bench: dominant launch {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
-                "kernel": "gemv_kernel<bf16, M=1, R=2 rows/wave, NL=2 slices, INT4> on N=14336 K=4096",
-                "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3)}
-    del sets, xs, ys
+                "kernel": "gemv_group_kernel<bf16, M=1, INT4, 1 staging sub-unit, 2-slice load groups, "
+                          "rows in one load group> over up/gate 14336x4096 + q/o 4096x4096 + "
+                          "k/v 1024x4096 (2304 workgroups of 8 rows)",
+                "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3),
+                "second_launch": {"kernel": "gemv_group_kernel streamed rows, down 4096x14336",
+                                  "avg_launch_us": round(avg_down * 1e6, 3),
+                                  "GBps": round(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[1], 4, 1) / avg_down / 1e9, 1)}}
+    del sets, xs, ys, plans, dom_plans, down_plans
     torch.cuda.empty_cache()
 
     sec = None
     if not args.no_secondary:
         log("bench: secondary measurements")
         sec = secondary(torch, gq, S, args)
+        sec["int4_decode_step_M1_per_linear"] = per_linear_step
         sec["int4_M1_per_linear"] = per_linear
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        cpu = cpu_baseline(S, args.cpu_steps)
+        cpu = cpu_baseline(S, args.cpu_steps, value)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(t / steps * 1e3, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Llama-3-8B decode step: 4 linears (N x K = 14336x4096, 4096x14336, "
-                               "4096x4096, 1024x4096), INT4 g128 weights, M=1 bf16 activations",
+                               "4096x4096, 1024x4096), INT4 g128 weights, M=1 bf16 activations, "
+                               "one grouped decode call per step",
                    "bits": 4, "group": 128, "M": 1, "bytes_per_step": nbytes,
                    "rotated_weight_copies": copies, "frac_hbm": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
