@@ -573,7 +573,7 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
   if ((lane & ((64 / V) - 1)) == 0 && idx < V0) {
     const int r = idx / M, m = idx % M;
     if (n0 + r < L.N)
-      y[(int64_t)m * L.N + n0 + r] = ACT == 0 ? f32_to_bf16_rne(tot) : f32_to_f16_bits(tot);
+      store_global16(y, (int64_t)m * L.N + n0 + r, ACT == 0 ? f32_to_bf16_rne(tot) : f32_to_f16_bits(tot));
   }
 }
 
@@ -633,10 +633,11 @@ __device__ __forceinline__ void tile_rows(const LayoutDev &L, const BlockInfo &b
   }
 }
 
-// The wave's R * M sums reduced across lanes; one lane per output stores.
+// The wave's R * M sums reduced across lanes; one lane per output stores
+// y[m][n0 + r] (row stride N) for n0 + r < nlim.
 template <int ACT, int M, int R>
-__device__ __forceinline__ void reduce_store(const float (&acc)[R][M], int lane, int n0, int N,
-                                             uint16_t *y) {
+__device__ __forceinline__ void reduce_store(const float (&acc)[R][M], int lane, int n0, int nlim,
+                                             int N, uint16_t *y) {
   constexpr int V0 = R * M;
   constexpr int V = V0 <= 1 ? 1 : V0 <= 2 ? 2 : V0 <= 4 ? 4 : V0 <= 8 ? 8 : 16;
   float vals[V];
@@ -646,7 +647,8 @@ __device__ __forceinline__ void reduce_store(const float (&acc)[R][M], int lane,
   const int idx = reduced_index<V>(lane);
   if ((lane & ((64 / V) - 1)) == 0 && idx < V0) {
     const int r = idx / M, m = idx % M;
-    if (n0 + r < N) y[(int64_t)m * N + n0 + r] = ACT == 0 ? f32_to_bf16_rne(tot) : f32_to_f16_bits(tot);
+    if (n0 + r < nlim)
+      store_global16(y, (int64_t)m * N + n0 + r, ACT == 0 ? f32_to_bf16_rne(tot) : f32_to_f16_bits(tot));
   }
 }
 
@@ -656,22 +658,43 @@ struct TilePos {
   int si, t, T, T0, T1;
 };
 
-// Grouped decode, one class of a plan.  Workgroup w of G takes the class's
-// chunks of `chunk` tiles w, w + G, ... (a grid of one workgroup per tile
-// when chunk is 1 and G the tile count; a persistent grid otherwise),
-// walking the segment list in order, and runs each tile with the
-// single-linear kernel's arithmetic and order (the outputs are the same
-// bits).  x of a linear is staged once per workgroup while consecutive
-// tiles stay in that linear.  Every branch below depends only on the
-// workgroup and the plan, so the waves of a workgroup meet the same
-// barriers.
+// Row resources of a wave's R rows at run-relative row rw of segment S:
+// rows past the run's end get empty resources (they load zeros and are
+// never stored).
+template <int BITS, int R>
+__device__ __forceinline__ void seg_rows(const GroupSeg &S, int rw, int K, RowRsrc<R> &rr) {
+  using Gm = Geo<BITS>;
+  const uint32_t RB = (uint32_t)(K * BITS / 8), GPR = (uint32_t)(K / Gm::G);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool live = rw + r < S.rows;
+    const uint64_t row = live ? (uint64_t)(rw + r) : 0u;
+    rr.c[r] = make_rsrc(S.codes + row * RB, live ? RB : 0u);
+    rr.s[r] = make_rsrc(S.scales + row * GPR, live ? 2u * GPR : 0u);
+    rr.z[r] = make_rsrc(S.zeros + row * GPR, live ? GPR : 0u);
+  }
+}
+
+// Grouped decode, one class of a plan.  Every tile runs the single-linear
+// kernel's arithmetic and order, so the outputs are the same bits as one
+// gq_linear call per linear.  x of a linear is staged once per workgroup
+// while consecutive tiles stay in that linear.  Every branch below depends
+// only on the workgroup and the plan, so the waves of a workgroup meet the
+// same barriers.
 //
-// PIPE (every row fits one load group and one staged chunk): software
-// pipelined -- each wave issues the loads of its next tile before it works
-// on the current one, so two tiles of codes are in flight per wave; the
-// pipeline restarts where the linear changes (x must be restaged first).
-// Otherwise each tile runs the single-linear kernel's workgroup body (rows
-// in one load group when ONE, else streamed group by group).
+// PIPE (persistent launch; every row fits one load group and one staged
+// chunk): workgroup w of G takes the contiguous tile range of its share of
+// the class's bytes and walks it segment by segment, software pipelined --
+// each wave issues the loads of its next tile before it works on the
+// current one, so two tiles of codes are in flight per wave.  Segment data
+// is read once per segment and a tile's row resources are a multiply-add
+// from the segment's base addresses.  The pipeline restarts where the
+// linear changes (x must be restaged first).
+//
+// Otherwise workgroup w takes the class's chunks of `chunk` tiles
+// w, w + G, ... (a grid of one workgroup per tile when chunk is 1 and G the
+// tile count) and runs each tile with the single-linear kernel's workgroup
+// body (rows in one load group when ONE, else streamed group by group).
 template <int ACT, int M, int BITS, int SS, int NL, bool ONE, bool PIPE>
 __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__restrict__ plan,
                                                               int cls, int chunk) {
@@ -687,6 +710,160 @@ __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__r
   const GroupItemDev *items = reinterpret_cast<const GroupItemDev *>(plan + H.items_off);
   const int nseg = C.nseg;
   const int G = gridDim.x, w = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+  const int lane = threadIdx.x & (kLanes - 1);
+
+  if constexpr (ONE && PIPE) {
+    // byte range [lo, hi) of the class; the tiles whose first byte is in it
+    const int64_t lo = C.bytes * w / G, hi = C.bytes * (w + 1) / G;
+    int ls = 0;
+    {
+      int a = 0, b = nseg - 1;              // last segment starting at or before lo
+      while (a < b) {
+        const int mid = (a + b + 1) >> 1;
+        if (segs[mid].cbyte0 <= lo) a = mid;
+        else b = mid - 1;
+      }
+      ls = a;
+    }
+    int lt = (int)((lo - segs[ls].cbyte0 + segs[ls].tile_bytes - 1) / segs[ls].tile_bytes);
+    if (lt >= segs[ls].ntiles) {
+      if (++ls >= nseg) return;
+      lt = 0;
+    }
+    // Load cursor: the tile whose loads are issued next.  Its segment's
+    // fields are read from the plan once per segment and kept in scalar
+    // registers (stores through y could alias the plan, so fields read
+    // again after a store would be loaded again); within a segment the
+    // cursor steps by one tile with a few adds.
+    int64_t lcb;                            // class byte of the cursor's tile
+    int64_t ltb;                            // bytes per tile of its segment
+    int lend;                               // tiles of the segment
+    int litem;                              // its linear
+    const uint8_t *pc;                      // codes of the wave's first row in the tile
+    const uint16_t *ps;                     // its scales
+    const uint8_t *pz;                      // its zero points
+    int lrows;                              // rows of the run from that row on
+    int ln0, lnlim;                         // that row in the linear; end of the run
+    int K = 0;                              // K of the linear being worked on
+    uint32_t RB = 0, GPR = 0;               // row bytes and groups per row
+    auto open_seg = [&](int sg, int tt) {
+      const GroupSeg &S = segs[sg];
+      const int rw = tt * kGroupTile + wave * R;
+      lcb = S.cbyte0 + (int64_t)tt * S.tile_bytes;
+      ltb = S.tile_bytes;
+      lend = S.ntiles;
+      litem = S.item;
+      const int Ks = items[litem].L.K;
+      const uint32_t rb = (uint32_t)(Ks * BITS / 8), gpr = (uint32_t)(Ks / Gm::G);
+      pc = S.codes + (uint64_t)rw * rb;
+      ps = S.scales + (uint64_t)rw * gpr;
+      pz = S.zeros + (uint64_t)rw * gpr;
+      lrows = S.rows - rw;
+      ln0 = S.tile0 * kGroupTile + rw;
+      lnlim = S.tile0 * kGroupTile + S.rows;
+    };
+    // step the cursor to the next tile of the range; false past its end
+    auto advance = [&]() -> bool {
+      if (++lt < lend) {
+        lcb += ltb;
+        pc += kGroupTile * RB;
+        ps += kGroupTile * GPR;
+        pz += kGroupTile * GPR;
+        lrows -= kGroupTile;
+        ln0 += kGroupTile;
+      } else {
+        if (ls + 1 >= nseg) return false;
+        ++ls;
+        lt = 0;
+        open_seg(ls, 0);
+      }
+      return lcb < hi;
+    };
+    // issue the loads of the cursor's tile into gl (or, when `none`, the
+    // same number of loads of empty resources); rows past the run's end get
+    // empty resources
+    auto issue_cursor = [&](LoadGroup<BITS, R, NL> &gl, bool none) {
+      RowRsrc<R> rr;
+      if (!none) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool live = lrows > r;
+          rr.c[r] = make_rsrc(pc + r * RB, live ? RB : 0u);
+          rr.s[r] = make_rsrc(ps + r * GPR, live ? 2u * GPR : 0u);
+          rr.z[r] = make_rsrc(pz + r * GPR, live ? GPR : 0u);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) rr.c[r] = rr.s[r] = rr.z[r] = make_rsrc(plan, 0u);
+      }
+      issue_group<BITS, R, NL, false>(gl, 0, NL, lane, rr);
+    };
+    open_seg(ls, lt);
+    if (lcb >= hi) return;
+
+    uint4 *pairs = reinterpret_cast<uint4 *>(lds);
+    int item = litem;
+    const uint16_t *yp = nullptr;
+    int yN = 0;
+    auto stage = [&](int it) {
+      const GroupItemDev &I = items[it];
+      K = I.L.K;
+      RB = (uint32_t)(K * BITS / 8);
+      GPR = (uint32_t)(K / Gm::G);
+      yp = reinterpret_cast<const uint16_t *>(I.y);
+      yN = I.L.N;
+      const int ns = (K * BITS / 8 + 1023) >> 10;
+      const uint32_t xbytes = (uint32_t)(M * K) * 2u;
+      StageRegs<SS> st;
+      stage_x_load<BITS, M, SS>(st, make_rsrc(I.x, xbytes), xbytes, K, 0, ns);
+      stage_x_store<BITS, ACT, M, SS>(st, ns, pairs,
+                                      reinterpret_cast<float *>(lds + M * ns * Gm::PW * kLanes));
+      lds_barrier();
+    };
+    // Work on the tile whose codes are in g (outputs from row n0, run end
+    // nlim), after issuing the loads of the next tile of the same linear
+    // into gn; returns false when the range is done.  The loads into gn are
+    // issued on every path (with empty resources when there is no next tile
+    // in this linear, so they return zeros without touching memory): the
+    // wait before the work on g then counts only g's loads.
+    int sn0 = 0, snlim = 0;                 // rows of the tile being worked on
+    auto step = [&](LoadGroup<BITS, R, NL> &g, LoadGroup<BITS, R, NL> &gn) -> bool {
+      const bool more = advance();
+      const bool same = more && litem == item;
+      issue_cursor(gn, !same);
+      const int ns = (K * BITS / 8 + 1023) >> 10;
+      const float *sm = reinterpret_cast<const float *>(lds + M * ns * Gm::PW * kLanes);
+      float acc[R][M];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+      compute_group<BITS, ACT, M, R, NL>(g, 0, ns, 0, lane, pairs, sm, ns, acc);
+      // rows past the run (a partial last tile) are past N: not stored
+      reduce_store<ACT, M, R>(acc, lane, sn0, snlim, yN, const_cast<uint16_t *>(yp));
+      if (!more) return false;
+      if (!same) {
+        // the next tile is in another linear: restage x, then its loads
+        item = litem;
+        lds_barrier();
+        stage(item);
+        issue_cursor(gn, false);
+      }
+      sn0 = ln0;
+      snlim = lnlim;
+      return true;
+    };
+    stage(item);
+    LoadGroup<BITS, R, NL> ga, gb;
+    issue_cursor(ga, false);
+    sn0 = ln0;
+    snlim = lnlim;
+    while (true) {
+      if (!step(ga, gb)) break;
+      if (!step(gb, ga)) break;
+    }
+  } else {
   const int tiles = C.tiles;
   // the segment holding class tile T
   auto seg_of_tile = [&](int T) -> int {
@@ -722,116 +899,33 @@ __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__r
     }
     return true;
   };
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-  const int lane = threadIdx.x & (kLanes - 1);
-
-  if constexpr (ONE && PIPE) {
-    uint4 *pairs = reinterpret_cast<uint4 *>(lds);
-    int item = segs[pos.si].item;
-    // first output channel of the wave in tile p, its block, and its rows
-    auto rows_of = [&](const TilePos &p, RowRsrc<R> &rr) -> int {
-      const GroupItemDev &I = items[segs[p.si].item];
-      const int nb = (segs[p.si].tile0 + p.t) * kGroupTile;
-      const int n0 = nb + wave * R;
-      BlockInfo bi = {BITS, 0, 0};
-      int blk = 0;
-      if (!I.uniform) {
-        blk = nb / I.L.block_n;
-        bi = block_info(I.L, blk);
-      }
-      tile_rows<BITS, R>(I.L, bi, blk, n0, reinterpret_cast<const uint8_t *>(I.codes),
-                         reinterpret_cast<const uint16_t *>(I.scales),
-                         reinterpret_cast<const uint8_t *>(I.zeros), rr);
-      return n0;
-    };
-    auto stage = [&](int it) {
-      const GroupItemDev &I = items[it];
-      const int K = I.L.K;
-      const int ns = (K * BITS / 8 + 1023) >> 10;
-      const uint32_t xbytes = (uint32_t)(M * K) * 2u;
-      StageRegs<SS> st;
-      stage_x_load<BITS, M, SS>(st, make_rsrc(I.x, xbytes), xbytes, K, 0, ns);
-      stage_x_store<BITS, ACT, M, SS>(st, ns, pairs,
-                                      reinterpret_cast<float *>(lds + M * ns * Gm::PW * kLanes));
-      lds_barrier();
-    };
-    // work on tile p (codes in g), after issuing the loads of the next tile
-    // of the same linear into gn; returns false when the range is done
-    auto step = [&](TilePos &p, int &n0, LoadGroup<BITS, R, NL> &g, LoadGroup<BITS, R, NL> &gn,
-                    int &n0n) -> bool {
-      TilePos q = {p.si, p.t + 1, p.T + 1, p.T0, p.T1};
-      const bool more = settle(q);
-      const bool same = more && segs[q.si].item == item;
-      if (same) {
-        RowRsrc<R> rr;
-        n0n = rows_of(q, rr);
-        issue_group<BITS, R, NL, false>(gn, 0, NL, lane, rr);
-      }
-      const GroupItemDev &I = items[item];
-      const int K = I.L.K;
-      const int ns = (K * BITS / 8 + 1023) >> 10;
-      const uint4 *pr = pairs;
-      const float *sm = reinterpret_cast<const float *>(lds + M * ns * Gm::PW * kLanes);
-      float acc[R][M];
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-      compute_group<BITS, ACT, M, R, NL>(g, 0, ns, 0, lane, pr, sm, ns, acc);
-      reduce_store<ACT, M, R>(acc, lane, n0, I.L.N, reinterpret_cast<uint16_t *>(I.y));
-      if (!more) return false;
-      if (!same) {
-        // the next tile is in another linear: restage x, then its loads
-        item = segs[q.si].item;
-        lds_barrier();
-        stage(item);
-        RowRsrc<R> rr;
-        n0n = rows_of(q, rr);
-        issue_group<BITS, R, NL, false>(gn, 0, NL, lane, rr);
-      }
-      p = q;
-      return true;
-    };
-    stage(item);
-    LoadGroup<BITS, R, NL> ga, gb;
-    int n0a = 0, n0b = 0;
-    {
-      RowRsrc<R> rr;
-      n0a = rows_of(pos, rr);
-      issue_group<BITS, R, NL, false>(ga, 0, NL, lane, rr);
+  int prev_item = -1;
+  do {
+    const int item = segs[pos.si].item;
+    const GroupItemDev &I = items[item];
+    const LayoutDev &L = I.L;
+    const int nb = (segs[pos.si].tile0 + pos.t) * kGroupTile;
+    const int n0 = nb + wave * R;
+    const int ns = (L.K * BITS / 8 + 1023) >> 10;
+    // restage when the linear changes, or every tile when a row does not
+    // fit one staged chunk; the barrier lets every wave finish reading
+    // the previous x first
+    const bool stage = item != prev_item || ns > chunk_slices(BITS, M, SS);
+    if (stage && prev_item >= 0) lds_barrier();
+    BlockInfo bi = {BITS, 0, 0};
+    int blk = 0;
+    if (!I.uniform) {
+      blk = nb / L.block_n;
+      bi = block_info(L, blk);
     }
-    while (true) {
-      if (!step(pos, n0a, ga, gb, n0b)) break;
-      if (!step(pos, n0b, gb, ga, n0a)) break;
-    }
-  } else {
-    int prev_item = -1;
-    do {
-      const int item = segs[pos.si].item;
-      const GroupItemDev &I = items[item];
-      const LayoutDev &L = I.L;
-      const int nb = (segs[pos.si].tile0 + pos.t) * kGroupTile;
-      const int n0 = nb + wave * R;
-      const int ns = (L.K * BITS / 8 + 1023) >> 10;
-      // restage when the linear changes, or every tile when a row does not
-      // fit one staged chunk; the barrier lets every wave finish reading
-      // the previous x first
-      const bool stage = item != prev_item || ns > chunk_slices(BITS, M, SS);
-      if (stage && prev_item >= 0) lds_barrier();
-      BlockInfo bi = {BITS, 0, 0};
-      int blk = 0;
-      if (!I.uniform) {
-        blk = nb / L.block_n;
-        bi = block_info(L, blk);
-      }
-      gemv_block<BITS, ACT, M, R, NL, SS, ONE>(
-          L, bi, blk, n0, n0 < L.N, reinterpret_cast<const uint16_t *>(I.x),
-          reinterpret_cast<const uint8_t *>(I.codes), reinterpret_cast<const uint16_t *>(I.scales),
-          reinterpret_cast<const uint8_t *>(I.zeros), reinterpret_cast<uint16_t *>(I.y), lds, stage);
-      prev_item = item;
-      ++pos.t;
-      ++pos.T;
-    } while (settle(pos));
+    gemv_block<BITS, ACT, M, R, NL, SS, ONE>(
+        L, bi, blk, n0, n0 < L.N, reinterpret_cast<const uint16_t *>(I.x),
+        reinterpret_cast<const uint8_t *>(I.codes), reinterpret_cast<const uint16_t *>(I.scales),
+        reinterpret_cast<const uint8_t *>(I.zeros), reinterpret_cast<uint16_t *>(I.y), lds, stage);
+    prev_item = item;
+    ++pos.t;
+    ++pos.T;
+  } while (settle(pos));
   }
   }
 }
@@ -1070,6 +1164,7 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
     C.ss = (keys[k] & 15) / 3;
     C.one = (keys[k] & 15) % 3;
     int tiles = 0;
+    int64_t cbytes = 0;
     for (int i = 0; i < count; ++i) {
       const LayoutDev &L = dst[i].L;
       if (L.N == 0) continue;
@@ -1081,18 +1176,28 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
         while (e < L.nblocks && block_info(L, e).bits == C.bits) ++e;
         const int t0 = b * L.block_n / kGroupTile;
         const int t1 = e == L.nblocks ? (L.N + kGroupTile - 1) / kGroupTile : e * L.block_n / kGroupTile;
+        const BlockInfo bi = block_info(L, b);
+        const int64_t rb = (int64_t)L.K * C.bits / 8;
         GroupSeg &S = segs[si++];
+        S.codes = reinterpret_cast<const uint8_t *>(items[i].codes) + bi.code_off;
+        S.scales = static_cast<const uint16_t *>(items[i].scales) + bi.grp_off;
+        S.zeros = static_cast<const uint8_t *>(items[i].zeros) + bi.grp_off;
         S.item = i;
         S.tile0 = t0;
         S.ntiles = t1 - t0;
         S.ctile0 = tiles;
+        S.rows = (e == L.nblocks ? L.N : e * L.block_n) - b * L.block_n;
+        S.tile_bytes = (int32_t)(rb * kGroupTile);
+        S.cbyte0 = cbytes;
         tiles += S.ntiles;
+        cbytes += (int64_t)S.ntiles * S.tile_bytes;
         b = e;
       }
       if (c.lds > C.lds) C.lds = c.lds;
     }
     C.nseg = si - C.seg0;
     C.tiles = tiles;
+    C.bytes = cbytes;
   }
   H.nclass = nkeys;
   H.nseg = si;
@@ -1114,7 +1219,7 @@ gq_status gemv_group_check(const void *plan) {
     const GroupClass &C = H.cls[c];
     if (C.seg0 != seg || C.nseg < 1 || (C.bits != 4 && C.bits != 2) ||
         (C.ss != 1 && C.ss != 2 && C.ss != 4) || C.one < 0 || C.one > kGroupNL || C.lds < 0 ||
-        C.lds > kLdsBytes || C.tiles < 1)
+        C.lds > kLdsBytes || C.tiles < 1 || C.bytes < C.tiles)
       return GQ_ERR_SHAPE;
     seg += C.nseg;
   }
@@ -1125,11 +1230,12 @@ hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hip
   const uint8_t *p = static_cast<const uint8_t *>(plan_dev);
   for (int c = 0; c < H.nclass; ++c) {
     const GroupClass &C = H.cls[c];
-    // a class with many tiles per resident workgroup runs as a persistent,
-    // software-pipelined grid taking chunks of kGroupChunk tiles in turn; a
-    // small one as one workgroup per tile (the hardware dispatcher then
-    // overlaps the workgroups' start and end, and no workgroup pays the
-    // pipeline's extra registers for a single tile)
+    // a class with many tiles per resident workgroup runs as a persistent
+    // grid (software pipelined over a byte-balanced contiguous tile range
+    // when its rows fit one load group, else taking chunks of kGroupChunk
+    // tiles in turn); a small one as one workgroup per tile (the hardware
+    // dispatcher then overlaps the workgroups' start and end, and no
+    // workgroup pays the pipeline's extra registers for a single tile)
     const GroupKernel kp = group_kernel(H.act, H.M, C.bits, C.ss, C.one, true);
     if (!kp) return hipErrorInvalidConfiguration;
     const int resident = resident_grid(kp, C.lds);
@@ -1137,7 +1243,7 @@ hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hip
     const bool persist = (int64_t)C.tiles >= (int64_t)kGroupPersistTiles * resident;
     const GroupKernel k = persist ? kp : group_kernel(H.act, H.M, C.bits, C.ss, C.one, false);
     const int chunk = persist ? kGroupChunk : 1;
-    int grid = persist ? resident : C.tiles;
+    const int grid = persist ? (resident < C.tiles ? resident : C.tiles) : C.tiles;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), C.lds, s, p, c, chunk);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -16,7 +16,9 @@ __device__ __forceinline__ Rsrc make_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                            0x00020000);
 }
-// voffset (per lane) is range-checked; soffset (uniform) is added to it.
+// voffset (per lane) and soffset (uniform) are added; the range check is
+// made on the sum, so a row cannot be reached through soffset past the
+// resource's range.
 __device__ __forceinline__ uint4 ld128(Rsrc r, uint32_t off, uint32_t soff = 0) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
@@ -47,6 +49,18 @@ __device__ __forceinline__ uint32_t ld16_nt(Rsrc r, uint32_t off, uint32_t soff 
 }
 __device__ __forceinline__ uint32_t ld8_nt(Rsrc r, uint32_t off, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, kNT);
+}
+
+// 16-bit store through a global address-space pointer.  A pointer read from
+// memory (a plan's output pointer) is generic, and a generic store is a FLAT
+// instruction, which counts on both the vector-memory and the LDS counters;
+// while one is pending the compiler cannot wait for a given number of
+// outstanding loads and falls back to waiting for all of them, which would
+// stall a software pipeline at every tile.  Outputs are always in device
+// memory, so the cast is exact.
+typedef __attribute__((address_space(1))) uint16_t global_u16;
+__device__ __forceinline__ void store_global16(uint16_t *p, int64_t i, uint16_t v) {
+  ((global_u16 *)p)[i] = v;
 }
 
 // (a & m) | o in one VALU op: gfx950's three-input bitwise op with truth

@@ -70,18 +70,24 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 //
 // Work is cut into row tiles of 4 * kGroupR output channels (the GEMV's
 // workgroup tile).  The tiles of one bit-width and kernel configuration form
-// a class, launched once as a persistent grid: workgroup w of G takes the
-// tiles of the class in chunks dealt round-robin (chunk c to workgroup
-// c mod G).  A class is a list of segments, runs of consecutive tiles of one
-// linear (a Channel-mix linear gives one segment per run of same-width
-// blocks).
+// a class, launched once.  A class is a list of segments, runs of
+// consecutive tiles of one linear over which the row stride is uniform (a
+// Channel-mix linear gives one segment per run of same-width blocks); each
+// segment carries the device addresses of its first row's codes, scales and
+// zero points, so a kernel finds any row of it with one multiply.
+//
+// A small class runs one workgroup per tile.  A class with many tiles runs
+// as a persistent grid of G workgroups, workgroup w taking the contiguous
+// range of tiles whose first packed byte (counted over the class) falls in
+// [w * B / G, (w + 1) * B / G), B the class's packed bytes: equal bytes per
+// workgroup however the row lengths of the class's linears differ.
 constexpr uint32_t kGroupMagic = 0x50475147u;   // "GQGP"
-constexpr uint32_t kGroupVersion = 2;
+constexpr uint32_t kGroupVersion = 3;
 constexpr int kGroupMaxClasses = 18;
 constexpr int kGroupR = 2;                       // rows per wave
 constexpr int kGroupNL = 2;                      // 1 KB slices per load group
 constexpr int kGroupTile = 4 * kGroupR;          // rows per tile
-constexpr int kGroupChunk = 4;                   // tiles per chunk of a persistent launch
+constexpr int kGroupChunk = 4;                   // tiles per chunk of a persistent streamed launch
 constexpr int kGroupPersistTiles = 4;            // tiles per resident workgroup to persist
 
 struct GroupClass {
@@ -93,6 +99,7 @@ struct GroupClass {
   int32_t lds;         // dynamic LDS bytes
   int32_t tiles;       // tiles in the class
   int32_t pad;
+  int64_t bytes;       // packed code bytes of the class's tiles (full tiles)
 };
 
 struct GroupPlanHeader {
@@ -122,11 +129,19 @@ struct GroupItemDev {
 };
 
 struct GroupSeg {
+  const uint8_t *codes;    // codes of the run's first row
+  const uint16_t *scales;  // its first scale
+  const uint8_t *zeros;    // its first zero point
+  int64_t cbyte0;          // class code bytes of the tiles before the run
   int32_t item;
-  int32_t tile0;       // first tile of the run, in the linear's tiles
+  int32_t tile0;           // first tile of the run, in the linear's tiles
   int32_t ntiles;
-  int32_t ctile0;      // class tiles before the run
+  int32_t ctile0;          // class tiles before the run
+  int32_t rows;            // output channels in the run (its last tile may be partial)
+  int32_t tile_bytes;      // code bytes of a full tile
+  int32_t pad[2];
 };
+static_assert(sizeof(GroupSeg) == 64, "GroupSeg");
 
 // Host: size of the plan (plan == nullptr) or the plan itself, after
 // checking every item; gemv.hip.
