@@ -16,7 +16,9 @@ Sources (page title, then the part of the page):
         (actual value = (quantized value - zero_point) x scale).
   [QP]  "大模型量化实战：从原理到4-bit部署的完整指南" (jsqmd.com) -- section 2.2:
         Q(x) = round(x/s) + z, s = (x_max - x_min)/(q_max - q_min),
-        z = round(0 - x_min/s), z kept inside the integer range.
+        z = round(0 - x_min/s), z kept inside the integer range; section
+        4.2: one layer (lm_head) kept at 8 bits inside a 4-bit model;
+        section 5.1: a zero-point configuration with groups of 128.
   [GB]  also the Q-SFT and Bitorch Engine paragraphs: full-parameter
         fine-tuning in the quantized weight space, which back-propagates
         through the low-bit weights.
@@ -42,6 +44,8 @@ notes of the repository):
     bits.
   * Channel-mix blocks are 128-output-channel blocks stored one after the
     other; a uniform (Layer-mix) linear is the one-block case.
+  * an 8-bit block (a layer or channel block kept at higher precision) uses
+    the same quantizer with q_max = 255 and groups of 128.
 
 Parity status: every function below is pinned by tests/test_oracle_pins.py
 against values the pages print, closed forms, invariants or brute force.
@@ -64,11 +68,16 @@ FLAG_SCALE_OVERFLOW = 2
 FLAG_ZERO_CLAMPED = 4
 
 # [GB] two-stage quantization paragraph: INT4 uses groups of 128, INT2 groups of 64.
-GROUP_SIZE = {4: 128, 2: 64}
+# 8-bit rows (layers kept at higher precision inside a low-bit model, [QP]
+# section 4.2: lm_head at 8 bits while the other layers stay at 4) take groups
+# of 128: the pages give no 8-bit group size, and 128 is the group size of the
+# zero-point weight-only configuration of [QP] section 5.1 (AWQ).
+GROUP_SIZE = {4: 128, 2: 64, 8: 128}
 
 
 def qmax(bits: int) -> int:
-    """Largest unsigned code: 2^b - 1 ([LB] datatype table: INT4 0~15, INT2 0~3)."""
+    """Largest unsigned code: 2^b - 1 ([LB] datatype table: INT4 0~15, INT2 0~3;
+    8 bits give 256 values, 0..255 in the unsigned frame of [QP] section 2.2)."""
     return (1 << bits) - 1
 
 
@@ -159,8 +168,9 @@ def unpack(words, bits: int, K: int) -> np.ndarray:
 @dataclass
 class Layout:
     """Bit-width map of one linear: N/block_n blocks of block_n output
-    channels, each INT4 (g=128) or INT2 (g=64).  block_n == N is a uniform
-    (Layer-mix) linear; block_n == 128 is Channel-mix ([GB])."""
+    channels, each INT4 (g=128), INT2 (g=64) or INT8 (g=128, rows kept at
+    higher precision).  block_n == N is a uniform (Layer-mix) linear;
+    block_n == 128 is Channel-mix ([GB])."""
     K: int
     N: int
     block_n: int
@@ -170,7 +180,7 @@ class Layout:
         assert self.N % self.block_n == 0, "N must be a multiple of block_n"
         assert len(self.bits) == self.N // self.block_n
         for b in self.bits:
-            assert b in GROUP_SIZE, "bit-widths are 4 or 2"
+            assert b in GROUP_SIZE, "bit-widths are 2, 4 or 8"
             assert self.K % GROUP_SIZE[b] == 0, "K must be a multiple of the group size"
 
     def blocks(self):
@@ -240,8 +250,8 @@ def block_fields(p: Packed, block: int):
 def dequant(p: Packed, rows=None) -> np.ndarray:
     """W_hat[n,k] = (c - z) * S in fp32 ([LB] "Zero Point").
 
-    The product is exact in fp32: |c - z| <= 15 has 4 bits and S has an
-    11-bit significand.  rows: optional iterable of output channels."""
+    The product is exact in fp32: |c - z| <= 255 has at most 8 bits and S
+    has an 11-bit significand.  rows: optional iterable of output channels."""
     L = p.layout
     sel = np.arange(L.N) if rows is None else np.asarray(list(rows), dtype=np.int64)
     out = np.zeros((len(sel), L.K), dtype=np.float32)
