@@ -1,6 +1,7 @@
 /*
  * gq.h -- C ABI of libgq: group-wise asymmetric MinMax weight quantization
- * (INT4 with groups of 128, INT2 with groups of 64) and the weight-only
+ * (INT4 with groups of 128, INT2 with groups of 64, and 8-bit blocks with
+ * groups of 128 for rows kept at higher precision) and the weight-only
  * low-bit matmul that consumes the packed format, for AMD Instinct MI355X
  * (gfx950).
  *
@@ -12,7 +13,10 @@
  *     Channel-mix (bit-width per block of output channels) layouts.
  *   "大模型量化实战：从原理到4-bit部署的完整指南", section 2.2 -- the affine
  *     quantizer Q(x) = round(x/s) + z, s = (x_max - x_min)/(q_max - q_min),
- *     z = round(0 - x_min/s), z kept inside the integer range.
+ *     z = round(0 - x_min/s), z kept inside the integer range; section 4.2
+ *     -- one layer (lm_head) kept at 8 bits inside a 4-bit model; section
+ *     5.1 -- a zero-point configuration with groups of 128, the group size
+ *     taken here for 8-bit blocks (the pages give none).
  *   "Low-bit Quantization: Slimming Large Models to the Extreme", "Zero
  *     Point" -- dequantized value = (quantized value - zero_point) x scale.
  *   "A Survey of Low-bit Large Language Models" (paper review), sections
@@ -61,12 +65,14 @@ typedef enum gq_status {
   GQ_OK = 0,
   GQ_ERR_NULL_ARG = 1,   /* a required pointer is NULL                          */
   GQ_ERR_SHAPE = 2,      /* K<=0, N<0, M<0, N % block_n, K % g, too many blocks */
-  GQ_ERR_BITS = 3,       /* a bit-width other than 2 or 4                       */
+  GQ_ERR_BITS = 3,       /* a bit-width other than 2, 4 or 8                    */
   GQ_ERR_ALIGNMENT = 4,  /* a device pointer is not 16-byte aligned             */
   GQ_ERR_DTYPE = 5,      /* unsupported dtype for this argument                 */
   GQ_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required             */
   GQ_ERR_HIP = 7,        /* the HIP runtime refused a launch                    */
-  GQ_ERR_TOO_LARGE = 8   /* gq_linear_noalloc: scratch need above the static size */
+  GQ_ERR_TOO_LARGE = 8,  /* gq_linear_noalloc: scratch need above the static size */
+  GQ_ERR_UNSUPPORTED = 9 /* a layout with 8-bit blocks on a path without an 8-bit
+                            kernel (gq_linear with M > 4, gq_linear_dx)          */
 } gq_status;
 
 typedef enum gq_dtype { GQ_BF16 = 0, GQ_FP16 = 1, GQ_FP32 = 2 } gq_dtype;
@@ -85,11 +91,16 @@ typedef enum gq_dtype { GQ_BF16 = 0, GQ_FP16 = 1, GQ_FP32 = 2 } gq_dtype;
 
 /* Bit-width map of one linear (the mixed-precision layouts of GreenBitAI's
  * two-stage quantization).  N/block_n blocks of block_n consecutive output
- * channels; bits[i] in {4, 2} is block i's width (INT4 uses groups of 128,
- * INT2 groups of 64).  A uniform linear (Layer-mix) has block_n == N and one
- * entry; Channel-mix uses block_n == 128.  Rules: N % block_n == 0; when there
- * is more than one block, block_n % 128 == 0; K is a positive multiple of 128
- * if any block is INT4, else of 64.  `bits` is a HOST array. */
+ * channels; bits[i] in {4, 2, 8} is block i's width (INT4 uses groups of 128,
+ * INT2 groups of 64; 8 marks a block kept at higher precision, groups of
+ * 128, as section 4.2 of the 4-bit deployment guide keeps lm_head at 8 bits).
+ * A uniform linear (Layer-mix) has block_n == N and one entry; Channel-mix
+ * uses block_n == 128.  Rules: N % block_n == 0; when there is more than one
+ * block, block_n % 128 == 0; K is a positive multiple of 128 if any block is
+ * INT4 or 8-bit, else of 64.  `bits` is a HOST array.  Layouts with 8-bit
+ * blocks are accepted by gq_packed_bytes, gq_quantize_pack, gq_dequant,
+ * gq_fake_quant, gq_linear / gq_linear_noalloc with M <= 4 and the grouped
+ * decode calls; the other paths return GQ_ERR_UNSUPPORTED. */
 typedef struct gq_layout {
   int32_t K;
   int32_t N;
@@ -98,8 +109,11 @@ typedef struct gq_layout {
 } gq_layout;
 
 /* Sizes of the three packed buffers for `layout`, in bytes (HOST outputs).
- * codes: sum over blocks of block_n*K*b/8; scales: 2 bytes per group;
- * zeros: 1 byte per group.  Pure host computation. */
+ * codes: sum over blocks of block_n*K*b/8, b bits per weight with nothing
+ * between codes (the dense sizes of the memory table of "Low-bit
+ * Quantization: Slimming Large Models to the Extreme": INT4 35 GB and INT2
+ * 17.5 GB for 70e9 weights); scales: 2 bytes per group; zeros: 1 byte per
+ * group.  Pure host computation. */
 gq_status gq_packed_bytes(const gq_layout *layout, size_t *codes_bytes,
                           size_t *scales_bytes, size_t *zeros_bytes);
 
@@ -139,7 +153,10 @@ gq_status gq_fake_quant(const gq_layout *layout, const float *w, gq_dtype out_dt
                         uint32_t *flags, void *stream);
 
 /* Workspace gq_linear needs for this layout, M and activation dtype (HOST
- * output *bytes; may be 0).  Pure host computation. */
+ * output *bytes; may be 0): room for the fp16 activations and the split-K
+ * fp32 partials of the floating-point matmul that weight-only quantization
+ * runs after dequantization (the survey review, section 5.2); 0 for M <= 4.
+ * GQ_ERR_UNSUPPORTED for 8-bit blocks with M > 4.  Pure host computation. */
 gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
                                     size_t *bytes);
 
@@ -243,8 +260,11 @@ gq_status gq_group_plan(int32_t count, const gq_group_item *items, int32_t M, gq
 gq_status gq_linear_group(const void *plan, const void *plan_dev, void *stream);
 
 /* Workspace gq_linear_dx needs for this layout, M and dtype (HOST output
- * *bytes; may be 0).  Returns GQ_ERR_SHAPE where gq_linear_dx would (N not a
- * multiple of 8, or buffers past 2 GiB).  Pure host computation. */
+ * *bytes; may be 0): the fp16 form of dy and the fp32 partials of the
+ * data-gradient product (GreenBitAI, the Q-SFT paragraph: training through
+ * the quantized weights).  Returns GQ_ERR_SHAPE where gq_linear_dx would (N
+ * not a multiple of 8, or buffers past 2 GiB) and GQ_ERR_UNSUPPORTED for
+ * 8-bit blocks.  Pure host computation. */
 gq_status gq_linear_dx_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype act,
                                        size_t *bytes);
 
@@ -301,7 +321,9 @@ typedef struct gq_kv_cache {
   const void *v_window;
 } gq_kv_cache;
 
-/* Workspace gq_kv_attention needs (HOST output *bytes).  Pure host. */
+/* Workspace gq_kv_attention needs (HOST output *bytes): the per-split
+ * softmax statistics and partial outputs of the decode attention over the
+ * quantized cache (the survey review's KV-cache bullet).  Pure host. */
 gq_status gq_kv_attention_workspace_bytes(const gq_kv_cache *cache, size_t *bytes);
 
 /* One decode step: for every sequence b and query head h (key/value head

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgq.so")
 
 GQ_OK, GQ_ERR_NULL_ARG, GQ_ERR_SHAPE, GQ_ERR_BITS, GQ_ERR_ALIGNMENT, GQ_ERR_DTYPE, \
-    GQ_ERR_WORKSPACE, GQ_ERR_HIP, GQ_ERR_TOO_LARGE = range(9)
+    GQ_ERR_WORKSPACE, GQ_ERR_HIP, GQ_ERR_TOO_LARGE, GQ_ERR_UNSUPPORTED = range(10)
 GQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 GQ_BF16, GQ_FP16, GQ_FP32 = 0, 1, 2
 GQ_FLAG_NONFINITE = 1
@@ -104,6 +104,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 def make_layout(K: int, N: int, block_n: int, bits) -> gq_layout:
+    """A gq_layout over a host copy of `bits`.  The C side reads N / block_n
+    entries, so a shorter list is refused here (it would be read past its
+    end)."""
+    if int(block_n) > 0 and int(N) >= 0 and int(N) % int(block_n) == 0 and len(bits) < int(N) // int(block_n):
+        raise ValueError(f"bits needs N / block_n = {int(N) // int(block_n)} entries, got {len(bits)}")
     arr = (ctypes.c_uint8 * max(1, len(bits)))(*[int(b) for b in bits])
     lay = gq_layout(int(K), int(N), int(block_n), ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8)))
     lay._keep = arr  # keep the host array alive with the struct
@@ -299,7 +304,8 @@ def empty_packed(K: int, N: int, bits, block_n: int | None = None, device="cuda"
 def quantize_pack(w: torch.Tensor, bits, block_n: int | None = None, stream=None) -> Packed:
     """Quantize fp32 weights w [N][K] group-wise (INT4 g128 / INT2 g64).
 
-    bits: 4, 2, or a list with one entry per block of block_n output channels."""
+    bits: 4, 2, 8, or a list with one entry per block of block_n output
+    channels (8 marks rows kept at higher precision: groups of 128)."""
     _cuda(w, "w")
     if w.dtype != torch.float32 or w.dim() != 2:
         raise ValueError("w must be a 2-D float32 tensor [N][K]")

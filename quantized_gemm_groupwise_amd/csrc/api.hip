@@ -58,6 +58,7 @@ gq_status check_linear(const gq_layout *layout, int32_t M, gq_dtype act, const v
   if (st != GQ_OK) return st;
   if (M < 0) return GQ_ERR_SHAPE;
   if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  if (L->n8 > 0 && M > kGemvMaxM) return GQ_ERR_UNSUPPORTED;   // 8-bit rows: M <= 4 only
   *done = M == 0 || L->N == 0;
   if (*done) return GQ_OK;
   if ((st = check_ptr16(x)) != GQ_OK) return st;
@@ -92,7 +93,7 @@ gq_status gq_packed_bytes(const gq_layout *layout, size_t *codes_bytes, size_t *
   for (int i = 0; i < L.nblocks; ++i) {
     const int b = layout->bits[i];
     cb += (size_t)L.block_n * (size_t)L.K * (size_t)b / 8u;
-    ng += (size_t)L.block_n * (size_t)L.K / (b == 4 ? 128u : 64u);
+    ng += (size_t)L.block_n * (size_t)L.K / (size_t)group_size(b);
   }
   *codes_bytes = cb;
   *scales_bytes = ng * 2u;
@@ -152,6 +153,7 @@ gq_status gq_linear_workspace_bytes(const gq_layout *layout, int32_t M, gq_dtype
   if (st != GQ_OK) return st;
   if (M < 0) return GQ_ERR_SHAPE;
   if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  if (L.n8 > 0 && M > kGemvMaxM) return GQ_ERR_UNSUPPORTED;
   *bytes = linear_workspace_bytes(L, M, act);
   return GQ_OK;
 }
@@ -217,6 +219,7 @@ gq_status gq_linear_dx_workspace_bytes(const gq_layout *layout, int32_t M, gq_dt
   if (st != GQ_OK) return st;
   if (M < 0) return GQ_ERR_SHAPE;
   if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  if (L.n8 > 0) return GQ_ERR_UNSUPPORTED;
   if (M > 0 && L.N > 0 && !dx_supported(L, M)) return GQ_ERR_SHAPE;
   *bytes = dx_workspace_bytes(L, M);
   return GQ_OK;
@@ -230,6 +233,7 @@ gq_status gq_linear_dx(const gq_layout *layout, int32_t M, gq_dtype act, const v
   if (st != GQ_OK) return st;
   if (M < 0) return GQ_ERR_SHAPE;
   if (act != GQ_BF16 && act != GQ_FP16) return GQ_ERR_DTYPE;
+  if (L.n8 > 0) return GQ_ERR_UNSUPPORTED;
   if (M == 0) return GQ_OK;
   if (L.N > 0 && !dx_supported(L, M)) return GQ_ERR_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -286,13 +290,15 @@ const char *gq_status_string(gq_status status) {
     case GQ_OK: return "GQ_OK: success";
     case GQ_ERR_NULL_ARG: return "GQ_ERR_NULL_ARG: a required pointer is NULL";
     case GQ_ERR_SHAPE: return "GQ_ERR_SHAPE: invalid K, N, M or block layout";
-    case GQ_ERR_BITS: return "GQ_ERR_BITS: bit-widths must be 2 or 4";
+    case GQ_ERR_BITS: return "GQ_ERR_BITS: bit-widths must be 2, 4 or 8";
     case GQ_ERR_ALIGNMENT: return "GQ_ERR_ALIGNMENT: a device pointer is misaligned";
     case GQ_ERR_DTYPE: return "GQ_ERR_DTYPE: unsupported dtype";
     case GQ_ERR_WORKSPACE: return "GQ_ERR_WORKSPACE: workspace missing or too small";
     case GQ_ERR_HIP: return "GQ_ERR_HIP: the HIP runtime refused a launch";
     case GQ_ERR_TOO_LARGE:
       return "GQ_ERR_TOO_LARGE: the call needs more scratch than the library's static buffer holds";
+    case GQ_ERR_UNSUPPORTED:
+      return "GQ_ERR_UNSUPPORTED: this path has no kernel for the layout's 8-bit blocks";
   }
   return "unknown gq_status";
 }

@@ -178,11 +178,11 @@ __device__ __forceinline__ int reduced_index(int lane) {
 // Geometry of one bit-width.
 template <int BITS>
 struct Geo {
-  static constexpr int G = BITS == 4 ? 128 : 64;       // group size
+  static constexpr int G = group_size(BITS);            // group size
   static constexpr int KPL = 128 / BITS;                // k per lane per slice
   static constexpr int SK = KPL * kLanes;               // k per slice
   static constexpr int PW = KPL / 2;                    // activation pair words per lane-slice
-  static constexpr int NSUM = BITS == 4 ? 1 : 2;        // floats per lane-slice in the sum table
+  static constexpr int NSUM = BITS == 2 ? 2 : 1;        // floats per lane-slice in the sum table
   static constexpr int SPU = KPL / 16;                  // staging sub-units per lane-slice
 };
 
@@ -256,6 +256,18 @@ __device__ __forceinline__ void stage_x_store(const StageRegs<SS> &st, int nslic
       for (int t = 0; t < 8; ++t) s = dot2<ACT>(p[t], ONES, s);
       s += dpp<0xb1>(s);                        // the other sub-unit of the unit
       s0 = s;
+      s1 = 0.f;
+    } else if constexpr (BITS == 8) {
+      // code word w covers k 4w..4w+3: pairs (k_4w, k_4w+2), (k_4w+1, k_4w+3)
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        p[2 * w] = pair_lo(q[2 * w + 1], q[2 * w]);
+        p[2 * w + 1] = pair_hi(q[2 * w + 1], q[2 * w]);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) s = dot2<ACT>(p[t], ONES, s);
+      s0 = s;                                   // one sub-unit per unit: nothing to combine
       s1 = 0.f;
     } else {
       // the code word covers k 0..15: pairs (k_i, k_{i+8}); classes by
@@ -409,6 +421,43 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
         for (int m = 0; m < M; ++m)
           acc[r][m] = fmaf(S, fmaf(-(BIASF + zz), xs[m], pa[r][m] + pb[r][m]), acc[r][m]);
       }
+    } else if constexpr (BITS == 8) {
+      // byte b of code word w is the code of k = 4w + b.  Its low nibble l
+      // and high nibble h go through the 4-bit bias trick separately: pl and
+      // ph accumulate (B + l) x and (B + h) x, and with X = sum x,
+      // sum q x = 16 (ph - B X) + (pl - B X)
+      const uint32_t mask = 0x000f000fu;
+      float pl[R][M], ph[R][M];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) pl[r][m] = ph[r][m] = 0.f;
+      uint32_t xc[M][8];
+      read_chunk(0, xc);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t wv = w == 0 ? g.cw[i][r].x : w == 1 ? g.cw[i][r].y : w == 2 ? g.cw[i][r].z : g.cw[i][r].w;
+          const uint32_t l02 = and_or(wv, mask, bias), h02 = and_or(wv >> 4, mask, bias);
+          const uint32_t l13 = and_or(wv >> 8, mask, bias), h13 = and_or(wv >> 12, mask, bias);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            pl[r][m] = dot2<ACT>(l02, xc[m][2 * w], pl[r][m]);
+            ph[r][m] = dot2<ACT>(h02, xc[m][2 * w], ph[r][m]);
+            pl[r][m] = dot2<ACT>(l13, xc[m][2 * w + 1], pl[r][m]);
+            ph[r][m] = dot2<ACT>(h13, xc[m][2 * w + 1], ph[r][m]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float S = f16_bits_to_f32((uint16_t)g.sb[i][r]);
+        const float zz = (float)g.zb[i][r];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          acc[r][m] = fmaf(S, fmaf(-(17.f * BIASF + zz), xs[m], fmaf(16.f, ph[r][m], pl[r][m])), acc[r][m]);
+      }
     } else {
       const uint32_t m1 = 0x00030003u, m4 = 0x000c000cu, m16 = 0x00300030u;
       float p1[R][M], p4[R][M], p16[R][M];
@@ -460,14 +509,14 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
 // Slices per staged chunk for a bit-width and M: each thread stages at most
 // ss sub-units and the chunk fits kLdsBytes.
 __host__ __device__ constexpr int chunk_slices(int bits, int M, int ss) {
-  const int pw = bits == 4 ? 16 : 32, nsum = bits == 4 ? 1 : 2;
-  const int by_units = ss * kThreads / (M * kLanes * (bits == 4 ? 2 : 4));
+  const int pw = 64 / bits, nsum = bits == 2 ? 2 : 1;
+  const int by_units = ss * kThreads / (M * kLanes * (8 / bits));
   const int by_lds = kLdsBytes / (M * kLanes * 4 * (pw + nsum));
   return by_units < by_lds ? by_units : by_lds;
 }
 
 __host__ __device__ constexpr int stage_bytes(int bits, int M, int nslice_row, int ss) {
-  const int pw = bits == 4 ? 16 : 32, nsum = bits == 4 ? 1 : 2;
+  const int pw = 64 / bits, nsum = bits == 2 ? 2 : 1;
   const int ch = chunk_slices(bits, M, ss);
   const int c = nslice_row < ch ? nslice_row : ch;
   return M * c * kLanes * 4 * (pw + nsum);
@@ -577,9 +626,10 @@ __device__ __forceinline__ void gemv_block(const LayoutDev &L, const BlockInfo &
   }
 }
 
-// BITSEL: 4 or 2 for a uniform (Layer-mix) linear, 0 for a Channel-mix
-// layout where the workgroup reads its block's width from the bit mask (the
-// 4R rows of a workgroup never straddle two blocks).
+// BITSEL: 4, 2 or 8 for a uniform (Layer-mix) linear; 0 for a Channel-mix
+// layout of INT4 and INT2 blocks and 1 for one that also has 8-bit blocks,
+// where the workgroup reads its block's width from the bit masks (the 4R
+// rows of a workgroup never straddle two blocks).
 template <int ACT, int M, int R, int NL, int BITSEL, int SS, bool ONE>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint16_t *__restrict__ x,
                                                         const uint8_t *__restrict__ codes,
@@ -594,6 +644,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint1
   // the launch picks SS so that a chunk holds at least one slice of every
   // bit-width in the layout; other combinations are never launched
   constexpr bool ok4 = chunk_slices(4, M, SS) >= 1, ok2 = chunk_slices(2, M, SS) >= 1;
+  constexpr bool ok8 = chunk_slices(8, M, SS) >= 1;
   if constexpr (BITSEL == 4) {
     BlockInfo bi = {4, 0, 0};
     if constexpr (ok4)
@@ -602,11 +653,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(LayoutDev L, const uint1
     BlockInfo bi = {2, 0, 0};
     if constexpr (ok2)
       gemv_block<2, ACT, M, R, NL, SS, ONE>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
-  } else if constexpr (ok4 && ok2) {
+  } else if constexpr (BITSEL == 8) {
+    BlockInfo bi = {8, 0, 0};
+    if constexpr (ok8)
+      gemv_block<8, ACT, M, R, NL, SS, ONE>(L, bi, 0, n0, active, x, codes, scales, zeros, y, lds);
+  } else if constexpr (ok4 && ok2 && (BITSEL == 0 || ok8)) {
     const int blk = nb / L.block_n;
     const BlockInfo bi = block_info(L, blk);
-    if (__builtin_amdgcn_readfirstlane(bi.bits) == 4)
+    const int bits = __builtin_amdgcn_readfirstlane(bi.bits);
+    if (bits == 4)
       gemv_block<4, ACT, M, R, NL, SS, ONE>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
+    else if (BITSEL == 1 && bits == 8)
+      gemv_block<8, ACT, M, R, NL, SS, ONE>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
     else
       gemv_block<2, ACT, M, R, NL, SS, ONE>(L, bi, blk, n0, active, x, codes, scales, zeros, y, lds);
   }
@@ -939,9 +997,12 @@ hipError_t launch_rows(const LayoutDev &L, int bitsel, const void *x, const uint
   uint16_t *yp = reinterpret_cast<uint16_t *>(y);
   const dim3 g(blocks), b(kThreads);
   const int ns4 = (L.K * 4 / 8 + 1023) / 1024, ns2 = (L.K * 2 / 8 + 1023) / 1024;
+  const int ns8 = (L.K + 1023) / 1024;
   const int s4 = stage_bytes(4, M, ns4, SS), s2 = stage_bytes(2, M, ns2, SS);
+  const int s8 = stage_bytes(8, M, ns8, SS);
   const bool one4 = ns4 <= NL && ns4 <= chunk_slices(4, M, SS);
   const bool one2 = ns2 <= NL && ns2 <= chunk_slices(2, M, SS);
+  const bool one8 = ns8 <= NL && ns8 <= chunk_slices(8, M, SS);
   if (bitsel == 4) {
     if (one4)
       hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 4, SS, true>), g, b, s4, s, L, xp, cp, scales, zeros, yp);
@@ -952,12 +1013,24 @@ hipError_t launch_rows(const LayoutDev &L, int bitsel, const void *x, const uint
       hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2, SS, true>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
     else
       hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 2, SS, false>), g, b, s2, s, L, xp, cp, scales, zeros, yp);
-  } else {
+  } else if (bitsel == 8) {
+    if (one8)
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 8, SS, true>), g, b, s8, s, L, xp, cp, scales, zeros, yp);
+    else
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 8, SS, false>), g, b, s8, s, L, xp, cp, scales, zeros, yp);
+  } else if (bitsel == 0) {
     const int sm = s4 > s2 ? s4 : s2;
     if (one4 && one2)
       hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0, SS, true>), g, b, sm, s, L, xp, cp, scales, zeros, yp);
     else
       hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 0, SS, false>), g, b, sm, s, L, xp, cp, scales, zeros, yp);
+  } else {
+    // a map with 8-bit blocks: rows stream unless every width fits one group
+    const int sm = s4 > s2 ? (s4 > s8 ? s4 : s8) : (s2 > s8 ? s2 : s8);
+    if (one4 && one2 && one8)
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 1, SS, true>), g, b, sm, s, L, xp, cp, scales, zeros, yp);
+    else
+      hipLaunchKernelGGL((gemv_kernel<ACT, M, R, NL, 1, SS, false>), g, b, sm, s, L, xp, cp, scales, zeros, yp);
   }
   return hipGetLastError();
 }
@@ -976,24 +1049,29 @@ hipError_t launch_r(const LayoutDev &L, int bitsel, bool two, int ns, const void
 template <int ACT, int M>
 hipError_t launch_m(const LayoutDev &L, const void *x, const uint32_t *codes,
                     const uint16_t *scales, const uint8_t *zeros, void *y, hipStream_t s) {
-  uint32_t any4 = 0, all4 = ~0u;
+  int n4 = 0, n8 = 0;
   for (int i = 0; i < L.nblocks; ++i) {
-    const uint32_t b = (L.int4_mask[i >> 5] >> (i & 31)) & 1u;
-    any4 |= b;
-    all4 &= b;
+    const int b = block_bits(L, i);
+    n4 += b == 4;
+    n8 += b == 8;
   }
-  const int bitsel = all4 ? 4 : (any4 ? 0 : 2);
+  const int n2 = L.nblocks - n4 - n8;
+  const int bitsel = n4 == L.nblocks ? 4 : n2 == L.nblocks ? 2 : n8 == L.nblocks ? 8 : (n8 ? 1 : 0);
   // Load groups of two 1 KB slices (one for rows of a single slice), issued
   // one group ahead; two rows per wave once N gives >= 2048 waves.  Measured
   // on MI355X over the Llama-3-8B decode shapes: issuing a whole long row at
   // once, or more rows per wave, leaves fewer waves to cover HBM latency.
-  const int ns = (L.K * (any4 ? 4 : 2) / 8 + 1023) / 1024;
+  const int widest = n8 ? 8 : (n4 ? 4 : 2);
+  const int ns = (L.K * widest / 8 + 1023) / 1024;
   const bool two = L.N >= 4096;
-  // staging sub-units per thread that hold a whole row of x (INT2 slices
-  // carry twice the activations of INT4 ones)
+  // staging sub-units per thread that hold a whole row of x (an INT2 slice
+  // carries twice the activations of an INT4 one, an 8-bit slice half)
   const int ns4 = (L.K * 4 / 8 + 1023) / 1024, ns2 = (L.K * 2 / 8 + 1023) / 1024;
-  const int u4 = any4 ? M * kLanes * 2 * ns4 : 0, u2 = all4 ? 0 : M * kLanes * 4 * ns2;
-  const int need = ((u4 > u2 ? u4 : u2) + kThreads - 1) / kThreads;
+  const int ns8 = (L.K + 1023) / 1024;
+  const int u4 = n4 ? M * kLanes * 2 * ns4 : 0, u2 = n2 ? M * kLanes * 4 * ns2 : 0;
+  const int u8 = n8 ? M * kLanes * ns8 : 0;
+  const int um = u4 > u2 ? (u4 > u8 ? u4 : u8) : (u2 > u8 ? u2 : u8);
+  const int need = (um + kThreads - 1) / kThreads;
   if (need <= 1) return launch_r<ACT, M, 1>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
   if (need <= 2) return launch_r<ACT, M, 2>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
   return launch_r<ACT, M, kStageSubMax>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
@@ -1033,6 +1111,7 @@ GroupKernel group_kernel_bits(int ss, int one, bool pipe) {
 
 template <int ACT, int M>
 GroupKernel group_kernel_m(int bits, int ss, int one, bool pipe) {
+  if (bits == 8) return group_kernel_bits<ACT, M, 8>(ss, one, pipe);
   return bits == 4 ? group_kernel_bits<ACT, M, 4>(ss, one, pipe) : group_kernel_bits<ACT, M, 2>(ss, one, pipe);
 }
 
@@ -1077,7 +1156,7 @@ struct WidthCfg {
 
 WidthCfg width_cfg(int bits, int K, int M) {
   const int ns = (K * bits / 8 + 1023) / 1024;
-  const int units = M * kLanes * (bits == 4 ? 2 : 4) * ns;
+  const int units = M * kLanes * (8 / bits) * ns;
   const int need = (units + kThreads - 1) / kThreads;
   WidthCfg c;
   c.ss = need <= 1 ? 1 : (need <= 2 ? 2 : kStageSubMax);
@@ -1087,7 +1166,10 @@ WidthCfg width_cfg(int bits, int K, int M) {
   return c;
 }
 
-inline int class_key(int bits, const WidthCfg &c) { return (bits == 4 ? 0 : 16) + c.ss * 3 + c.one; }
+// key of a kernel class: width (4, 2, 8 -> 0, 16, 32), then staging and
+// load-group configuration
+inline int class_key(int bits, const WidthCfg &c) { return (bits == 4 ? 0 : bits == 2 ? 16 : 32) + c.ss * 3 + c.one; }
+inline int key_bits(int key) { return key < 16 ? 4 : key < 32 ? 2 : 8; }
 
 }  // namespace
 
@@ -1117,7 +1199,7 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
       const int key = class_key(bits, width_cfg(bits, L.K, M));
       bool seen = false;
       for (int k = 0; k < nkeys; ++k) seen |= keys[k] == key;
-      if (!seen) keys[nkeys++] = key;   // at most 2 widths x 3 x 3 = 18 keys
+      if (!seen) keys[nkeys++] = key;   // at most 3 widths x 3 x 3 = 27 keys
     }
   }
   if (nseg > INT32_MAX / 2) return GQ_ERR_SHAPE;
@@ -1160,7 +1242,7 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
   for (int k = 0; k < nkeys; ++k) {
     GroupClass &C = H.cls[k];
     C.seg0 = si;
-    C.bits = keys[k] < 16 ? 4 : 2;
+    C.bits = key_bits(keys[k]);
     C.ss = (keys[k] & 15) / 3;
     C.one = (keys[k] & 15) % 3;
     int tiles = 0;
@@ -1217,7 +1299,7 @@ gq_status gemv_group_check(const void *plan) {
   int seg = 0;
   for (int c = 0; c < H.nclass; ++c) {
     const GroupClass &C = H.cls[c];
-    if (C.seg0 != seg || C.nseg < 1 || (C.bits != 4 && C.bits != 2) ||
+    if (C.seg0 != seg || C.nseg < 1 || (C.bits != 4 && C.bits != 2 && C.bits != 8) ||
         (C.ss != 1 && C.ss != 2 && C.ss != 4) || C.one < 0 || C.one > kGroupNL || C.lds < 0 ||
         C.lds > kLdsBytes || C.tiles < 1 || C.bytes < C.tiles)
       return GQ_ERR_SHAPE;

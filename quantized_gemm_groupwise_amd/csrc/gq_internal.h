@@ -11,34 +11,52 @@
 namespace gq {
 
 // Layout as the kernels see it: the bit map of GreenBitAI's Layer-mix /
-// Channel-mix layouts folded into a bit mask (bit i set = block i is INT4,
-// clear = INT2).  Block offsets are popcount prefixes over the mask, so no
-// offset table has to live in device memory.
+// Channel-mix layouts folded into bit masks (bit i of int4_mask set: block
+// i is INT4; of int8_mask: 8-bit; neither: INT2).  Block offsets are
+// popcount prefixes over the masks, so no offset table has to live in
+// device memory.
 struct LayoutDev {
   int32_t K;
   int32_t N;
   int32_t block_n;
   int32_t nblocks;
+  int32_t n8;          // 8-bit blocks in the map
+  int32_t pad[3];
   uint32_t int4_mask[GQ_MAX_BLOCKS / 32];
+  uint32_t int8_mask[GQ_MAX_BLOCKS / 32];
 };
 
 struct BlockInfo {
-  int bits;            // 4 or 2
+  int bits;            // 2, 4 or 8
   uint64_t code_off;   // byte offset of the block's codes
   uint64_t grp_off;    // index of the block's first scale / zero
 };
 
+// Weights per group: 64 for INT2, 128 for INT4 and 8-bit.
+__host__ __device__ constexpr int group_size(int bits) { return bits == 2 ? 64 : 128; }
+
+__host__ __device__ inline int block_bits(const LayoutDev &L, int blk) {
+  const uint32_t bit = 1u << (blk & 31);
+  return (L.int8_mask[blk >> 5] & bit) ? 8 : (L.int4_mask[blk >> 5] & bit) ? 4 : 2;
+}
+
 __host__ __device__ inline BlockInfo block_info(const LayoutDev &L, int blk) {
-  int c4 = 0;  // INT4 blocks before blk
+  int c4 = 0, c8 = 0;  // INT4 and 8-bit blocks before blk
   const int w = blk >> 5;
-  for (int i = 0; i < w; ++i) c4 += __builtin_popcount(L.int4_mask[i]);
-  c4 += __builtin_popcount(L.int4_mask[w] & ((1u << (blk & 31)) - 1u));
+  for (int i = 0; i < w; ++i) {
+    c4 += __builtin_popcount(L.int4_mask[i]);
+    c8 += __builtin_popcount(L.int8_mask[i]);
+  }
+  const uint32_t below = (1u << (blk & 31)) - 1u;
+  c4 += __builtin_popcount(L.int4_mask[w] & below);
+  c8 += __builtin_popcount(L.int8_mask[w] & below);
   BlockInfo b;
-  b.bits = ((L.int4_mask[w] >> (blk & 31)) & 1u) ? 4 : 2;
+  b.bits = block_bits(L, blk);
   const uint64_t bk = (uint64_t)L.block_n * (uint64_t)L.K;
-  // INT4 rows take K/2 bytes and K/128 groups, INT2 rows K/4 bytes and K/64 groups.
-  b.code_off = bk * (uint64_t)(blk + c4) / 4u;
-  b.grp_off = bk * (uint64_t)(2 * blk - c4) / 128u;
+  // INT2 rows take K/4 bytes and K/64 groups, INT4 rows K/2 bytes and K/128
+  // groups, 8-bit rows K bytes and K/128 groups.
+  b.code_off = bk * (uint64_t)(blk + c4 + 3 * c8) / 4u;
+  b.grp_off = bk * (uint64_t)(2 * blk - c4 - c8) / 128u;
   return b;
 }
 
@@ -83,7 +101,7 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 // workgroup however the row lengths of the class's linears differ.
 constexpr uint32_t kGroupMagic = 0x50475147u;   // "GQGP"
 constexpr uint32_t kGroupVersion = 3;
-constexpr int kGroupMaxClasses = 18;
+constexpr int kGroupMaxClasses = 27;                // 3 widths x 3 staging x 3 load-group configs
 constexpr int kGroupR = 2;                       // rows per wave
 constexpr int kGroupNL = 2;                      // 1 KB slices per load group
 constexpr int kGroupTile = 4 * kGroupR;          // rows per tile

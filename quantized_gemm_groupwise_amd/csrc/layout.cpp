@@ -21,14 +21,17 @@ gq_status make_layout(const gq_layout *in, LayoutDev *out) {
   out->nblocks = nblocks;
   for (int i = 0; i < nblocks; ++i) {
     const int b = in->bits[i];
-    if (b != 4 && b != 2) return GQ_ERR_BITS;
-    const int g = b == 4 ? 128 : 64;
-    if (in->K % g != 0) return GQ_ERR_SHAPE;
+    if (b != 4 && b != 2 && b != 8) return GQ_ERR_BITS;
+    if (in->K % group_size(b) != 0) return GQ_ERR_SHAPE;
     if (b == 4) out->int4_mask[i >> 5] |= 1u << (i & 31);
+    if (b == 8) {
+      out->int8_mask[i >> 5] |= 1u << (i & 31);
+      ++out->n8;
+    }
   }
   // K * block_n bytes of codes per block must fit the 64-bit offsets; rows of
   // at most 2^31 weights keep the per-row index arithmetic in 32 bits.
-  if ((int64_t)in->K * 4 > (int64_t)INT32_MAX) return GQ_ERR_SHAPE;
+  if ((int64_t)in->K * 8 > (int64_t)INT32_MAX) return GQ_ERR_SHAPE;
   return GQ_OK;
 }
 

@@ -51,7 +51,7 @@ __device__ __forceinline__ void quant_segment(const float (&v)[8], bool active, 
                                               uint16_t *__restrict__ srow,
                                               uint8_t *__restrict__ zrow, void *__restrict__ orow,
                                               uint32_t *flags) {
-  constexpr int G = BITS == 4 ? 128 : 64;
+  constexpr int G = group_size(BITS);
   constexpr int LPG = G / 8;  // lanes per group: 16 (one DPP row) or 8 (half a row)
   const int lane = threadIdx.x & (kLanes - 1);
   // IEEE 754-2019 minimum / maximum (NaN-propagating, v_minimum3 /
@@ -111,13 +111,16 @@ __device__ __forceinline__ void quant_segment(const float (&v)[8], bool active, 
   }
   const float z = __builtin_amdgcn_fmed3f(zr, 0.f, qm);
   const bool zclamp = zr < 0.f || zr > qm;   // a group of one sign, away from 0
-  uint32_t packed = 0;
+  // the lane's 8 codes, packed: 32 bits (INT4), 16 (INT2) or 64 (8-bit,
+  // one byte per code: lo holds codes 0..3, hi codes 4..7)
+  uint32_t packed = 0, packed_hi = 0;
   float fq[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float c = __builtin_amdgcn_fmed3f(qn[i] + z, 0.f, qm);
-    packed |= ((uint32_t)c) << (BITS * i);
-    fq[i] = (c - z) * S;                     // exact: |c - z| <= 15, S has 11 bits
+    if (BITS == 8 && i >= 4) packed_hi |= ((uint32_t)c) << (8 * (i - 4));
+    else packed |= ((uint32_t)c) << (BITS * i);
+    fq[i] = (c - z) * S;                     // exact: |c - z| <= 255, S has 11 bits
   }
   if (MODE != kPack) {
     if (active) {
@@ -145,7 +148,9 @@ __device__ __forceinline__ void quant_segment(const float (&v)[8], bool active, 
     return;
   }
   if (!active) return;
-  if (BITS == 4) {
+  if (BITS == 8) {
+    *reinterpret_cast<uint2 *>(crow + kl) = make_uint2(packed, packed_hi);
+  } else if (BITS == 4) {
     *reinterpret_cast<uint32_t *>(crow + (kl >> 1)) = packed;
   } else {
     *reinterpret_cast<uint16_t *>(crow + (kl >> 2)) = (uint16_t)packed;
@@ -227,6 +232,11 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
       const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(K / 128);
       quant_segment<4, MODE>(cur, active, kl, crow, MODE == kPack ? scales + g0 : nullptr,
                              MODE == kPack ? zeros + g0 : nullptr, orow, flags);
+    } else if (bi.bits == 8) {
+      uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)K : nullptr;
+      const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(K / 128);
+      quant_segment<8, MODE>(cur, active, kl, crow, MODE == kPack ? scales + g0 : nullptr,
+                             MODE == kPack ? zeros + g0 : nullptr, orow, flags);
     } else {
       uint8_t *crow = MODE == kPack ? codes + bi.code_off + (uint64_t)r * (uint64_t)(K / 4) : nullptr;
       const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(K / 64);
@@ -242,10 +252,10 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
       // next block: its codes and groups follow this block's
       const uint64_t bk = (uint64_t)L.block_n * (uint64_t)K;
       bi.code_off += bk * (uint64_t)bi.bits / 8u;
-      bi.grp_off += bk / (bi.bits == 4 ? 128u : 64u);
+      bi.grp_off += bk / (uint64_t)group_size(bi.bits);
       ++blk;
       r = 0;
-      if (blk < L.nblocks) bi.bits = ((L.int4_mask[blk >> 5] >> (blk & 31)) & 1u) ? 4 : 2;
+      if (blk < L.nblocks) bi.bits = block_bits(L, blk);
     }
     n = n1;
     seg = s1;
@@ -284,7 +294,8 @@ int quant_grid(int64_t waves) {
 
 // ------------------------------------------------------------ dequant
 
-// One thread expands one packed uint32 word: 8 INT4 or 16 INT2 weights.
+// One thread expands one packed uint32 word: 8 INT4, 16 INT2 or 4 8-bit
+// weights.
 template <int OUT>  // 0 bf16, 1 fp16, 2 fp32
 __global__ __launch_bounds__(256) void dequant_kernel(LayoutDev L, const uint8_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ scales,
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(LayoutDev L, const uint8_t
   const int words = L.K / per;               // words per row
   const int j = chunk * 256 + (int)threadIdx.x;
   if (j >= words) return;
-  const int g = bits == 4 ? 128 : 64;
+  const int g = group_size(bits);
   const uint32_t *crow =
       reinterpret_cast<const uint32_t *>(codes + bi.code_off + (uint64_t)r * (uint64_t)(L.K * bits / 8));
   const uint64_t g0 = bi.grp_off + (uint64_t)r * (uint64_t)(L.K / g);
@@ -313,7 +324,23 @@ __global__ __launch_bounds__(256) void dequant_kernel(LayoutDev L, const uint8_t
   const float z = (float)zeros[g0 + gi];
   const uint32_t mask = (1u << bits) - 1u;
   const int64_t obase = (int64_t)n * L.K + k0;
-  if (OUT == 2) {
+  if (bits == 8) {
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = ((float)((wd >> (8 * i)) & 255u) - z) * S;
+    if (OUT == 2) {
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + obase) = make_float4(q[0], q[1], q[2], q[3]);
+    } else {
+      uint32_t h[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint16_t ha = OUT == 0 ? f32_to_bf16_rne(q[2 * p]) : f32_to_f16_bits(q[2 * p]);
+        const uint16_t hb = OUT == 0 ? f32_to_bf16_rne(q[2 * p + 1]) : f32_to_f16_bits(q[2 * p + 1]);
+        h[p] = (uint32_t)ha | ((uint32_t)hb << 16);
+      }
+      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + obase) = make_uint2(h[0], h[1]);
+    }
+  } else if (OUT == 2) {
     float *o = reinterpret_cast<float *>(out) + obase;
     for (int i = 0; i < per; i += 4) {
       float4 q;
@@ -377,7 +404,7 @@ hipError_t launch_fake_quant(const LayoutDev &L, const float *w, gq_dtype out, v
 hipError_t launch_dequant(const LayoutDev &L, const uint32_t *codes, const uint16_t *scales,
                           const uint8_t *zeros, gq_dtype out, void *w_out, hipStream_t s) {
   if (L.N == 0) return hipSuccess;
-  const int max_words = L.K / 8;  // INT4 rows have the most words
+  const int max_words = L.n8 > 0 ? L.K / 4 : L.K / 8;  // words of the widest row
   const int chunks = (max_words + 255) / 256;
   const dim3 grid((unsigned)((int64_t)L.N * chunks));
   const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);

@@ -39,6 +39,7 @@ def test_single_hip_runtime_mapped(lib):
 @pytest.mark.parametrize("K,N,block_n,bits", [
     (512, 512, 512, [4]), (4096, 14336, 14336, [4]), (14336, 4096, 4096, [2]),
     (8192, 28672, 128, [4, 2] * 112), (256, 384, 128, [2, 4, 2]), (64, 5, 5, [2]),
+    (4096, 4096, 4096, [8]), (1024, 640, 128, [8, 2, 4, 8, 2]), (128, 3, 3, [8]),
 ])
 def test_packed_sizes_match_oracle_layout(K, N, block_n, bits):
     cb, sb, zb = gq.gq_packed_bytes(gq.make_layout(K, N, block_n, bits))
@@ -57,7 +58,9 @@ def test_layout_validation(lib):
         return lib.gq_packed_bytes(ctypes.byref(lay), ctypes.byref(c), ctypes.byref(s), ctypes.byref(z))
     assert pb(P(512, 512, 512, [4])) == gq.GQ_OK
     assert pb(P(512, 512, 512, [3])) == gq.GQ_ERR_BITS
-    assert pb(P(512, 512, 512, [8])) == gq.GQ_ERR_BITS
+    assert pb(P(512, 512, 512, [16])) == gq.GQ_ERR_BITS
+    assert pb(P(512, 512, 512, [8])) == gq.GQ_OK
+    assert pb(P(192, 512, 512, [8])) == gq.GQ_ERR_SHAPE      # 8-bit groups are 128
     assert pb(P(192, 512, 512, [4])) == gq.GQ_ERR_SHAPE      # K % 128
     assert pb(P(192, 512, 512, [2])) == gq.GQ_OK              # K % 64 ok for INT2
     assert pb(P(100, 512, 512, [2])) == gq.GQ_ERR_SHAPE
@@ -239,8 +242,33 @@ def test_group_plan_refusals_and_size(lib):
     assert lib.gq_linear_group(b0, A, None) == gq.GQ_OK
 
 
+def test_eight_bit_paths_refused_before_launch(lib):
+    """Layouts with 8-bit blocks run quantize/pack, dequant, fake quant, the
+    M <= 4 decode kernel and grouped decode; the other matmul paths refuse
+    them with GQ_ERR_UNSUPPORTED on the host, before any launch."""
+    A = 0x10000
+    for lay in (gq.make_layout(1024, 256, 256, [8]), gq.make_layout(1024, 384, 128, [4, 8, 2])):
+        assert gq.gq_linear_workspace_bytes(lay, 4) == 0
+        for M in (5, 32, 2048):
+            with pytest.raises(gq.GqError) as e:
+                gq.gq_linear_workspace_bytes(lay, M)
+            assert e.value.status == gq.GQ_ERR_UNSUPPORTED
+            assert lib.gq_linear(ctypes.byref(lay), M, gq.GQ_BF16, A, A, A, A, A, A, 1 << 30,
+                                 None) == gq.GQ_ERR_UNSUPPORTED
+            assert lib.gq_linear_noalloc(ctypes.byref(lay), M, gq.GQ_BF16, A, A, A, A, A,
+                                         None) == gq.GQ_ERR_UNSUPPORTED
+        sz = ctypes.c_size_t()
+        assert lib.gq_linear_dx_workspace_bytes(ctypes.byref(lay), 8, gq.GQ_BF16,
+                                                ctypes.byref(sz)) == gq.GQ_ERR_UNSUPPORTED
+        assert lib.gq_linear_dx(ctypes.byref(lay), 8, gq.GQ_BF16, A, A, A, A, A, A, 1 << 30,
+                                None) == gq.GQ_ERR_UNSUPPORTED
+        # grouped decode plans accept them
+        n = gq.gq_group_plan_bytes([gq.gq_group_item(lay, A, A, A, A, A)], 4)
+        assert n > 0
+
+
 def test_status_strings():
-    for st in range(9):
+    for st in range(10):
         assert gq.gq_status_string(st).startswith("GQ_")
     assert "unknown" in gq.gq_status_string(99)
 

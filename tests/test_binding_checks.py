@@ -90,3 +90,15 @@ def test_kv_attention_refuses_bad_q_and_out():
         gq.kv_attention(q, c, out=torch.empty((B, Hq, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="bfloat16"):
         gq.kv_attention(q, c, out=torch.empty((B, Hq, 128), dtype=torch.float32))
+
+
+def test_layout_bits_length_is_checked():
+    """The C side reads N / block_n bit-widths from the host array: a shorter
+    list is refused by the binding instead of being read past its end."""
+    import quantized_gemm_groupwise_amd as gq
+    with pytest.raises(ValueError):
+        gq.make_layout(1024, 4096, 1024, [8])
+    with pytest.raises(ValueError):
+        gq.make_layout(1024, 384, 128, [4, 2])
+    assert gq.make_layout(1024, 256, 128, [4, 8]).N == 256
+    assert gq.make_layout(1024, 0, 1, [4]).N == 0          # no block reads the entry
