@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--copies", type=int, default=16, help="rotated weight copies (defeat MALL)")
+    ap.add_argument("--bits", type=int, default=4, choices=(4, 2),
+                    help="weight width of the headline decode step (4 is the headline; 2 runs the "
+                         "INT2 g64 step alone, for counter runs)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--gemm-only", action="store_true",
                     help="only the Channel-mix M=2048 GEMM measurements (for counter runs)")
@@ -549,8 +552,9 @@ def main():
         return
     copies = args.copies
     steps = args.steps
-    log(f"bench: building INT4 decode weights ({copies} rotated copies)")
-    sets, xs, ys, nbytes = build_decode(torch, gq, S, 4, 1, copies)
+    bits = args.bits
+    log(f"bench: building INT{bits} decode weights ({copies} rotated copies)")
+    sets, xs, ys, nbytes = build_decode(torch, gq, S, bits, 1, copies)
     plans = group_plans(gq, sets, xs, ys, copies)
     log("bench: timing decode steps (one grouped call per step)")
     t, wall = time_steps(torch, gq, sets, xs, ys, copies, steps, args.warmup, plans=plans)
@@ -566,7 +570,7 @@ def main():
     # streams its rows in a second launch
     dom = (0, 2, 3)
     dom_plans = group_plans(gq, sets, xs, ys, copies, shapes=dom)
-    per_launch = sum(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[j], 4, 1) for j in dom)
+    per_launch = sum(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[j], bits, 1) for j in dom)
     avg = group_avg(torch, gq, dom_plans)
     achieved = per_launch / avg / 1e9
     down_plans = group_plans(gq, sets, xs, ys, copies, shapes=(1,))
@@ -575,17 +579,18 @@ def main():
     for j, name in enumerate(("up_gate", "down", "q_o", "k_v")):
         Nj, Kj = S.LLAMA3_8B_SHAPE_LIST[j]
         a = kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=20)
-        per_linear[name] = {"us": round(a * 1e6, 2), "GBps": round(decode_bytes(Nj, Kj, 4, 1) / a / 1e9, 1)}
+        per_linear[name] = {"us": round(a * 1e6, 2), "GBps": round(decode_bytes(Nj, Kj, bits, 1) / a / 1e9, 1)}
     log(f"bench: dominant launch {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(),
-                "kernel": "gemv_group_kernel<bf16, M=1, INT4, 1 staging sub-unit, 2-slice load groups, "
-                          "rows in one load group> over up/gate 14336x4096 + q/o 4096x4096 + "
-                          "k/v 1024x4096 (2304 workgroups of 8 rows)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic() if bits == 4 else None,
+                "kernel": (f"gemv_group_kernel<bf16, M=1, INT{bits}, 1 staging sub-unit, "
+                           f"{2 if bits == 4 else 1}-slice load groups, rows in one load group> over "
+                           "up/gate 14336x4096 + q/o 4096x4096 + k/v 1024x4096 "
+                           "(2432 workgroups of 8 rows)"),
                 "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3),
                 "second_launch": {"kernel": "gemv_group_kernel streamed rows, down 4096x14336",
                                   "avg_launch_us": round(avg_down * 1e6, 3),
-                                  "GBps": round(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[1], 4, 1) / avg_down / 1e9, 1)}}
+                                  "GBps": round(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[1], bits, 1) / avg_down / 1e9, 1)}}
     del sets, xs, ys, plans, dom_plans, down_plans
     torch.cuda.empty_cache()
 
@@ -605,9 +610,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(t / steps * 1e3, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Llama-3-8B decode step: 4 linears (N x K = 14336x4096, 4096x14336, "
-                               "4096x4096, 1024x4096), INT4 g128 weights, M=1 bf16 activations, "
-                               "one grouped decode call per step",
-                   "bits": 4, "group": 128, "M": 1, "bytes_per_step": nbytes,
+                               f"4096x4096, 1024x4096), INT{bits} g{128 if bits == 4 else 64} weights, "
+                               "M=1 bf16 activations, one grouped decode call per step",
+                   "bits": bits, "group": 128 if bits == 4 else 64, "M": 1, "bytes_per_step": nbytes,
                    "rotated_weight_copies": copies, "frac_hbm": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
