@@ -61,7 +61,16 @@
 extern "C" {
 #endif
 
-typedef enum gq_status {
+/* Under C++ both enums have int as their fixed underlying type (the size C
+ * gives them), so any int a C or foreign-function caller passes is a valid
+ * value that the checks below can reject, not undefined behaviour. */
+#ifdef __cplusplus
+#define GQ_ENUM_INT : int
+#else
+#define GQ_ENUM_INT
+#endif
+
+typedef enum gq_status GQ_ENUM_INT {
   GQ_OK = 0,
   GQ_ERR_NULL_ARG = 1,   /* a required pointer is NULL                          */
   GQ_ERR_SHAPE = 2,      /* K<=0, N<0, M<0, N % block_n, K % g, too many blocks */
@@ -75,7 +84,7 @@ typedef enum gq_status {
                             kernel (gq_linear with M > 4, gq_linear_dx)          */
 } gq_status;
 
-typedef enum gq_dtype { GQ_BF16 = 0, GQ_FP16 = 1, GQ_FP32 = 2 } gq_dtype;
+typedef enum gq_dtype GQ_ENUM_INT { GQ_BF16 = 0, GQ_FP16 = 1, GQ_FP32 = 2 } gq_dtype;
 
 /* Device flag bits OR-ed into *flags by gq_quantize_pack and gq_fake_quant. */
 #define GQ_FLAG_NONFINITE 1u      /* a group held NaN or Inf; its codes are unspecified   */
