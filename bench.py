@@ -586,7 +586,7 @@ def main():
                 "kernel": (f"gemv_group_kernel<bf16, M=1, INT{bits}, 1 staging sub-unit, "
                            f"{2 if bits == 4 else 1}-slice load groups, rows in one load group> over "
                            "up/gate 14336x4096 + q/o 4096x4096 + k/v 1024x4096 "
-                           "(2432 workgroups of 8 rows)"),
+                           f"({19456 // (8 if bits == 4 else 16)} workgroups of {8 if bits == 4 else 16} rows)"),
                 "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3),
                 "second_launch": {"kernel": "gemv_group_kernel streamed rows, down 4096x14336",
                                   "avg_launch_us": round(avg_down * 1e6, 3),

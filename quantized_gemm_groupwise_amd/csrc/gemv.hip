@@ -757,7 +757,8 @@ template <int ACT, int M, int BITS, int SS, int NL, bool ONE, bool PIPE>
 __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__restrict__ plan,
                                                               int cls, int chunk) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  constexpr int R = kGroupR;
+  constexpr int R = group_r(BITS);
+  constexpr int kTile = group_tile(BITS);
   using Gm = Geo<BITS>;
   if constexpr (chunk_slices(BITS, M, SS) < 1) {
     return;                                 // never launched: SS too small for M
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__r
     uint32_t RB = 0, GPR = 0;               // row bytes and groups per row
     auto open_seg = [&](int sg, int tt) {
       const GroupSeg &S = segs[sg];
-      const int rw = tt * kGroupTile + wave * R;
+      const int rw = tt * kTile + wave * R;
       lcb = S.cbyte0 + (int64_t)tt * S.tile_bytes;
       ltb = S.tile_bytes;
       lend = S.ntiles;
@@ -818,18 +819,18 @@ __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__r
       ps = S.scales + (uint64_t)rw * gpr;
       pz = S.zeros + (uint64_t)rw * gpr;
       lrows = S.rows - rw;
-      ln0 = S.tile0 * kGroupTile + rw;
-      lnlim = S.tile0 * kGroupTile + S.rows;
+      ln0 = S.tile0 * kTile + rw;
+      lnlim = S.tile0 * kTile + S.rows;
     };
     // step the cursor to the next tile of the range; false past its end
     auto advance = [&]() -> bool {
       if (++lt < lend) {
         lcb += ltb;
-        pc += kGroupTile * RB;
-        ps += kGroupTile * GPR;
-        pz += kGroupTile * GPR;
-        lrows -= kGroupTile;
-        ln0 += kGroupTile;
+        pc += kTile * RB;
+        ps += kTile * GPR;
+        pz += kTile * GPR;
+        lrows -= kTile;
+        ln0 += kTile;
       } else {
         if (ls + 1 >= nseg) return false;
         ++ls;
@@ -962,7 +963,7 @@ __global__ __launch_bounds__(kThreads) void gemv_group_kernel(const uint8_t *__r
     const int item = segs[pos.si].item;
     const GroupItemDev &I = items[item];
     const LayoutDev &L = I.L;
-    const int nb = (segs[pos.si].tile0 + pos.t) * kGroupTile;
+    const int nb = (segs[pos.si].tile0 + pos.t) * kTile;
     const int n0 = nb + wave * R;
     const int ns = (L.K * BITS / 8 + 1023) >> 10;
     // restage when the linear changes, or every tile when a row does not
@@ -1256,8 +1257,9 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
         if (block_info(L, b).bits != C.bits) { ++b; continue; }
         int e = b;
         while (e < L.nblocks && block_info(L, e).bits == C.bits) ++e;
-        const int t0 = b * L.block_n / kGroupTile;
-        const int t1 = e == L.nblocks ? (L.N + kGroupTile - 1) / kGroupTile : e * L.block_n / kGroupTile;
+        const int tile = group_tile(C.bits);
+        const int t0 = b * L.block_n / tile;
+        const int t1 = e == L.nblocks ? (L.N + tile - 1) / tile : e * L.block_n / tile;
         const BlockInfo bi = block_info(L, b);
         const int64_t rb = (int64_t)L.K * C.bits / 8;
         GroupSeg &S = segs[si++];
@@ -1269,7 +1271,7 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
         S.ntiles = t1 - t0;
         S.ctile0 = tiles;
         S.rows = (e == L.nblocks ? L.N : e * L.block_n) - b * L.block_n;
-        S.tile_bytes = (int32_t)(rb * kGroupTile);
+        S.tile_bytes = (int32_t)(rb * tile);
         S.cbyte0 = cbytes;
         tiles += S.ntiles;
         cbytes += (int64_t)S.ntiles * S.tile_bytes;

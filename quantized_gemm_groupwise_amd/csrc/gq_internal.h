@@ -86,8 +86,8 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 // caller keeps a byte copy in device memory, which the kernels read; the
 // host copy gives the launch configuration.
 //
-// Work is cut into row tiles of 4 * kGroupR output channels (the GEMV's
-// workgroup tile).  The tiles of one bit-width and kernel configuration form
+// Work is cut into row tiles of 4 * group_r(bits) output channels (the
+// GEMV's workgroup tile).  The tiles of one bit-width and kernel configuration form
 // a class, launched once.  A class is a list of segments, runs of
 // consecutive tiles of one linear over which the row stride is uniform (a
 // Channel-mix linear gives one segment per run of same-width blocks); each
@@ -102,9 +102,12 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 constexpr uint32_t kGroupMagic = 0x50475147u;   // "GQGP"
 constexpr uint32_t kGroupVersion = 3;
 constexpr int kGroupMaxClasses = 27;                // 3 widths x 3 staging x 3 load-group configs
-constexpr int kGroupR = 2;                       // rows per wave
+// rows per wave: 4 for INT2 rows (a row of K = 4096 is 1 KB, and four per
+// wave amortize the per-tile reduction and bookkeeping), 2 for INT4 and 8-bit
+// rows (twice and four times the bytes per row, and more registers per row)
+__host__ __device__ constexpr int group_r(int bits) { return bits == 2 ? 4 : 2; }
 constexpr int kGroupNL = 2;                      // 1 KB slices per load group
-constexpr int kGroupTile = 4 * kGroupR;          // rows per tile
+__host__ __device__ constexpr int group_tile(int bits) { return 4 * group_r(bits); }   // rows per tile
 constexpr int kGroupChunk = 4;                   // tiles per chunk of a persistent streamed launch
 constexpr int kGroupPersistTiles = 4;            // tiles per resident workgroup to persist
 
