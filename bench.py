@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16
+WARM_SECONDS = 0.1          # sustained replays before each secondary measurement
 METRIC = "W4/W2 GEMV effective HBM GB/s (% of peak) + M=2048 GEMM TFLOPS"
 PMC_FILE = os.path.join(ROOT, "profiles", "gemv_group_int4_decode_pmc.json")
 
@@ -54,7 +55,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=2048,
+                    help="untimed steps first (2048 steps, ~40 ms: past the GPU's power ramp)")
     ap.add_argument("--copies", type=int, default=16, help="rotated weight copies (defeat MALL)")
     ap.add_argument("--bits", type=int, default=4, choices=(4, 2),
                     help="weight width of the headline decode step (4 is the headline; 2 runs the "
@@ -92,6 +94,18 @@ class GraphTimer:
         with torch.cuda.graph(self.g):
             fn()
         torch.cuda.synchronize()
+
+    def warm(self, seconds=None):
+        """Replay for `seconds` of wall time.  Bandwidth-heavy work on this
+        GPU runs up to 20% slower for its first 20-30 ms after an idle spell
+        (the power state ramps with load), so each measurement starts from
+        sustained load."""
+        t = self.torch
+        seconds = WARM_SECONDS if seconds is None else seconds
+        w0 = time.perf_counter()
+        while time.perf_counter() - w0 < seconds:
+            self.g.replay()
+            t.cuda.synchronize()
 
     def run(self, reps):
         t = self.torch
@@ -176,7 +190,7 @@ def time_steps(torch, gq, sets, xs, ys, copies, steps, warmup, plans=None):
 def kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=40):
     """Average duration of one linear's launch (rotating copies)."""
     gt = GraphTimer(torch, lambda: [gq.linear(xs[j], sets[j][c], out=ys[j]) for c in range(copies)])
-    gt.run(4)
+    gt.warm()
     t, _ = gt.run(reps)
     return t / (reps * copies)
 
@@ -184,7 +198,7 @@ def kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=40):
 def group_avg(torch, gq, plans, reps=40):
     """Average duration of one grouped call (rotating plans)."""
     gt = GraphTimer(torch, lambda: [gq.linear_group(p) for p in plans])
-    gt.run(4)
+    gt.warm()
     t, _ = gt.run(reps)
     return t / (reps * len(plans))
 
@@ -201,10 +215,10 @@ def ceilings(torch):
         acc = torch.empty((), dtype=torch.float32, device="cuda")
         reps = 20 if count == 1 else 2
         st = GraphTimer(torch, lambda: [torch.sum(b, dim=0, out=acc) for b in bufs])
-        st.run(2)
+        st.warm()
         t, _ = st.run(reps)
         ct = GraphTimer(torch, lambda: [d.copy_(b) for b, d in zip(bufs, dsts)])
-        ct.run(2)
+        ct.warm()
         tc, _ = ct.run(reps)
         n = reps * count
         out[f"torch_sum_read_{label}"] = {"GBps": round(nbytes * n / t / 1e9, 1),
@@ -372,7 +386,7 @@ def secondary(torch, gq, S, args):
         ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for (_, _, N, K, _) in assign]
         plan = gq.group_plan([(xs[p.K], p, y) for p, y in zip(packs, ys)])
         gt = GraphTimer(torch, lambda: gq.linear_group(plan))
-        gt.run(3)
+        gt.warm()
         t, _ = gt.run(10)
         b = pbytes + sum(2 * M * K + 2 * M * N for (_, _, N, K, _) in assign)
         lg[f"M{M}"] = {"ms_per_pass": round(t / 10 * 1e3, 4), "GBps": round(b * 10 / t / 1e9, 1),
@@ -389,7 +403,7 @@ def secondary(torch, gq, S, args):
             for p, y in zip(packs, ys):
                 gq.linear(xs[p.K], p, out=y, ws=ws)
         gt = GraphTimer(torch, one_pass)
-        gt.run(2)
+        gt.warm()
         t, _ = gt.run(10)
         b = pbytes + sum(2 * M * K + 2 * M * N for (_, _, N, K, _) in assign)
         lm[f"M{M}"] = {"ms_per_pass": round(t / 10 * 1e3, 4), "GBps": round(b * 10 / t / 1e9, 1),
@@ -432,7 +446,7 @@ def kv_decode(torch, gq):
         cache = gq.kv_cache(B, Hq, Hkv, kp, vp, kw, vw)
         ws = gq.workspace(gq.gq_kv_attention_workspace_bytes(cache), "cuda")
         gt = GraphTimer(torch, lambda: gq.kv_attention(q, cache, out=o, ws=ws))
-        gt.run(20)
+        gt.warm()
         t, _ = gt.run(50)
         nbytes = kp.nbytes() + vp.nbytes() + 2 * kw.numel() * 2 + 2 * q.numel() * 2
         out[name] = {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "t_packed": tp, "t_window": tw, "bits": bits,
@@ -458,7 +472,7 @@ def channel_mix(torch, gq, S):
         qt = GraphTimer(torch, lambda: gq.gq_quantize_pack(
             p.layout, W.data_ptr(), p.codes.data_ptr(), p.scales.data_ptr(), p.zeros.data_ptr(),
             p.flags.data_ptr()))
-        qt.run(2)
+        qt.warm()
         t, _ = qt.run(10)
         qb = N * K * 4 + p.nbytes()
         out[f"quantize_pack_mlp{j}"] = {"N": N, "K": K, "us": round(t / 10 * 1e6, 1),
@@ -469,7 +483,7 @@ def channel_mix(torch, gq, S):
         wfq = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
         ft = GraphTimer(torch, lambda: gq.gq_fake_quant(p.layout, W.data_ptr(), gq.GQ_BF16,
                                                         wfq.data_ptr(), p.flags.data_ptr()))
-        ft.run(2)
+        ft.warm()
         t, _ = ft.run(10)
         fb = N * K * (4 + 2)
         out[f"fake_quant_bf16_mlp{j}"] = {"N": N, "K": K, "us": round(t / 10 * 1e6, 1),
@@ -482,7 +496,7 @@ def channel_mix(torch, gq, S):
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         ws = gq.workspace(gq.gq_linear_workspace_bytes(p.layout, M), "cuda")
         gt = GraphTimer(torch, lambda: gq.linear(x, p, out=y, ws=ws))
-        gt.run(20)                                   # warm clocks
+        gt.warm()
         t, _ = gt.run(20)
         fl = 2.0 * M * N * K
         tf = fl * 20 / t / 1e12
@@ -493,7 +507,7 @@ def channel_mix(torch, gq, S):
         wd = torch.randn((K, N), device="cuda", dtype=torch.float16)   # W^T, contiguous
         yd = torch.empty((M, N), device="cuda", dtype=torch.float16)
         dt = GraphTimer(torch, lambda: torch.matmul(xd, wd, out=yd))
-        dt.run(10)
+        dt.warm()
         td, _ = dt.run(20)
         tfd = fl * 20 / td / 1e12
         del xd, wd, yd
@@ -512,7 +526,7 @@ def channel_mix(torch, gq, S):
         dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
         wsd = gq.workspace(gq.gq_linear_dx_workspace_bytes(p.layout, M), "cuda")
         xt = GraphTimer(torch, lambda: gq.linear_dx(dy, p, out=dx, ws=wsd))
-        xt.run(10)
+        xt.warm()
         t, _ = xt.run(20)
         tf = fl * 20 / t / 1e12
         out[f"dx_channel_mix_M2048_mlp{j}"] = {
