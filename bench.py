@@ -579,33 +579,29 @@ def main():
                        "frac_hbm": round(nbytes * steps / tl / 1e9 / HBM_PEAK_GBS, 4),
                        "us_per_step": round(tl / steps * 1e6, 2), "launch": "four gq_linear calls"}
 
-    # roofline: the step's dominant launch, the grouped kernel over the three
-    # K = 4096 linears (up/gate, q/o, k/v); the down projection (K = 14336)
-    # streams its rows in a second launch
-    dom = (0, 2, 3)
-    dom_plans = group_plans(gq, sets, xs, ys, copies, shapes=dom)
-    per_launch = sum(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[j], bits, 1) for j in dom)
-    avg = group_avg(torch, gq, dom_plans)
+    # roofline: the step is one launch (the grouped call's one-workgroup-per-
+    # tile classes run in one grid: down's streamed tiles first, then the
+    # K = 4096 linears' tiles), so the dominant kernel is that launch over
+    # the step's bytes
+    per_launch = nbytes
+    avg = group_avg(torch, gq, plans)
     achieved = per_launch / avg / 1e9
-    down_plans = group_plans(gq, sets, xs, ys, copies, shapes=(1,))
-    avg_down = group_avg(torch, gq, down_plans)
     per_linear = {}
     for j, name in enumerate(("up_gate", "down", "q_o", "k_v")):
         Nj, Kj = S.LLAMA3_8B_SHAPE_LIST[j]
         a = kernel_avg(torch, gq, sets, xs, ys, j, copies, reps=20)
         per_linear[name] = {"us": round(a * 1e6, 2), "GBps": round(decode_bytes(Nj, Kj, bits, 1) / a / 1e9, 1)}
     log(f"bench: dominant launch {avg * 1e6:.2f} us -> {achieved:.1f} GB/s")
+    tile = 8 if bits == 4 else 16
+    down_tiles, short_tiles = 4096 // tile, 19456 // tile
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": pmc_traffic() if bits == 4 else None,
-                "kernel": (f"gemv_group_kernel<bf16, M=1, INT{bits}, 1 staging sub-unit, "
-                           f"{2 if bits == 4 else 1}-slice load groups, rows in one load group> over "
-                           "up/gate 14336x4096 + q/o 4096x4096 + k/v 1024x4096 "
-                           f"({19456 // (8 if bits == 4 else 16)} workgroups of {8 if bits == 4 else 16} rows)"),
-                "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3),
-                "second_launch": {"kernel": "gemv_group_kernel streamed rows, down 4096x14336",
-                                  "avg_launch_us": round(avg_down * 1e6, 3),
-                                  "GBps": round(decode_bytes(*S.LLAMA3_8B_SHAPE_LIST[1], bits, 1) / avg_down / 1e9, 1)}}
-    del sets, xs, ys, plans, dom_plans, down_plans
+                "kernel": (f"gemv_group_fused_kernel<bf16, M=1, INT{bits}>, {down_tiles + short_tiles} "
+                           f"workgroups of {tile} rows: down 4096x14336 ({down_tiles} streamed-row tiles), "
+                           f"then up/gate 14336x4096 + q/o 4096x4096 + k/v 1024x4096 ({short_tiles} tiles "
+                           "of one load group per row)"),
+                "bytes_per_launch": per_launch, "avg_launch_us": round(avg * 1e6, 3)}
+    del sets, xs, ys, plans
     torch.cuda.empty_cache()
 
     sec = None

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgq.so")
-SOURCES = ["api.hip", "layout.cpp", "quant.hip", "gemv.hip", "gemm.hip", "skinny.hip", "dx.hip", "kv.hip"]
+SOURCES = ["api.hip", "layout.cpp", "quant.hip", "gemv.hip", "gemv_group.hip", "gemm.hip", "skinny.hip", "dx.hip", "kv.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

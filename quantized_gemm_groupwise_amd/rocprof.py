@@ -29,7 +29,7 @@ import sys
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # sources whose text decides the decode GEMV kernel (its counters go stale
 # when any of them changes)
-GEMV_SOURCES = ("gemv.hip", "gq_internal.h", "gq_device.h")
+GEMV_SOURCES = ("gemv_group.hip", "gemv_core.h", "gq_internal.h", "gq_device.h")
 
 
 def source_digest(names=GEMV_SOURCES) -> str:

@@ -76,6 +76,34 @@ def test_group_equals_independent_calls(M):
         assert np.array_equal(y_bits(y), y_bits(ref)), f"item {i} {SPECS[i]}: differs from gq_linear"
 
 
+SPECS_ALL_WIDTHS = [
+    (256, 4096, [8], None),                # 8-bit rows of four slices, streamed
+    (64, 1024, [8], None),                 # 8-bit, one slice
+    (40, 2048, [8], None),                 # 8-bit, two slices (ragged tile)
+    (384, 1024, [8, 4, 2], 128),           # Channel-mix with an 8-bit block
+    (24, 512, [4], None),
+    (100, 14336, [4], None),               # long INT4 rows next to short ones
+    (16, 256, [2], None),
+    (48, 8192, [2], None),
+]
+
+
+@pytest.mark.parametrize("M,dtype", [(1, torch.bfloat16), (3, torch.float16), (4, torch.bfloat16)])
+def test_group_fused_launch_all_widths(M, dtype):
+    """Several small classes of each width (8-bit, INT4, INT2), each run by
+    one launch per width that holds all of that width's classes: every output
+    is the bits gq_linear writes."""
+    _say("fused classes, all widths, M =", M, dtype)
+    items = _make(SPECS_ALL_WIDTHS, M, 8700 + M, dtype=dtype)
+    plan = gq.group_plan([(x, p, y) for (x, p, y, _, _) in items])
+    gq.linear_group(plan)
+    torch.cuda.synchronize()
+    for i, (x, p, y, W, xb) in enumerate(items):
+        ref = gq.linear(x, p)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"item {i} {SPECS_ALL_WIDTHS[i]}"
+
+
 def test_group_fp16_activations():
     items = _make(SPECS[:4], 2, 8300, dtype=torch.float16)
     plan = gq.group_plan([(x, p, y) for (x, p, y, _, _) in items])
