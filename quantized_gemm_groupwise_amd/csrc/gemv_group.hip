@@ -321,17 +321,26 @@ constexpr int kFuseMax = 9;                  // 3 staging x 3 load-group configu
 struct FuseArgs {
   int32_t n;                                 // classes in the launch
   int32_t cls[kFuseMax];                     // their indices in the plan
-  int32_t cfg[kFuseMax];                     // 3 * staging sub-units + load-group configuration
+  int32_t one[kFuseMax];                     // their load-group configuration (GroupClass::one)
   int32_t start[kFuseMax + 1];               // first workgroup of each; start[n] = grid
 };
 
-template <int ACT, int M, int BITS, int SS>
-__device__ __forceinline__ void fused_body(int one, const uint8_t *__restrict__ plan, int cls,
-                                           int G, int w, uint32_t *lds) {
-  if (one == 1) group_body<ACT, M, BITS, SS, 1, true, false>(plan, cls, 1, G, w, lds);
-  else if (one == 2) group_body<ACT, M, BITS, SS, 2, true, false>(plan, cls, 1, G, w, lds);
-  else group_body<ACT, M, BITS, SS, kGroupNL, false, false>(plan, cls, 1, G, w, lds);
+// x staging sub-units per thread in the fused launch: the fewest whose
+// staged chunk holds `slices` 1 KB slices.  Which thread stages which 16
+// activations depends on this count, the LDS contents and the per-lane sums
+// do not (a unit's sub-units sit in adjacent lanes of one pass and are
+// combined in a fixed order), so any count whose chunk holds a one-group row
+// gives the bits of the class's own kernel.  Fewer sub-units hold fewer
+// registers, and the fused kernel holds the registers of its largest body.
+__host__ __device__ constexpr int fuse_ss(int bits, int M, int slices) {
+  return chunk_slices(bits, M, 1) >= slices ? 1 : chunk_slices(bits, M, 2) >= slices ? 2 : kStageSubMax;
 }
+// Slices per staged chunk of a streamed row in the fused launch.  Measured
+// on the Llama-3-8B decode step (M = 1): INT4 down rows (7 slices) run
+// fastest in chunks of 2 (one staging sub-unit, the fewest registers, so the
+// most resident workgroups for the launch's other classes), INT2 down rows
+// (4 slices) in one chunk of 4 (no restaging).
+__host__ __device__ constexpr int fuse_stream_chunk(int bits) { return bits == 2 ? 4 : 2; }
 
 // Every one-workgroup-per-tile class of one width in one launch.  Between
 // two launches on a stream the first one's last workgroups finish before
@@ -339,27 +348,30 @@ __device__ __forceinline__ void fused_body(int one, const uint8_t *__restrict__ 
 // class's workgroups as soon as CUs free up, so the launch pays one ramp and
 // one tail instead of one per class.  The classes are ordered longest tiles
 // first, so the workgroups dispatched last are the shortest.  Each
-// workgroup runs the body of its own class (a branch uniform over the
-// workgroup); the kernel holds the registers of the largest body and the
-// LDS of the largest class.
+// workgroup runs the body of its class's load-group configuration (a branch
+// uniform over the workgroup), with the staging of fuse_ss; the LDS is the
+// largest class's.
 template <int ACT, int M, int BITS>
 __global__ __launch_bounds__(kThreads) void gemv_group_fused_kernel(const uint8_t *__restrict__ plan,
                                                                     FuseArgs fa) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int b = blockIdx.x;
-  int cls = fa.cls[0], cfg = fa.cfg[0], s0 = 0, s1 = fa.start[1];
+  int cls = fa.cls[0], one = fa.one[0], s0 = 0, s1 = fa.start[1];
 #pragma unroll
   for (int j = 1; j < kFuseMax; ++j)
     if (j < fa.n && b >= fa.start[j]) {
       cls = fa.cls[j];
-      cfg = fa.cfg[j];
+      one = fa.one[j];
       s0 = fa.start[j];
       s1 = fa.start[j + 1];
     }
-  const int ss = cfg / 3, one = cfg % 3;
-  if (ss == 1) fused_body<ACT, M, BITS, 1>(one, plan, cls, s1 - s0, b - s0, lds);
-  else if (ss == 2) fused_body<ACT, M, BITS, 2>(one, plan, cls, s1 - s0, b - s0, lds);
-  else fused_body<ACT, M, BITS, kStageSubMax>(one, plan, cls, s1 - s0, b - s0, lds);
+  const int G = s1 - s0, w = b - s0;
+  if (one == 1)
+    group_body<ACT, M, BITS, fuse_ss(BITS, M, 1), 1, true, false>(plan, cls, 1, G, w, lds);
+  else if (one == 2)
+    group_body<ACT, M, BITS, fuse_ss(BITS, M, 2), 2, true, false>(plan, cls, 1, G, w, lds);
+  else
+    group_body<ACT, M, BITS, fuse_ss(BITS, M, fuse_stream_chunk(BITS)), kGroupNL, false, false>(plan, cls, 1, G, w, lds);
 }
 
 typedef void (*GroupKernel)(const uint8_t *, int, int);
@@ -628,9 +640,11 @@ hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hip
     FuseArgs &F = fuse[wi];
     if (F.n >= kFuseMax) return hipErrorInvalidConfiguration;
     F.cls[F.n] = c;
-    F.cfg[F.n] = C.ss * 3 + C.one;
+    F.one[F.n] = C.one;
     ++F.n;
-    if (C.lds > fuse_lds[wi]) fuse_lds[wi] = C.lds;
+    // a streamed class stages chunks of fuse_ss's size in the fused launch
+    const int lds = C.one ? C.lds : stage_bytes(C.bits, H.M, 1 << 20, fuse_ss(C.bits, H.M, fuse_stream_chunk(C.bits)));
+    if (lds > fuse_lds[wi]) fuse_lds[wi] = lds;
   }
   for (int wi = 0; wi < 3; ++wi) {
     FuseArgs &F = fuse[wi];
@@ -646,11 +660,11 @@ hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hip
         for (int b = a; b > 0; --b) {
           const GroupClass &P = H.cls[F.cls[b - 1]], &Q = H.cls[F.cls[b]];
           if (P.bytes * Q.tiles >= Q.bytes * P.tiles) break;
-          const int tc = F.cls[b], tg = F.cfg[b];
+          const int tc = F.cls[b], to = F.one[b];
           F.cls[b] = F.cls[b - 1];
-          F.cfg[b] = F.cfg[b - 1];
+          F.one[b] = F.one[b - 1];
           F.cls[b - 1] = tc;
-          F.cfg[b - 1] = tg;
+          F.one[b - 1] = to;
         }
       int64_t grid = 0;
       for (int j = 0; j < F.n; ++j) {
