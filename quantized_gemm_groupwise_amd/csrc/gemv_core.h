@@ -108,6 +108,11 @@ __device__ __forceinline__ void swap16(float &a, float &b) {
 // (each lane keeps half of the values and adds its partner's copy of that
 // half), then a butterfly on the last value.  Afterwards lane l holds the
 // total of value index  sum_b bit(l, 5-b) * V/2^(b+1)  (b = 0..log2 V - 1).
+// Every V adds the same lanes in the same tree -- partners at lane offsets
+// 32, 16 and 8, then the mirror inside 8 lanes (l and 7 - l, which differ in
+// bit 2), then offsets 2 and 1 -- so a value's total is the same bits
+// whatever else is reduced with it (the decode kernels' outputs do not
+// depend on rows per wave or M).
 template <int V>
 __device__ __forceinline__ float wave_reduce_multi(const float (&v)[V], int lane) {
   constexpr int LOGV = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : 4;
@@ -138,7 +143,9 @@ __device__ __forceinline__ float wave_reduce_multi(const float (&v)[V], int lane
     for (int i = 0; i < n; ++i) {
       const float keep = upper ? cur[i + n] : cur[i];
       const float send = upper ? cur[i] : cur[i + n];
-      cur[i] = keep + (off == 8 ? dpp<0x128>(send) : __shfl_xor(send, off));
+      // offset 8: row_ror:8 (lane l + 8 within a row of 16); the level of
+      // bit 2: row_half_mirror (lane 7 - l within 8), the butterfly's partner
+      cur[i] = keep + (off == 8 ? dpp<0x128>(send) : dpp<0x141>(send));
     }
   }
   // butterfly over the remaining G = 64/V lanes (every lane of the group

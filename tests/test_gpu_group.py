@@ -104,6 +104,27 @@ def test_group_fused_launch_all_widths(M, dtype):
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"item {i} {SPECS_ALL_WIDTHS[i]}"
 
 
+@pytest.mark.parametrize("M", [3, 4])
+def test_group_int2_full_size_m3_m4_equals_gq_linear(M):
+    """INT2 rows run four per wave in the grouped kernels and at most two in
+    gq_linear, so at M = 3 and 4 a wave reduces 16 values against 8.  A
+    value's total must come out the same bits either way: the wave reduction
+    adds the same lanes in the same tree for every number of values.  A
+    different tree changes a bf16 output only near a rounding boundary, so
+    this runs on full-size layers (up/gate and down, 18432 rows)."""
+    _say("INT2 full size, grouped vs gq_linear, M =", M)
+    specs = [(14336, 4096, [2], None), (4096, 14336, [2], None)]
+    items = _make(specs, M, 9100 + M)
+    plan = gq.group_plan([(x, p, y) for (x, p, y, _, _) in items])
+    gq.linear_group(plan)
+    torch.cuda.synchronize()
+    for i, (x, p, y, W, xb) in enumerate(items):
+        ref = gq.linear(x, p)
+        torch.cuda.synchronize()
+        d = int((y.view(torch.int16) != ref.view(torch.int16)).sum().item())
+        assert d == 0, f"{specs[i]}: {d} outputs differ from gq_linear"
+
+
 def test_group_fp16_activations():
     items = _make(SPECS[:4], 2, 8300, dtype=torch.float16)
     plan = gq.group_plan([(x, p, y) for (x, p, y, _, _) in items])
