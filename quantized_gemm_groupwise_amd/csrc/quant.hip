@@ -73,12 +73,10 @@ __device__ __forceinline__ void quant_segment(const float (&v)[8], bool active, 
     lo = mn(lo, dppf<0x140>(lo));           // row_mirror
     hi = mx(hi, dppf<0x140>(hi));
   }
-  // NaN or Inf anywhere in the group (min and max skip NaN)
-  bool nf = false;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) nf |= !__builtin_isfinite(v[i]);
-  const uint64_t nfm = __ballot(nf);
-  const bool finite = ((nfm >> (lane & ~(LPG - 1))) & ((1ull << LPG) - 1)) == 0;
+  // NaN or Inf anywhere in the group: minimum / maximum propagate NaN, and
+  // an infinity is an extreme, so the group is finite exactly when its
+  // reduced lo and hi are
+  const bool finite = __builtin_isfinite(lo) && __builtin_isfinite(hi);
   const float qm = (float)((1 << BITS) - 1);
   const float s32 = (hi - lo) / qm;          // correctly rounded fp32 divide
   _Float16 s16 = (_Float16)s32;              // nearest even
@@ -168,11 +166,14 @@ __device__ __forceinline__ void quant_segment(const float (&v)[8], bool active, 
   }
 }
 
-// A wave walks a contiguous range of the layout's 512-weight segments (row
-// by row, segment by segment), loading the next segment before it works on
-// the current one, so every wave keeps two segments' reads in flight.  The
-// grid holds as many waves as the chip keeps resident, so the loads of the
-// whole launch overlap with the arithmetic of the waves.
+// The layout's 512-weight segments, numbered row by row, are dealt to the
+// grid's waves in turn: wave g takes segments g, g + W, g + 2W, ... (W the
+// waves of the grid), so at any moment the waves read neighbouring segments
+// of the matrix.  A wave loads the next two of its segments before it works
+// on the current one, so it keeps three segments' reads in flight.  The
+// grid holds as many waves as the chip keeps resident.  Positions advance by
+// W segments with adds only (row, segment of the row, block, row in the
+// block), no division per segment.
 template <int MODE>
 __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
     LayoutDev L, const float *__restrict__ w, uint8_t *__restrict__ codes,
@@ -180,19 +181,25 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
     uint32_t *flags, int segs_per_row) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
   const int lane = threadIdx.x & (kLanes - 1);
-  const int64_t nw = (int64_t)gridDim.x * kWaves;
-  const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
-  const int64_t total = (int64_t)L.N * segs_per_row;
-  const int64_t u0 = total * gw / nw, u1 = total * (gw + 1) / nw;
-  if (u0 >= u1) return;
-  int n = (int)(u0 / segs_per_row);
-  int seg = (int)(u0 - (int64_t)n * segs_per_row);
+  const int nw = (int)gridDim.x * kWaves;
+  const int gw = (int)blockIdx.x * kWaves + wave;
+  const int spr = segs_per_row;
+  if ((int64_t)gw >= (int64_t)L.N * spr) return;
   const int K = L.K;
-  // loads of segment (n, seg): lanes past the row end load nothing
-  auto load = [&](int nn, int sg, float (&v)[8]) {
+  const int dq = nw / spr, dr = nw - dq * spr;   // a step of nw segments: dq rows and dr segments
+  auto advance = [&](int &n, int &sg) {
+    n += dq;
+    sg += dr;
+    if (sg >= spr) {
+      sg -= spr;
+      ++n;
+    }
+  };
+  // loads of segment (n, sg); past the last row or the row end: nothing
+  auto load = [&](int n, int sg, float (&v)[8]) {
     const int kl = sg * kSeg + lane * 8;
-    if (kl < K) {
-      const float *src = w + (int64_t)nn * K + kl;
+    if (n < L.N && kl < K) {
+      const float *src = w + (int64_t)n * K + kl;
       const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
       const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + 4));
       v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
@@ -202,27 +209,21 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
       for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
   };
-  // two segments in flight ahead of the one being quantized
-  auto advance = [&](int &nn, int &sg) {
-    if (++sg == segs_per_row) { sg = 0; ++nn; }
-  };
+  int n = gw / spr, seg = gw - (gw / spr) * spr;  // current segment
+  int ln = n, ls = seg;                           // the segment loaded next
   float cur[8], nx1[8];
-  load(n, seg, cur);
-  int n1 = n, s1 = seg;
-  advance(n1, s1);
-  if (u0 + 1 < u1) load(n1, s1, nx1);
-  // the row's block, advanced row by row (the block changes every block_n
-  // rows; its offsets grow by the previous block's size)
+  load(ln, ls, cur);
+  advance(ln, ls);
+  load(ln, ls, nx1);
+  advance(ln, ls);
+  // the current row's block, and the row within it
   int blk = n / L.block_n;
   int r = n - blk * L.block_n;
   BlockInfo bi = block_info(L, blk);
-  for (int64_t u = u0; u < u1; ++u) {
-    // the segment after the next, loaded before this one is quantized
-    int n2 = n1, s2 = s1;
-    advance(n2, s2);
+  while (n < L.N) {
     float nx2[8];
-    if (u + 2 < u1) load(n2, s2, nx2);
-    const int nn = n1;
+    load(ln, ls, nx2);
+    advance(ln, ls);
     const int kl = seg * kSeg + lane * 8;
     const bool active = kl < K;
     void *orow = nullptr;
@@ -248,19 +249,18 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
       cur[i] = nx1[i];
       nx1[i] = nx2[i];
     }
-    if (nn != n && ++r == L.block_n) {
-      // next block: its codes and groups follow this block's
-      const uint64_t bk = (uint64_t)L.block_n * (uint64_t)K;
-      bi.code_off += bk * (uint64_t)bi.bits / 8u;
-      bi.grp_off += bk / (uint64_t)group_size(bi.bits);
-      ++blk;
-      r = 0;
-      if (blk < L.nblocks) bi.bits = block_bits(L, blk);
+    const int n0 = n;
+    advance(n, seg);
+    r += n - n0;
+    if (r >= L.block_n && n < L.N) {
+      // blocks passed, counted without a division; the new block's offsets
+      // from its position in the bit map (one set of independent loads)
+      do {
+        r -= L.block_n;
+        ++blk;
+      } while (r >= L.block_n);
+      bi = block_info(L, blk);
     }
-    n = n1;
-    seg = s1;
-    n1 = n2;
-    s1 = s2;
   }
 }
 
