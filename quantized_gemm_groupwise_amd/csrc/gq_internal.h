@@ -40,16 +40,20 @@ __host__ __device__ inline int block_bits(const LayoutDev &L, int blk) {
   return (L.int8_mask[blk >> 5] & bit) ? 8 : (L.int4_mask[blk >> 5] & bit) ? 4 : 2;
 }
 
-__host__ __device__ inline BlockInfo block_info(const LayoutDev &L, int blk) {
-  int c4 = 0, c8 = 0;  // INT4 and 8-bit blocks before blk
-  const int w = blk >> 5;
-  for (int i = 0; i < w; ++i) {
-    c4 += __builtin_popcount(L.int4_mask[i]);
-    c8 += __builtin_popcount(L.int8_mask[i]);
+// INT4 and 8-bit blocks among blocks [a, b) of the map, added to c4 and c8.
+__host__ __device__ inline void count_blocks(const LayoutDev &L, int a, int b, int &c4, int &c8) {
+  for (int w = a >> 5; a < b && w <= ((b - 1) >> 5); ++w) {
+    uint32_t m = ~0u;
+    if (w == (a >> 5)) m &= ~0u << (a & 31);
+    if (w == ((b - 1) >> 5)) m &= ~0u >> (31 - ((b - 1) & 31));
+    c4 += __builtin_popcount(L.int4_mask[w] & m);
+    c8 += __builtin_popcount(L.int8_mask[w] & m);
   }
-  const uint32_t below = (1u << (blk & 31)) - 1u;
-  c4 += __builtin_popcount(L.int4_mask[w] & below);
-  c8 += __builtin_popcount(L.int8_mask[w] & below);
+}
+
+// Block blk's width and offsets, given the INT4 (c4) and 8-bit (c8) blocks
+// before it.
+__host__ __device__ inline BlockInfo block_info_counted(const LayoutDev &L, int blk, int c4, int c8) {
   BlockInfo b;
   b.bits = block_bits(L, blk);
   const uint64_t bk = (uint64_t)L.block_n * (uint64_t)L.K;
@@ -58,6 +62,12 @@ __host__ __device__ inline BlockInfo block_info(const LayoutDev &L, int blk) {
   b.code_off = bk * (uint64_t)(blk + c4 + 3 * c8) / 4u;
   b.grp_off = bk * (uint64_t)(2 * blk - c4 - c8) / 128u;
   return b;
+}
+
+__host__ __device__ inline BlockInfo block_info(const LayoutDev &L, int blk) {
+  int c4 = 0, c8 = 0;  // INT4 and 8-bit blocks before blk
+  count_blocks(L, 0, blk, c4, c8);
+  return block_info_counted(L, blk, c4, c8);
 }
 
 // Host-side helpers (layout.cpp).

@@ -219,7 +219,9 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
   // the current row's block, and the row within it
   int blk = n / L.block_n;
   int r = n - blk * L.block_n;
-  BlockInfo bi = block_info(L, blk);
+  int c4 = 0, c8 = 0;                              // INT4 and 8-bit blocks before blk
+  count_blocks(L, 0, blk, c4, c8);
+  BlockInfo bi = block_info_counted(L, blk, c4, c8);
   while (n < L.N) {
     float nx2[8];
     load(ln, ls, nx2);
@@ -253,13 +255,15 @@ __global__ __launch_bounds__(kWaves * kLanes) void quantize_pack_kernel(
     advance(n, seg);
     r += n - n0;
     if (r >= L.block_n && n < L.N) {
-      // blocks passed, counted without a division; the new block's offsets
-      // from its position in the bit map (one set of independent loads)
+      // blocks passed, counted without a division; the running counts of
+      // INT4 and 8-bit blocks take the passed blocks' bits of the map
+      const int blk0 = blk;
       do {
         r -= L.block_n;
         ++blk;
       } while (r >= L.block_n);
-      bi = block_info(L, blk);
+      count_blocks(L, blk0, blk, c4, c8);
+      bi = block_info_counted(L, blk, c4, c8);
     }
   }
 }
