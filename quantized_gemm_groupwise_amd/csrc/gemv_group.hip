@@ -76,8 +76,8 @@ __device__ __forceinline__ void seg_rows(const GroupSeg &S, int rw, int K, RowRs
 template <int ACT, int M, int BITS, int SS, int NL, bool ONE, bool PIPE>
 __device__ __forceinline__ void group_body(const uint8_t *__restrict__ plan, int cls, int chunk,
                                            const int G, const int w, uint32_t *lds) {
-  constexpr int R = group_r(BITS);
-  constexpr int kTile = group_tile(BITS);
+  constexpr int R = group_r(BITS, M);
+  constexpr int kTile = group_tile(BITS, M);
   using Gm = Geo<BITS>;
   if constexpr (chunk_slices(BITS, M, SS) < 1) {
     return;                                 // never launched: SS too small for M
@@ -560,7 +560,7 @@ gq_status gemv_group_plan(int count, const gq_group_item *items, int M, gq_dtype
         if (block_info(L, b).bits != C.bits) { ++b; continue; }
         int e = b;
         while (e < L.nblocks && block_info(L, e).bits == C.bits) ++e;
-        const int tile = group_tile(C.bits);
+        const int tile = group_tile(C.bits, M);
         const int t0 = b * L.block_n / tile;
         const int t1 = e == L.nblocks ? (L.N + tile - 1) / tile : e * L.block_n / tile;
         const BlockInfo bi = block_info(L, b);

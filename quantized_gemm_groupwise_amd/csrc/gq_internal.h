@@ -96,7 +96,7 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 // caller keeps a byte copy in device memory, which the kernels read; the
 // host copy gives the launch configuration.
 //
-// Work is cut into row tiles of 4 * group_r(bits) output channels (the
+// Work is cut into row tiles of 4 * group_r(bits, M) output channels (the
 // GEMV's workgroup tile).  The tiles of one bit-width and kernel configuration form
 // a class, launched once.  A class is a list of segments, runs of
 // consecutive tiles of one linear over which the row stride is uniform (a
@@ -112,12 +112,17 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 constexpr uint32_t kGroupMagic = 0x50475147u;   // "GQGP"
 constexpr uint32_t kGroupVersion = 3;
 constexpr int kGroupMaxClasses = 27;                // 3 widths x 3 staging x 3 load-group configs
-// rows per wave: 4 for INT2 rows (a row of K = 4096 is 1 KB, and four per
-// wave amortize the per-tile reduction and bookkeeping), 2 for INT4 and 8-bit
-// rows (twice and four times the bytes per row, and more registers per row)
-__host__ __device__ constexpr int group_r(int bits) { return bits == 2 ? 4 : 2; }
+// rows per wave: 4 for INT2 rows at M <= 2 (a row of K = 4096 is 1 KB, and
+// four per wave amortize the per-tile reduction and bookkeeping), else 2:
+// INT4 and 8-bit rows carry two and four times the bytes and registers per
+// row, and at M = 3-4 the accumulators of four INT2 rows leave too few
+// waves (the 224-linear Layer-mix pass: 0.78 -> 0.75 ms at M = 3, 1.01 ->
+// 0.94 ms at M = 4 with two rows; at M = 2 two rows were slower, 0.54 ->
+// 0.59 ms).  Outputs do not depend on it: the wave reduction adds each value
+// in one tree.
+__host__ __device__ constexpr int group_r(int bits, int M) { return bits == 2 && M <= 2 ? 4 : 2; }
 constexpr int kGroupNL = 2;                      // 1 KB slices per load group
-__host__ __device__ constexpr int group_tile(int bits) { return 4 * group_r(bits); }   // rows per tile
+__host__ __device__ constexpr int group_tile(int bits, int M) { return 4 * group_r(bits, M); }   // rows per tile
 constexpr int kGroupChunk = 4;                   // tiles per chunk of a persistent streamed launch
 constexpr int kGroupPersistTiles = 4;            // tiles per resident workgroup to persist
 
