@@ -335,12 +335,19 @@ struct FuseArgs {
 __host__ __device__ constexpr int fuse_ss(int bits, int M, int slices) {
   return chunk_slices(bits, M, 1) >= slices ? 1 : chunk_slices(bits, M, 2) >= slices ? 2 : kStageSubMax;
 }
-// Slices per staged chunk of a streamed row in the fused launch.  Measured
-// on the Llama-3-8B decode step (M = 1): INT4 down rows (7 slices) run
-// fastest in chunks of 2 (one staging sub-unit, the fewest registers, so the
-// most resident workgroups for the launch's other classes), INT2 down rows
-// (4 slices) in one chunk of 4 (no restaging).
-__host__ __device__ constexpr int fuse_stream_chunk(int bits) { return bits == 2 ? 4 : 2; }
+// Slices per staged chunk of a streamed row in the fused launch, and slices
+// per load group of its body.  The fused kernel holds the registers of its
+// largest body, and the streamed body is the largest, so these choices set
+// the resident waves of the whole launch.  Measured on the Llama-3-8B decode
+// step (M = 1): INT4 down rows (7 slices) run fastest in chunks of 2 with
+// one staging sub-unit; INT2 down rows (4 slices) in chunks of 1 (one
+// sub-unit: 77 registers, 6 waves per SIMD, against 140 and 3 waves for one
+// chunk of 4, which saves the restaging but starves the rest of the launch:
+// INT2 step 12.6 -> 11.1 us).  Loads of one slice per group (a wave streams
+// its rows slice by slice) hold the fewest registers again (INT4 step
+// 15.5 -> 15.3 us).
+__host__ __device__ constexpr int fuse_stream_chunk(int bits) { return bits == 2 ? 1 : 2; }
+constexpr int kFuseStreamNL = 1;
 
 // Every one-workgroup-per-tile class of one width in one launch.  Between
 // two launches on a stream the first one's last workgroups finish before
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void gemv_group_fused_kernel(const uint8_
   else if (one == 2)
     group_body<ACT, M, BITS, fuse_ss(BITS, M, 2), 2, true, false>(plan, cls, 1, G, w, lds);
   else
-    group_body<ACT, M, BITS, fuse_ss(BITS, M, fuse_stream_chunk(BITS)), kGroupNL, false, false>(plan, cls, 1, G, w, lds);
+    group_body<ACT, M, BITS, fuse_ss(BITS, M, fuse_stream_chunk(BITS)), kFuseStreamNL, false, false>(plan, cls, 1, G, w, lds);
 }
 
 typedef void (*GroupKernel)(const uint8_t *, int, int);
