@@ -357,8 +357,11 @@ constexpr int kFuseStreamNL = 1;
 // first, so the workgroups dispatched last are the shortest.  Each
 // workgroup runs the body of its class's load-group configuration (a branch
 // uniform over the workgroup), with the staging of fuse_ss; the LDS is the
-// largest class's.
-template <int ACT, int M, int BITS>
+// largest class's.  BODIES is the set of load-group configurations the
+// launch's classes use (bit 0: rows of one slice, bit 1: rows of two
+// slices, bit 2: streamed rows): a kernel holds the registers of the largest
+// body it contains, so it contains only those.
+template <int ACT, int M, int BITS, int BODIES>
 __global__ __launch_bounds__(kThreads) void gemv_group_fused_kernel(const uint8_t *__restrict__ plan,
                                                                     FuseArgs fa) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
@@ -373,12 +376,19 @@ __global__ __launch_bounds__(kThreads) void gemv_group_fused_kernel(const uint8_
       s1 = fa.start[j + 1];
     }
   const int G = s1 - s0, w = b - s0;
-  if (one == 1)
-    group_body<ACT, M, BITS, fuse_ss(BITS, M, 1), 1, true, false>(plan, cls, 1, G, w, lds);
-  else if (one == 2)
-    group_body<ACT, M, BITS, fuse_ss(BITS, M, 2), 2, true, false>(plan, cls, 1, G, w, lds);
-  else
-    group_body<ACT, M, BITS, fuse_ss(BITS, M, fuse_stream_chunk(BITS)), kFuseStreamNL, false, false>(plan, cls, 1, G, w, lds);
+  if constexpr ((BODIES & 1) != 0)
+    if (one == 1) {
+      group_body<ACT, M, BITS, fuse_ss(BITS, M, 1), 1, true, false>(plan, cls, 1, G, w, lds);
+      return;
+    }
+  if constexpr ((BODIES & 2) != 0)
+    if (one == 2) {
+      group_body<ACT, M, BITS, fuse_ss(BITS, M, 2), 2, true, false>(plan, cls, 1, G, w, lds);
+      return;
+    }
+  if constexpr ((BODIES & 4) != 0)
+    if (one == 0)
+      group_body<ACT, M, BITS, fuse_ss(BITS, M, fuse_stream_chunk(BITS)), kFuseStreamNL, false, false>(plan, cls, 1, G, w, lds);
 }
 
 typedef void (*GroupKernel)(const uint8_t *, int, int);
@@ -420,19 +430,34 @@ GroupKernel group_kernel(int act, int M, int bits, int ss, int one, bool pipe) {
 
 typedef void (*FusedKernel)(const uint8_t *, FuseArgs);
 
-template <int ACT, int M>
-FusedKernel fused_kernel_m(int bits) {
-  if (bits == 8) return gemv_group_fused_kernel<ACT, M, 8>;
-  return bits == 4 ? gemv_group_fused_kernel<ACT, M, 4> : gemv_group_fused_kernel<ACT, M, 2>;
+template <int ACT, int M, int BITS>
+FusedKernel fused_kernel_b(int bodies) {
+  switch (bodies) {
+    case 1: return gemv_group_fused_kernel<ACT, M, BITS, 1>;
+    case 2: return gemv_group_fused_kernel<ACT, M, BITS, 2>;
+    case 3: return gemv_group_fused_kernel<ACT, M, BITS, 3>;
+    case 4: return gemv_group_fused_kernel<ACT, M, BITS, 4>;
+    case 5: return gemv_group_fused_kernel<ACT, M, BITS, 5>;
+    case 6: return gemv_group_fused_kernel<ACT, M, BITS, 6>;
+    default: return gemv_group_fused_kernel<ACT, M, BITS, 7>;
+  }
 }
 
-FusedKernel fused_kernel(int act, int M, int bits) {
+template <int ACT, int M>
+FusedKernel fused_kernel_m(int bits, int bodies) {
+  if (bits == 8) return fused_kernel_b<ACT, M, 8>(bodies);
+  return bits == 4 ? fused_kernel_b<ACT, M, 4>(bodies) : fused_kernel_b<ACT, M, 2>(bodies);
+}
+
+// bodies: the set of load-group configurations of the launch's classes
+// (bit 0: one slice, bit 1: two slices, bit 2: streamed)
+FusedKernel fused_kernel(int act, int M, int bits, int bodies) {
   const bool bf = act == GQ_BF16;
   switch (M) {
-    case 1: return bf ? fused_kernel_m<0, 1>(bits) : fused_kernel_m<1, 1>(bits);
-    case 2: return bf ? fused_kernel_m<0, 2>(bits) : fused_kernel_m<1, 2>(bits);
-    case 3: return bf ? fused_kernel_m<0, 3>(bits) : fused_kernel_m<1, 3>(bits);
-    default: return bf ? fused_kernel_m<0, 4>(bits) : fused_kernel_m<1, 4>(bits);
+    case 1: return bf ? fused_kernel_m<0, 1>(bits, bodies) : fused_kernel_m<1, 1>(bits, bodies);
+    case 2: return bf ? fused_kernel_m<0, 2>(bits, bodies) : fused_kernel_m<1, 2>(bits, bodies);
+    case 3: return bf ? fused_kernel_m<0, 3>(bits, bodies) : fused_kernel_m<1, 3>(bits, bodies);
+    default: return bf ? fused_kernel_m<0, 4>(bits, bodies) : fused_kernel_m<1, 4>(bits, bodies);
   }
 }
 
@@ -680,7 +705,9 @@ hipError_t launch_gemv_group(const GroupPlanHeader &H, const void *plan_dev, hip
       }
       if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
       F.start[F.n] = (int32_t)grid;
-      const FusedKernel k = fused_kernel(H.act, H.M, wi == 0 ? 4 : wi == 1 ? 2 : 8);
+      int bodies = 0;
+      for (int j = 0; j < F.n; ++j) bodies |= F.one[j] == 1 ? 1 : F.one[j] == 2 ? 2 : 4;
+      const FusedKernel k = fused_kernel(H.act, H.M, wi == 0 ? 4 : wi == 1 ? 2 : 8, bodies);
       hipLaunchKernelGGL(k, dim3((uint32_t)grid), dim3(kThreads), fuse_lds[wi], s, p, F);
     }
     const hipError_t e = hipGetLastError();
