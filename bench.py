@@ -76,6 +76,12 @@ def decode_bytes(N, K, bits, M):
     return N * K * bits // 8 + (N * K // g) * 3 + 2 * M * K + 2 * M * N
 
 
+def decode_step_bytes(bits, M=1):
+    """Algorithmic bytes of the four-linear Llama-3-8B decode step."""
+    import synth as S
+    return sum(decode_bytes(N, K, bits, M) for (N, K) in S.LLAMA3_8B_SHAPE_LIST)
+
+
 # ----------------------------------------------------------------- timing
 
 class GraphTimer:
@@ -228,6 +234,41 @@ def ceilings(torch):
                                                  "frac_hbm": round(2 * nbytes * n / tc / 1e9 / HBM_PEAK_GBS, 3),
                                                  "us_per_call": round(tc / n * 1e6, 2)}
         del bufs, dsts
+        torch.cuda.empty_cache()
+    return out
+
+
+def read_ceiling(torch):
+    """The plain streaming-read probe (libgq_probe.so: 128-bit nontemporal
+    loads, one launch, no arithmetic) at the byte counts of the INT4 and INT2
+    decode steps and at 1 GB: what one launch moving the same bytes gets
+    from this GPU, ramp and drain included.  Buffers rotate past the
+    Infinity Cache like the decode step's weight copies."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantized_gemm_groupwise_amd", "libgq_probe.so"))
+    fn = lib.gqprobe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = {}
+    for label, nbytes, count in (("int4_decode_step_bytes", decode_step_bytes(4), 16),
+                                 ("int2_decode_step_bytes", decode_step_bytes(2), 16),
+                                 ("1GB", 1 << 30, 2)):
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(count)]
+
+        def one():
+            for b in bufs:
+                st = fn(b.data_ptr(), nbytes, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"gqprobe_stream_read: {st}")
+        gt = GraphTimer(torch, one)
+        gt.warm()
+        reps = 50 if count > 2 else 20
+        t, _ = gt.run(reps)
+        n = reps * count
+        out[label] = {"bytes": nbytes, "us": round(t / n * 1e6, 2), "GBps": round(nbytes * n / t / 1e9, 1),
+                      "frac_hbm": round(nbytes * n / t / 1e9 / HBM_PEAK_GBS, 3)}
+        del bufs
         torch.cuda.empty_cache()
     return out
 
@@ -413,6 +454,7 @@ def secondary(torch, gq, S, args):
     del packs
     torch.cuda.empty_cache()
     out["streaming_ceilings"] = ceilings(torch)
+    out["read_ceiling"] = read_ceiling(torch)
 
     out.update(channel_mix(torch, gq, S))
     out.update(kv_decode(torch, gq))

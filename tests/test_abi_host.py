@@ -283,3 +283,21 @@ def test_product_path_refuses_missing_library(tmp_path):
             mod.load_library(str(tmp_path / "nope.so"))
     finally:
         mod._lib = saved
+
+
+def test_stream_probe_library_refuses_bad_arguments():
+    """The benchmark's streaming-read probe (its own library) loads and
+    refuses a null buffer or sink, a zero or unaligned size and an unaligned
+    address before any launch."""
+    import torch  # noqa: F401  -- torch's HIP runtime first, as for libgq
+    path = os.path.join(ROOT, "quantized_gemm_groupwise_amd", "libgq_probe.so")
+    probe = ctypes.CDLL(path)
+    fn = probe.gqprobe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    buf, sink = 0x7F0000000000, 0x7F0000100000
+    assert fn(None, 1024, sink, None) == -1
+    assert fn(buf, 1024, None, None) == -1
+    assert fn(buf, 0, sink, None) == -1
+    assert fn(buf, 1000, sink, None) == -1
+    assert fn(buf + 8, 1024, sink, None) == -1
