@@ -97,10 +97,18 @@ hipError_t launch_rows(const LayoutDev &L, int bitsel, const void *x, const uint
   return hipGetLastError();
 }
 
+// rows per wave: rsel 1 or 2; 4 for layouts with INT2 blocks at M >= 3,
+// whose INT2 rows run on the matrix cores four rows per wave
 template <int ACT, int M, int SS>
-hipError_t launch_r(const LayoutDev &L, int bitsel, bool two, int ns, const void *x,
+hipError_t launch_r(const LayoutDev &L, int bitsel, int rsel, int ns, const void *x,
                     const uint32_t *codes, const uint16_t *scales, const uint8_t *zeros, void *y,
                     hipStream_t s) {
+  if constexpr (M >= 3) {
+    if (rsel == 4)
+      return ns <= 1 ? launch_rows<ACT, M, 4, 1, SS>(L, bitsel, x, codes, scales, zeros, y, s)
+                     : launch_rows<ACT, M, 4, 2, SS>(L, bitsel, x, codes, scales, zeros, y, s);
+  }
+  const bool two = rsel == 2;
   if (ns <= 1)
     return two ? launch_rows<ACT, M, 2, 1, SS>(L, bitsel, x, codes, scales, zeros, y, s)
                : launch_rows<ACT, M, 1, 1, SS>(L, bitsel, x, codes, scales, zeros, y, s);
@@ -120,12 +128,14 @@ hipError_t launch_m(const LayoutDev &L, const void *x, const uint32_t *codes,
   const int n2 = L.nblocks - n4 - n8;
   const int bitsel = n4 == L.nblocks ? 4 : n2 == L.nblocks ? 2 : n8 == L.nblocks ? 8 : (n8 ? 1 : 0);
   // Load groups of two 1 KB slices (one for rows of a single slice), issued
-  // one group ahead; two rows per wave once N gives >= 2048 waves.  Measured
+  // one group ahead; two rows per wave once N gives >= 2048 waves (four for
+  // layouts with INT2 blocks at M >= 3: the matrix-core path).  Measured
   // on MI355X over the Llama-3-8B decode shapes: issuing a whole long row at
   // once, or more rows per wave, leaves fewer waves to cover HBM latency.
   const int widest = n8 ? 8 : (n4 ? 4 : 2);
   const int ns = (L.K * widest / 8 + 1023) / 1024;
   const bool two = L.N >= 4096;
+  const int rsel = (M >= 3 && n2 > 0) ? 4 : two ? 2 : 1;
   // staging sub-units per thread that hold a whole row of x (an INT2 slice
   // carries twice the activations of an INT4 one, an 8-bit slice half)
   const int ns4 = (L.K * 4 / 8 + 1023) / 1024, ns2 = (L.K * 2 / 8 + 1023) / 1024;
@@ -134,9 +144,9 @@ hipError_t launch_m(const LayoutDev &L, const void *x, const uint32_t *codes,
   const int u8 = n8 ? M * kLanes * ns8 : 0;
   const int um = u4 > u2 ? (u4 > u8 ? u4 : u8) : (u2 > u8 ? u2 : u8);
   const int need = (um + kThreads - 1) / kThreads;
-  if (need <= 1) return launch_r<ACT, M, 1>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
-  if (need <= 2) return launch_r<ACT, M, 2>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
-  return launch_r<ACT, M, kStageSubMax>(L, bitsel, two, ns, x, codes, scales, zeros, y, s);
+  if (need <= 1) return launch_r<ACT, M, 1>(L, bitsel, rsel, ns, x, codes, scales, zeros, y, s);
+  if (need <= 2) return launch_r<ACT, M, 2>(L, bitsel, rsel, ns, x, codes, scales, zeros, y, s);
+  return launch_r<ACT, M, kStageSubMax>(L, bitsel, rsel, ns, x, codes, scales, zeros, y, s);
 }
 
 template <int ACT>

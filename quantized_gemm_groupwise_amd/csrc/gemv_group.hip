@@ -13,9 +13,13 @@ namespace {
 
 // The wave's R * M sums reduced across lanes; one lane per output stores
 // y[m][n0 + r] (row stride N) for n0 + r < nlim.
-template <int ACT, int M, int R>
+template <int ACT, int M, int R, int BITS>
 __device__ __forceinline__ void reduce_store(const float (&acc)[R][M], int lane, int n0, int nlim,
                                              int N, uint16_t *y) {
+  if constexpr (mfma_decode(BITS, M, R)) {
+    mfma_reduce_store<ACT, M>(acc[0], lane, n0, nlim, N, y);
+    return;
+  }
   constexpr int V0 = R * M;
   constexpr int V = V0 <= 1 ? 1 : V0 <= 2 ? 2 : V0 <= 4 ? 4 : V0 <= 8 ? 8 : 16;
   float vals[V];
@@ -163,18 +167,13 @@ __device__ __forceinline__ void group_body(const uint8_t *__restrict__ plan, int
     auto issue_cursor = [&](LoadGroup<BITS, R, NL> &gl, bool none) {
       RowRsrc<R> rr;
       if (!none) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const bool live = lrows > r;
-          rr.c[r] = make_rsrc(pc + r * RB, live ? RB : 0u);
-          rr.s[r] = make_rsrc(ps + r * GPR, live ? 2u * GPR : 0u);
-          rr.z[r] = make_rsrc(pz + r * GPR, live ? GPR : 0u);
-        }
+        make_row_rsrc<BITS, M, R>(rr, pc, ps, pz, RB, GPR, lrows);
       } else {
+        rr.rb = rr.gpr = 0u;
 #pragma unroll
         for (int r = 0; r < R; ++r) rr.c[r] = rr.s[r] = rr.z[r] = make_rsrc(plan, 0u);
       }
-      issue_group<BITS, R, NL, false>(gl, 0, NL, lane, rr);
+      issue_group<BITS, R, NL, false, mfma_decode(BITS, M, R)>(gl, 0, NL, lane, rr);
     };
     open_seg(ls, lt);
     if (lcb >= hi) return;
@@ -218,7 +217,7 @@ __device__ __forceinline__ void group_body(const uint8_t *__restrict__ plan, int
         for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
       compute_group<BITS, ACT, M, R, NL>(g, 0, ns, 0, lane, pairs, sm, ns, acc);
       // rows past the run (a partial last tile) are past N: not stored
-      reduce_store<ACT, M, R>(acc, lane, sn0, snlim, yN, const_cast<uint16_t *>(yp));
+      reduce_store<ACT, M, R, BITS>(acc, lane, sn0, snlim, yN, const_cast<uint16_t *>(yp));
       if (!more) return false;
       if (!same) {
         // the next tile is in another linear: restage x, then its loads

@@ -112,15 +112,12 @@ hipError_t launch_gemm(const LayoutDev &L, int M, gq_dtype act, const void *x,
 constexpr uint32_t kGroupMagic = 0x50475147u;   // "GQGP"
 constexpr uint32_t kGroupVersion = 3;
 constexpr int kGroupMaxClasses = 27;                // 3 widths x 3 staging x 3 load-group configs
-// rows per wave: 4 for INT2 rows at M <= 2 (a row of K = 4096 is 1 KB, and
-// four per wave amortize the per-tile reduction and bookkeeping), else 2:
-// INT4 and 8-bit rows carry two and four times the bytes and registers per
-// row, and at M = 3-4 the accumulators of four INT2 rows leave too few
-// waves (the 224-linear Layer-mix pass: 0.78 -> 0.75 ms at M = 3, 1.01 ->
-// 0.94 ms at M = 4 with two rows; at M = 2 two rows were slower, 0.54 ->
-// 0.59 ms).  Outputs do not depend on it: the wave reduction adds each value
-// in one tree.
-__host__ __device__ constexpr int group_r(int bits, int M) { return bits == 2 && M <= 2 ? 4 : 2; }
+// rows per wave: 4 for INT2 rows (a row of K = 4096 is 1 KB, and four per
+// wave amortize the per-tile reduction and bookkeeping; at M = 3-4 the
+// wave's four rows share the matrix-core products of the decode kernel),
+// else 2: INT4 and 8-bit rows carry two and four times the bytes and
+// registers per row.
+__host__ __device__ constexpr int group_r(int bits, int M) { return bits == 2 ? 4 : 2; }
 constexpr int kGroupNL = 2;                      // 1 KB slices per load group
 __host__ __device__ constexpr int group_tile(int bits, int M) { return 4 * group_r(bits, M); }   // rows per tile
 constexpr int kGroupChunk = 4;                   // tiles per chunk of a persistent streamed launch

@@ -64,6 +64,7 @@ CASES = [
     # (M, N, K, block_n, bits): dot-product, small batch, GEMM, 256 x 256 GEMM
     (1, 192, 512, 192, [2]),
     (3, 256, 1024, 128, [2, 4]),
+    (4, 200, 1536, 200, [2]),                # matrix-core decode path, ragged rows, 1.5 slices
     (8, 192, 512, 192, [2]),
     (24, 384, 2048, 128, [2, 4, 2]),
     (32, 128, 28672, 128, [2]),              # long k range: small-batch K split
@@ -162,7 +163,7 @@ def _gate(got_bits, ref, a_bits, wabs):
 
 
 @pytest.mark.parametrize("kind", ["huge", "tiny", "span"])
-@pytest.mark.parametrize("M", [1, 8, 64, 300])
+@pytest.mark.parametrize("M", [1, 4, 8, 64, 300])
 def test_linear_activation_range(kind, M):
     """The GEMM rescales each bf16 row by a power of two into fp16; the other
     paths use bf16 as given.  Rows at 2^60, at 2^-60 and spanning 2^40."""

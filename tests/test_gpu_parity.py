@@ -286,11 +286,13 @@ def test_linear_exact_integer_case_large_tiles():
     assert np.array_equal(O.bf16_bits_to_f64(y_bits(y)), exact)
 
 
-@pytest.mark.parametrize("M", [2, 20, 70])
-def test_linear_fp16_activations(M):
+@pytest.mark.parametrize("M,bits", [(2, 4), (20, 4), (70, 4), (3, 2), (4, 2)])
+def test_linear_fp16_activations(M, bits):
+    """fp16 activations; INT2 at M = 3-4 is the matrix-core decode path
+    (its f16 4x4x4 products)."""
     N, K = 256, 512
     W = S.decode_weight(3, N=N, K=K)
-    ref = O.quantize_pack(W, O.Layout(K, N, N, [4]))
+    ref = O.quantize_pack(W, O.Layout(K, N, N, [bits]))
     p = upload_packed(ref)
     xf = np.random.default_rng(M).standard_normal((M, K)).astype(np.float16)
     # the oracle takes bf16 bit patterns; use fp16 values exact in fp64 instead
