@@ -180,6 +180,14 @@ __device__ __forceinline__ int reduced_index(int lane) {
   return idx;
 }
 
+// Slot of lane l's x pairs in the 64 slots (1 KB) of a staged row-slice
+// ms = m * nslice + slice: l XOR 4 * (ms mod 4).  A permutation, so the
+// dot-product path's reads (each lane its own slot) stay conflict-free; for
+// the matrix-core path, whose lanes 4b + j read row j of one slot in 16
+// lanes at a time, rows that differ in ms mod 4 land on different LDS banks
+// (without it the rows, 8 KB apart, hit the same banks).
+__device__ __forceinline__ int pair_slot(int l, int ms) { return l ^ ((ms & 3) << 2); }
+
 // Geometry of one bit-width.
 template <int BITS>
 struct Geo {
@@ -296,7 +304,7 @@ __device__ __forceinline__ void stage_x_store(const StageRegs<SS> &st, int nslic
       s1 = BIASF * fmaf(c16, 0.0625f, fmaf(c4, 0.25f, c1));
     }
     if (su < subs) {                            // LDS slot exists
-      uint4 *dst = pairs + (ms * (Gm::PW / 4) + 2 * part) * kLanes + lane;
+      uint4 *dst = pairs + (ms * (Gm::PW / 4) + 2 * part) * kLanes + pair_slot(lane, ms);
       dst[0] = make_uint4(p[0], p[1], p[2], p[3]);
       dst[kLanes] = make_uint4(p[4], p[5], p[6], p[7]);
       if (part == 0) {
@@ -473,7 +481,7 @@ __device__ __forceinline__ void compute_group_mfma(const LoadGroup<2, 4, NL> &g,
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = b + 16 * u;                // chunk (group) within the slice
-        const uint4 *xsrc = pairs + (msx * (Gm::PW / 4)) * kLanes + c;
+        const uint4 *xsrc = pairs + (msx * (Gm::PW / 4)) * kLanes + pair_slot(c, msx);
         mf_f32x4 d1 = zero4, d4 = zero4, d16 = zero4;
         uint32_t pq6 = 0, pq7 = 0, px6 = 0, px7 = 0;
 #pragma unroll
@@ -582,7 +590,7 @@ __device__ __forceinline__ void compute_group(const LoadGroup<BITS, R, NL> &g, i
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const int ms = m * chunk_nslice + lsl;
-        const uint4 *src = pairs + (ms * (Gm::PW / 4)) * kLanes + lane;
+        const uint4 *src = pairs + (ms * (Gm::PW / 4)) * kLanes + pair_slot(lane, ms);
         const uint4 a = src[(2 * c) * kLanes], b = src[(2 * c + 1) * kLanes];
         xc[m][0] = a.x; xc[m][1] = a.y; xc[m][2] = a.z; xc[m][3] = a.w;
         xc[m][4] = b.x; xc[m][5] = b.y; xc[m][6] = b.z; xc[m][7] = b.w;
