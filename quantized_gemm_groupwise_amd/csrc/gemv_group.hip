@@ -40,23 +40,6 @@ struct TilePos {
   int si, t, T, T0, T1;
 };
 
-// Row resources of a wave's R rows at run-relative row rw of segment S:
-// rows past the run's end get empty resources (they load zeros and are
-// never stored).
-template <int BITS, int R>
-__device__ __forceinline__ void seg_rows(const GroupSeg &S, int rw, int K, RowRsrc<R> &rr) {
-  using Gm = Geo<BITS>;
-  const uint32_t RB = (uint32_t)(K * BITS / 8), GPR = (uint32_t)(K / Gm::G);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool live = rw + r < S.rows;
-    const uint64_t row = live ? (uint64_t)(rw + r) : 0u;
-    rr.c[r] = make_rsrc(S.codes + row * RB, live ? RB : 0u);
-    rr.s[r] = make_rsrc(S.scales + row * GPR, live ? 2u * GPR : 0u);
-    rr.z[r] = make_rsrc(S.zeros + row * GPR, live ? GPR : 0u);
-  }
-}
-
 // Grouped decode: workgroup w of G of one class of a plan.  Every tile runs
 // the single-linear kernel's arithmetic and order, so the outputs are the
 // same bits as one gq_linear call per linear.  x of a linear is staged once per workgroup
