@@ -48,15 +48,27 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
   const uint16_t *row = x + (int64_t)m * K;
   __shared__ float red[4];
   int e = 0;
+  // each thread keeps kPrepLoads 16-byte loads in flight: one at a time
+  // left the pass waiting on memory latency (a 57 KB row is 14 loads per
+  // thread)
+  constexpr int kPrepLoads = 4;
   if (ACT == 0) {
     float amax = 0.f;
-    for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(row + c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int c0 = threadIdx.x * 8; c0 < K; c0 += kPrepLoads * 256 * 8) {
+      uint4 v[kPrepLoads];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
-        amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
+      for (int u = 0; u < kPrepLoads; ++u) {
+        const int c = c0 + u * 256 * 8;
+        v[u] = c < K ? *reinterpret_cast<const uint4 *>(row + c) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kPrepLoads; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+          amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
+        }
       }
     }
 #pragma unroll
@@ -71,12 +83,22 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
     }
   }
   if (threadIdx.x == 0) rexp[m] = e;
-  for (int c = threadIdx.x * 8; c < Kp; c += 256 * 8) {
+  for (int c0 = threadIdx.x * 8; c0 < Kp; c0 += kPrepLoads * 256 * 8) {
+    uint4 vin[kPrepLoads];
+#pragma unroll
+    for (int u = 0; u < kPrepLoads; ++u) {
+      const int c = c0 + u * 256 * 8;
+      vin[u] = c < K ? *reinterpret_cast<const uint4 *>(row + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepLoads; ++u) {
+    const int c = c0 + u * 256 * 8;
+    if (c >= Kp) break;
     if (c >= K) {
       *reinterpret_cast<uint4 *>(out + c) = make_uint4(0u, 0u, 0u, 0u);
       continue;
     }
-    const uint4 v = *reinterpret_cast<const uint4 *>(row + c);
+    const uint4 v = vin[u];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint16_t h[8];
 #pragma unroll
@@ -103,6 +125,7 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
       o.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
     }
     *reinterpret_cast<uint4 *>(out + c) = o;
+    }
   }
 }
 
