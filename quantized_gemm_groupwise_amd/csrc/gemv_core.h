@@ -335,10 +335,10 @@ struct RowRsrc {
 // issues 8 v_dot2 per 16 codes and activation row, the matrix-core path a
 // fixed 4 instructions per 16 codes for all rows together plus the group's
 // scale arithmetic per row.  Measured on MI355X (Llama-3-8B up/gate, one
-// launch; the 224-linear Layer-mix pass, grouped): M = 2 8.0 against
-// 8.3 us and 0.526 against 0.519 ms, M = 3 10.2 against 9.2 us and 0.73
-// against 0.58 ms, M = 4 12.0 against 10.3 us and 0.92 against 0.66 ms
-// (dot-product against matrix core).
+// launch; the 224-linear Layer-mix pass, grouped; dot-product against
+// matrix core): M = 2 7.8 against 8.2 us and 0.545 against 0.523 ms,
+// M = 3 10.2 against 9.0 us and 0.73 against 0.58 ms, M = 4 12.0 against
+// 9.8 us and 0.92 against 0.62 ms.
 __host__ __device__ constexpr bool mfma_decode(int bits, int M, int R) {
   return bits == 2 && M >= 3 && R == 4;
 }
@@ -450,10 +450,9 @@ __device__ __forceinline__ mf_f32x4 mfma4(uint32_t a0, uint32_t a1, uint32_t b0,
 // INT2 at M = 3-4 on the matrix cores.  A wave's four rows share k: lane
 // 4b + j holds, for each of its four 16-byte chunks (one group of 64 codes
 // of row j), the codes as exact bias values in the B operand, and the same
-// lane supplies activation row j (zeros for j >= M) at the same k in the A
-// operand (lanes past M read row 0: rows m >= M of D are never used),
-// read from the x pairs the staging wrote for that chunk.  The
-// 16 blocks are 16 groups.  Codes unpack as on the dot-product path --
+// lane supplies activation row j at the same k in the A operand (lanes
+// past M read row 0: rows m >= M of D are never used), read from the x
+// pairs the staging wrote for that chunk.  The 16 blocks are 16 groups.  Codes unpack as on the dot-product path --
 // pairs (q_i, q_i+8) at weights 1, 4 and 16 -- and each weight class
 // accumulates in its own D, so after the group's 16 instructions lane
 // 4b + j holds, for activation rows m = 0..3,
